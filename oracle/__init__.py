@@ -1,0 +1,130 @@
+"""fp64 CPU oracle for causal multi-head self-attention (forward and backward).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+CPU-baseline leg of the benchmark, never by the GPU library or its binding.
+It shares no code with the GPU path. The arithmetic lives in
+``attn_oracle.c`` (plain C, fp64, libm exp/log); this module only builds,
+loads and marshals numpy arrays into it.
+
+Definition followed: the slow written-out attention of nanoGPT's model.py
+(page "nanoGPT: a real GPT in two 300-line files", section 2 "How the code
+works": q @ k^T, times 1/sqrt(head size), future filled with -inf, softmax,
+then @ v) with the causal rule of section 8 "Self-check" (a position sees
+itself and earlier positions), and the analytic gradient of sum(dO * O) that
+autograd forms (section 1 "Summary").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_DP = ctypes.POINTER(ctypes.c_double)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile attn_oracle.c into liboracle.so with gcc (no fast-math, no FMA
+    contraction, so every sum is evaluated exactly as written)."""
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c99",
+           "-shared", "-fPIC", "-pthread", _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    L, I = ctypes.c_long, ctypes.c_int
+    lib.oracle_attn_fwd.argtypes = [L, L, L, _DP, _DP, _DP, _DP, _DP, I]
+    lib.oracle_attn_fwd.restype = I
+    lib.oracle_attn_bwd.argtypes = [L, L, L, _DP, _DP, _DP, _DP, _DP, _DP, _DP, I]
+    lib.oracle_attn_bwd.restype = I
+    lib.oracle_attn_head_intermediates.argtypes = [L, L, _DP, _DP, _DP, _DP, _DP, _DP,
+                                                   _DP, _DP]
+    lib.oracle_attn_head_intermediates.restype = I
+    _lib = lib
+    return lib
+
+
+def _as_f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # a torch tensor: widen exactly to fp64 on the CPU
+        x = x.detach().cpu().double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_DP)
+
+
+def _default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _heads_shape(q: np.ndarray):
+    if q.ndim < 2:
+        raise ValueError("expected [..., T, D]")
+    T, D = q.shape[-2], q.shape[-1]
+    heads = int(np.prod(q.shape[:-2])) if q.ndim > 2 else 1
+    return heads, T, D
+
+
+def attn_fwd(q, k, v, nthreads: int | None = None):
+    """Return (O, LSE) in fp64 for inputs shaped [..., T, D]."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v shapes differ")
+    heads, T, D = _heads_shape(q)
+    o = np.zeros(q.shape, dtype=np.float64)
+    lse = np.zeros(q.shape[:-1], dtype=np.float64)
+    st = _load().oracle_attn_fwd(heads, T, D, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                 nthreads or _default_threads())
+    if st != 0:
+        raise RuntimeError(f"oracle_attn_fwd failed with status {st}")
+    return o, lse
+
+
+def attn_bwd(q, k, v, dout, nthreads: int | None = None):
+    """Return (dQ, dK, dV) in fp64: the gradient of sum(dout * O)."""
+    q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    if not (q.shape == k.shape == v.shape == dout.shape):
+        raise ValueError("q, k, v, dout shapes differ")
+    heads, T, D = _heads_shape(q)
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(q.shape, dtype=np.float64)
+    dv = np.zeros(q.shape, dtype=np.float64)
+    st = _load().oracle_attn_bwd(heads, T, D, _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), nthreads or _default_threads())
+    if st != 0:
+        raise RuntimeError(f"oracle_attn_bwd failed with status {st}")
+    return dq, dk, dv
+
+
+def head_intermediates(q, k, v, dout) -> dict:
+    """One head ([T, D] inputs): full T x T P, dP, dS and delta [T]."""
+    q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    if q.ndim != 2:
+        raise ValueError("expected one head [T, D]")
+    T, D = q.shape
+    P = np.zeros((T, T))
+    dP = np.zeros((T, T))
+    dS = np.zeros((T, T))
+    delta = np.zeros(T)
+    st = _load().oracle_attn_head_intermediates(T, D, _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                                _ptr(P), _ptr(dP), _ptr(dS), _ptr(delta))
+    if st != 0:
+        raise RuntimeError(f"oracle_attn_head_intermediates failed with status {st}")
+    return {"P": P, "dP": dP, "dS": dS, "delta": delta}

@@ -1,0 +1,285 @@
+/*
+ * Plain fp64 CPU oracle for causal multi-head self-attention, forward and
+ * backward.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path links, loads or calls
+ * this file; only the test suite, the smoke check and the CPU-baseline leg of
+ * the benchmark do. It shares no code, header or constant with the GPU
+ * library.
+ *
+ * What it computes (layout [B, H, T, D], contiguous, row-major):
+ *
+ *   Forward, the "slow, written-out" attention that nanoGPT's model.py keeps
+ *   beside its fused call (page "nanoGPT: a real GPT in two 300-line files",
+ *   section 2 "How the code works"): scores q.k^T multiplied by
+ *   1/sqrt(head size), every future position set to -infinity, a softmax
+ *   over each row, then the product with v. "Causal" means a position sees
+ *   only itself and earlier positions (same page, section 8 "Self-check"),
+ *   so key j is visible to query i iff j <= i.
+ *
+ *   For one head, with s = 1/sqrt(D) and j <= i:
+ *     S_ij   = s * sum_d Q_id K_jd
+ *     m_i    = max_j S_ij,   l_i = sum_j exp(S_ij - m_i)
+ *     P_ij   = exp(S_ij - m_i) / l_i          (P_ij = 0 for j > i)
+ *     O_i    = sum_j P_ij V_j
+ *     LSE_i  = m_i + ln l_i                    (natural log, scaled scores)
+ *
+ *   Backward: the analytic gradient of L = sum(dO * O) that autograd forms
+ *   for nanoGPT's loss.backward() (same page, section 1 "Summary"):
+ *     delta_i = sum_d dO_id O_id
+ *     dP_ij   = sum_d dO_id V_jd
+ *     dS_ij   = P_ij (dP_ij - delta_i)
+ *     dV_j    = sum_{i>=j} P_ij dO_i
+ *     dQ_i    = s sum_{j<=i} dS_ij K_j
+ *     dK_j    = s sum_{i>=j} dS_ij Q_i
+ *
+ * It is the plain two-pass (max, then sum) softmax per row, not an online
+ * one; rows of P are recomputed in the backward instead of being stored.
+ * Sums run in ascending index order; exp and log are libm's. Each (b, h) head
+ * is computed by exactly one thread, so results do not depend on the thread
+ * count.
+ *
+ * Parity pins (checked by the CPU test suite, independent of this file):
+ * 50-digit brute force with the explicit softmax Jacobian, central finite
+ * differences, the library routine scaled_dot_product_attention in fp64,
+ * closed forms (row 0, all keys equal, T = 1), zero row sums of dS, column
+ * sums of dK and dV, and equivariances.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL 1
+#define ORACLE_ENOMEM 2
+
+/* ---- one head ---------------------------------------------------------- */
+
+/* Row i of the attention matrix: fills p[0..i] with P_ij, returns LSE_i. */
+static double softmax_row(long i, long D, double s, const double* q,
+                          const double* k, double* p) {
+  const double* qi = q + i * D;
+  double m = -INFINITY;
+  for (long j = 0; j <= i; ++j) {
+    const double* kj = k + j * D;
+    double dot = 0.0;
+    for (long d = 0; d < D; ++d) dot += qi[d] * kj[d];
+    p[j] = s * dot;
+    if (p[j] > m) m = p[j];
+  }
+  double l = 0.0;
+  for (long j = 0; j <= i; ++j) {
+    p[j] = exp(p[j] - m);
+    l += p[j];
+  }
+  for (long j = 0; j <= i; ++j) p[j] /= l;
+  return m + log(l);
+}
+
+static void head_forward(long T, long D, const double* q, const double* k,
+                         const double* v, double* o, double* lse, double* p) {
+  const double s = 1.0 / sqrt((double)D);
+  for (long i = 0; i < T; ++i) {
+    double li = softmax_row(i, D, s, q, k, p);
+    if (lse) lse[i] = li;
+    double* oi = o + i * D;
+    for (long d = 0; d < D; ++d) oi[d] = 0.0;
+    for (long j = 0; j <= i; ++j) {
+      const double* vj = v + j * D;
+      for (long d = 0; d < D; ++d) oi[d] += p[j] * vj[d];
+    }
+  }
+}
+
+/* o is scratch of T*D doubles, p of T doubles. */
+static void head_backward(long T, long D, const double* q, const double* k,
+                          const double* v, const double* dout, double* dq,
+                          double* dk, double* dv, double* o, double* p,
+                          double* delta) {
+  const double s = 1.0 / sqrt((double)D);
+  head_forward(T, D, q, k, v, o, NULL, p);
+  for (long i = 0; i < T; ++i) {
+    double acc = 0.0;
+    for (long d = 0; d < D; ++d) acc += dout[i * D + d] * o[i * D + d];
+    delta[i] = acc;
+  }
+  memset(dq, 0, sizeof(double) * T * D);
+  memset(dk, 0, sizeof(double) * T * D);
+  memset(dv, 0, sizeof(double) * T * D);
+  for (long i = 0; i < T; ++i) {
+    softmax_row(i, D, s, q, k, p);
+    const double* qi = q + i * D;
+    const double* doi = dout + i * D;
+    double* dqi = dq + i * D;
+    for (long j = 0; j <= i; ++j) {
+      const double* kj = k + j * D;
+      const double* vj = v + j * D;
+      double dp = 0.0;
+      for (long d = 0; d < D; ++d) dp += doi[d] * vj[d];
+      const double ds = p[j] * (dp - delta[i]);
+      double* dvj = dv + j * D;
+      double* dkj = dk + j * D;
+      for (long d = 0; d < D; ++d) {
+        dvj[d] += p[j] * doi[d];
+        dqi[d] += s * ds * kj[d];
+        dkj[d] += s * ds * qi[d];
+      }
+    }
+  }
+}
+
+/* ---- threads over heads ------------------------------------------------ */
+
+typedef struct {
+  int backward;
+  long heads, T, D;
+  const double *q, *k, *v, *dout;
+  double *o, *lse, *dq, *dk, *dv;
+  int tid, nthreads;
+  int status;
+} job_t;
+
+static void* run_job(void* arg) {
+  job_t* jb = (job_t*)arg;
+  const long T = jb->T, D = jb->D, E = T * D;
+  double* p = (double*)malloc(sizeof(double) * (size_t)T);
+  double* o = jb->backward ? (double*)malloc(sizeof(double) * (size_t)E) : NULL;
+  double* delta = jb->backward ? (double*)malloc(sizeof(double) * (size_t)T) : NULL;
+  if (!p || (jb->backward && (!o || !delta))) {
+    jb->status = ORACLE_ENOMEM;
+  } else {
+    for (long h = jb->tid; h < jb->heads; h += jb->nthreads) {
+      if (jb->backward)
+        head_backward(T, D, jb->q + h * E, jb->k + h * E, jb->v + h * E,
+                      jb->dout + h * E, jb->dq + h * E, jb->dk + h * E,
+                      jb->dv + h * E, o, p, delta);
+      else
+        head_forward(T, D, jb->q + h * E, jb->k + h * E, jb->v + h * E,
+                     jb->o + h * E, jb->lse ? jb->lse + h * T : NULL, p);
+    }
+    jb->status = ORACLE_OK;
+  }
+  free(p);
+  free(o);
+  free(delta);
+  return NULL;
+}
+
+static int run_all(job_t proto, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 1024) nthreads = 1024;
+  if ((long)nthreads > proto.heads) nthreads = (int)(proto.heads > 0 ? proto.heads : 1);
+  job_t* jobs = (job_t*)calloc((size_t)nthreads, sizeof(job_t));
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  if (!jobs || !th) {
+    free(jobs);
+    free(th);
+    return ORACLE_ENOMEM;
+  }
+  int status = ORACLE_OK;
+  for (int t = 0; t < nthreads; ++t) {
+    jobs[t] = proto;
+    jobs[t].tid = t;
+    jobs[t].nthreads = nthreads;
+  }
+  int started = 0;
+  for (int t = 1; t < nthreads; ++t) {
+    if (pthread_create(&th[t], NULL, run_job, &jobs[t]) != 0) break;
+    started = t;
+  }
+  /* Threads that failed to start are run on this thread. */
+  run_job(&jobs[0]);
+  for (int t = 1; t <= started; ++t) pthread_join(th[t], NULL);
+  for (int t = started + 1; t < nthreads; ++t) run_job(&jobs[t]);
+  for (int t = 0; t < nthreads; ++t)
+    if (jobs[t].status != ORACLE_OK) status = jobs[t].status;
+  free(jobs);
+  free(th);
+  return status;
+}
+
+/* ---- exported ---------------------------------------------------------- */
+
+/* O [heads, T, D] and LSE [heads, T] (lse may be NULL). heads = B*H. */
+int oracle_attn_fwd(long heads, long T, long D, const double* q, const double* k,
+                    const double* v, double* o, double* lse, int nthreads) {
+  if (heads < 0 || T < 0 || D < 1 || !q || !k || !v || !o) return ORACLE_EINVAL;
+  if (heads == 0 || T == 0) return ORACLE_OK;
+  job_t jb;
+  memset(&jb, 0, sizeof jb);
+  jb.backward = 0;
+  jb.heads = heads;
+  jb.T = T;
+  jb.D = D;
+  jb.q = q;
+  jb.k = k;
+  jb.v = v;
+  jb.o = o;
+  jb.lse = lse;
+  return run_all(jb, nthreads);
+}
+
+/* dQ, dK, dV [heads, T, D] for the upstream gradient dout [heads, T, D]. */
+int oracle_attn_bwd(long heads, long T, long D, const double* q, const double* k,
+                    const double* v, const double* dout, double* dq, double* dk,
+                    double* dv, int nthreads) {
+  if (heads < 0 || T < 0 || D < 1 || !q || !k || !v || !dout || !dq || !dk || !dv)
+    return ORACLE_EINVAL;
+  if (heads == 0 || T == 0) return ORACLE_OK;
+  job_t jb;
+  memset(&jb, 0, sizeof jb);
+  jb.backward = 1;
+  jb.heads = heads;
+  jb.T = T;
+  jb.D = D;
+  jb.q = q;
+  jb.k = k;
+  jb.v = v;
+  jb.dout = dout;
+  jb.dq = dq;
+  jb.dk = dk;
+  jb.dv = dv;
+  return run_all(jb, nthreads);
+}
+
+/*
+ * One head's full T x T intermediates, for small T: P, dP, dS (row-major,
+ * zero above the diagonal) and delta [T]. Used by tests of row identities.
+ */
+int oracle_attn_head_intermediates(long T, long D, const double* q, const double* k,
+                                   const double* v, const double* dout, double* P,
+                                   double* dP, double* dS, double* delta) {
+  if (T < 1 || D < 1 || !q || !k || !v || !dout || !P || !dP || !dS || !delta)
+    return ORACLE_EINVAL;
+  const double s = 1.0 / sqrt((double)D);
+  double* o = (double*)malloc(sizeof(double) * (size_t)(T * D));
+  double* p = (double*)malloc(sizeof(double) * (size_t)T);
+  if (!o || !p) {
+    free(o);
+    free(p);
+    return ORACLE_ENOMEM;
+  }
+  head_forward(T, D, q, k, v, o, NULL, p);
+  for (long i = 0; i < T; ++i) {
+    double acc = 0.0;
+    for (long d = 0; d < D; ++d) acc += dout[i * D + d] * o[i * D + d];
+    delta[i] = acc;
+  }
+  memset(P, 0, sizeof(double) * (size_t)(T * T));
+  memset(dP, 0, sizeof(double) * (size_t)(T * T));
+  memset(dS, 0, sizeof(double) * (size_t)(T * T));
+  for (long i = 0; i < T; ++i) {
+    softmax_row(i, D, s, q, k, p);
+    for (long j = 0; j <= i; ++j) {
+      double dp = 0.0;
+      for (long d = 0; d < D; ++d) dp += dout[i * D + d] * v[j * D + d];
+      P[i * T + j] = p[j];
+      dP[i * T + j] = dp;
+      dS[i * T + j] = p[j] * (dp - delta[i]);
+    }
+  }
+  free(o);
+  free(p);
+  return ORACLE_OK;
+}
