@@ -1,0 +1,307 @@
+// Causal attention backward, bf16 inputs, fp32 accumulation and fp32
+// gradients, head dim 64, for gfx950 (CDNA4).
+//
+// The gradient of sum(dO * O) for O = softmax(Q K^T / sqrt(64), causal) V:
+// what autograd forms for nanoGPT's loss.backward() through the fused
+// attention call (page "nanoGPT: a real GPT in two 300-line files", sections
+// 1 "Summary" and 2 "How the code works"). With s = 1/sqrt(64):
+//   delta_i = sum_d dO_id O_id
+//   P_ij    = exp(s Q_i.K_j - LSE_i)        (recomputed; j <= i)
+//   dV_j    = sum_i P_ij dO_i
+//   dP_ij   = dO_i . V_j
+//   dS_ij   = P_ij (dP_ij - delta_i)
+//   dK_j    = s sum_i dS_ij Q_i,   dQ_i = s sum_j dS_ij K_j
+//
+// Kernel 1 (prep) forms delta from the stored O (plus its low part o_lo
+// when the forward kept it, which restores fp32 accuracy) and zeroes dQ.
+// Kernel 2 (main): a workgroup of 4 waves owns 128 consecutive keys of one
+// head (32 per wave) and keeps their K, V fragments and dK, dV accumulators
+// in registers. It walks the 64-query tiles from its diagonal to the end of
+// the sequence; per tile it stages Q and dO in LDS both row-major in bf16
+// (for the S = Q K^T and dP = dO V^T products) and transposed in fp16 (for
+// dK^T += Q^T dS and dV^T += dO^T P), recomputes P from the saved LSE, forms
+// dS, and writes dS to LDS. Each wave then forms one 32x32 block of the
+// tile's dQ = dS K over all 128 keys from LDS and adds it into the fp32 dQ
+// with atomic adds.
+//
+// Precision: S = Q K^T and dP = dO V^T multiply bf16 inputs exactly. The
+// three products with a rounded operand (dV += P^T dO, dK += dS^T Q,
+// dQ += dS K) use fp16 MFMA: P and dS are rounded to fp16 (11 significant
+// bits) and the bf16 Q, K, dO tiles convert to fp16 exactly.
+#include "attn_common.h"
+#include "attn_launch.h"
+
+namespace gpt_attn {
+namespace {
+
+constexpr int kBK = 128;      // keys per workgroup
+constexpr int kBQ = 64;       // queries per step
+constexpr int kThreads = 256;
+constexpr int kRowQ = 72;     // padded row of a 64-wide 16-bit LDS tile
+constexpr int kRowK = 136;    // padded row of a 128-wide 16-bit LDS tile
+
+__global__ __launch_bounds__(256) void attn_bwd_prep_bf16_kernel(
+    const bf16* __restrict__ o, const bf16* __restrict__ o_lo, const bf16* __restrict__ dout,
+    float* __restrict__ delta, float* __restrict__ dq, long long rows) {
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = gid >> 3;
+  const int part = (int)(gid & 7);
+  float acc = 0.f;
+  if (row < rows) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + row * kHeadDim + part * 8);
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dout + row * kHeadDim + part * 8);
+    if (o_lo) {
+      const bf16x8 c = *reinterpret_cast<const bf16x8*>(o_lo + row * kHeadDim + part * 8);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc = fmaf((float)a[t] + (float)c[t], (float)b[t], acc);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc = fmaf((float)a[t], (float)b[t], acc);
+    }
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4* dst = reinterpret_cast<f32x4*>(dq + row * kHeadDim + part * 8);
+    dst[0] = z;
+    dst[1] = z;
+  }
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 2, 64);
+  acc += __shfl_xor(acc, 4, 64);
+  if (row < rows && part == 0) delta[row] = acc;
+}
+
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ delta, float* __restrict__ dq, float* __restrict__ dk,
+    float* __restrict__ dv, int n_heads, int T, int n_ktiles, float scale, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) bf16 Qs[kBQ * kRowQ];        // [q][d]
+  __shared__ __attribute__((aligned(16))) bf16 dOs[kBQ * kRowQ];       // [q][d]
+  __shared__ __attribute__((aligned(16))) f16 Qt[kHeadDim * kRowQ];    // [d][q]
+  __shared__ __attribute__((aligned(16))) f16 dOt[kHeadDim * kRowQ];   // [d][q]
+  __shared__ __attribute__((aligned(16))) f16 Kt[kHeadDim * kRowK];    // [d][key]
+  __shared__ __attribute__((aligned(16))) f16 dSs[kBQ * kRowK];        // [q][key]
+  __shared__ __attribute__((aligned(16))) float lse2s[kBQ];
+  __shared__ __attribute__((aligned(16))) float dels[kBQ];
+
+  const TileMap tm = map_tile_xcd(blockIdx.x, n_heads, n_ktiles, false);
+  if (!tm.valid) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+
+  const size_t hoff = (size_t)tm.head * (size_t)T * kHeadDim;
+  const size_t roff = (size_t)tm.head * (size_t)T;
+  const bf16* qh = q + hoff;
+  const bf16* kh = k + hoff;
+  const bf16* vh = v + hoff;
+  const bf16* doh = dout + hoff;
+
+  const int k0 = tm.tile * kBK;
+  const int kw0 = k0 + wave * 32;
+  const int my_key = kw0 + l32;  // the key column this lane owns
+
+  // K and V of this wave's 32 keys as B operands (lane: its key, 8 dims).
+  bf16x8 kf[4], vf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    kf[kk] = load_bf16x8(kh + (size_t)my_key * kHeadDim + kk * 16 + 8 * hf, my_key < T);
+    vf[kk] = load_bf16x8(vh + (size_t)my_key * kHeadDim + kk * 16 + 8 * hf, my_key < T);
+  }
+
+  // K^T of all 128 keys for the dQ product: thread takes key pair and 8 dims.
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int c = tid + kThreads * p;          // 0..511
+    const int j = 2 * (c & 63), d0 = (c >> 6) * 8;
+    const bf16x8 x0 = load_bf16x8(kh + (size_t)(k0 + j) * kHeadDim + d0, k0 + j < T);
+    const bf16x8 x1 = load_bf16x8(kh + (size_t)(k0 + j + 1) * kHeadDim + d0, k0 + j + 1 < T);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      f16x2 pr = {bf16_to_f16(x0[t]), bf16_to_f16(x1[t])};
+      *reinterpret_cast<f16x2*>(&Kt[(d0 + t) * kRowK + j]) = pr;
+    }
+  }
+
+  f32x16 dvacc[2], dkacc[2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dvacc[db][r] = 0.f;
+      dkacc[db][r] = 0.f;
+    }
+
+  for (int qs = k0; qs < T; qs += kBQ) {
+    // ---- stage Q and dO tiles (row-major and transposed), LSE*log2e, delta
+    {
+      const int qa = 2 * (tid & 31), d0 = (tid >> 5) * 8;
+      const int r0 = qs + qa, r1 = qs + qa + 1;
+      const bf16x8 x0 = load_bf16x8(qh + (size_t)r0 * kHeadDim + d0, r0 < T);
+      const bf16x8 x1 = load_bf16x8(qh + (size_t)r1 * kHeadDim + d0, r1 < T);
+      const bf16x8 y0 = load_bf16x8(doh + (size_t)r0 * kHeadDim + d0, r0 < T);
+      const bf16x8 y1 = load_bf16x8(doh + (size_t)r1 * kHeadDim + d0, r1 < T);
+      *reinterpret_cast<bf16x8*>(&Qs[qa * kRowQ + d0]) = x0;
+      *reinterpret_cast<bf16x8*>(&Qs[(qa + 1) * kRowQ + d0]) = x1;
+      *reinterpret_cast<bf16x8*>(&dOs[qa * kRowQ + d0]) = y0;
+      *reinterpret_cast<bf16x8*>(&dOs[(qa + 1) * kRowQ + d0]) = y1;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        f16x2 pq = {bf16_to_f16(x0[t]), bf16_to_f16(x1[t])};
+        f16x2 pd = {bf16_to_f16(y0[t]), bf16_to_f16(y1[t])};
+        *reinterpret_cast<f16x2*>(&Qt[(d0 + t) * kRowQ + qa]) = pq;
+        *reinterpret_cast<f16x2*>(&dOt[(d0 + t) * kRowQ + qa]) = pd;
+      }
+      if (tid < kBQ) {
+        const int r = qs + tid;
+        lse2s[tid] = r < T ? lse[roff + r] * kLog2e : 0.f;
+        dels[tid] = r < T ? delta[roff + r] : 0.f;
+      }
+    }
+    __syncthreads();
+
+    // ---- per wave: S, P, dP, dS for its 32 keys x 64 queries
+    f16x8 pbf[2][2], dsbf[2][2];
+    bool act[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int qb0 = qs + mb * 32;
+      act[mb] = (qb0 < T) && (kw0 < T) && (kw0 <= qb0 + 31);
+      if (!act[mb]) continue;
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+      const int arow = (mb * 32 + perm32(l32)) * kRowQ + 8 * hf;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(&Qs[arow + kk * 16]), kf[kk], s);
+        dp = mfma32x32x16(*reinterpret_cast<const bf16x8*>(&dOs[arow + kk * 16]), vf[kk], dp);
+      }
+      const bool need_mask = (qb0 < kw0 + 31) || (kw0 + 32 > T) || (qb0 + 32 > T);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        // Register 8c + t of half hf is query qb0 + 16c + 8hf + t.
+        const int qoff = mb * 32 + 16 * c + 8 * hf;
+        const f32x4 L0 = *reinterpret_cast<const f32x4*>(&lse2s[qoff]);
+        const f32x4 L1 = *reinterpret_cast<const f32x4*>(&lse2s[qoff + 4]);
+        const f32x4 E0 = *reinterpret_cast<const f32x4*>(&dels[qoff]);
+        const f32x4 E1 = *reinterpret_cast<const f32x4*>(&dels[qoff + 4]);
+        float p[8], ds[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float lse2 = t < 4 ? L0[t] : L1[t - 4];
+          const float del = t < 4 ? E0[t] : E1[t - 4];
+          const int qi = qs + qoff + t;
+          float pv = fast_exp2(fmaf(s[8 * c + t], scale_log2, -lse2));
+          if (need_mask && (my_key > qi || my_key >= T || qi >= T)) pv = 0.f;
+          p[t] = pv;
+          ds[t] = pv * (dp[8 * c + t] - del);
+        }
+        pbf[mb][c] = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+        dsbf[mb][c] = pack_f16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) dSs[(qoff + t) * kRowK + wave * 32 + l32] = dsbf[mb][c][t];
+      }
+    }
+
+    // ---- dV^T += dO^T P, dK^T += Q^T dS (k steps of 16 queries)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      if (!act[mb]) continue;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int ks = 2 * mb + c;
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const int aoff = (db * 32 + l32) * kRowQ + ks * 16 + 8 * hf;
+          dvacc[db] = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&dOt[aoff]), pbf[mb][c],
+                                       dvacc[db]);
+          dkacc[db] = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&Qt[aoff]), dsbf[mb][c],
+                                       dkacc[db]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- dQ block (queries 32qb.., dims 32db..) = dS K over the 128 keys
+    {
+      const int qb = wave >> 1, db = wave & 1;
+      const int qb0 = qs + qb * 32;
+      if (qb0 < T) {
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        bool any = false;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          // Keys k0 + 16ks .. +15 belong to wave ks/2; skip the blocks that
+          // wave left out (wholly in the future of these queries or past T).
+          const int kws = k0 + (ks >> 1) * 32;
+          if (kws >= T || kws > qb0 + 31) continue;
+          any = true;
+          const f16x8 a =
+              *reinterpret_cast<const f16x8*>(&dSs[(qb * 32 + l32) * kRowK + ks * 16 + 8 * hf]);
+          const f16x8 b =
+              *reinterpret_cast<const f16x8*>(&Kt[(db * 32 + l32) * kRowK + ks * 16 + 8 * hf]);
+          acc = mfma32x32x16_f16(a, b, acc);
+        }
+        if (any) {
+          float* dqh = dq + hoff;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qi = qb0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (qi < T)
+              atomicAdd(dqh + (size_t)qi * kHeadDim + db * 32 + l32, acc[r] * scale);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: dV, dK = s * acc (lane: its key; 4 consecutive dims per store)
+  if (my_key < T) {
+    float* dvr = dv + hoff + (size_t)my_key * kHeadDim;
+    float* dkr = dk + hoff + (size_t)my_key * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * hf;
+        f32x4 a = {dvacc[db][4 * g], dvacc[db][4 * g + 1], dvacc[db][4 * g + 2],
+                   dvacc[db][4 * g + 3]};
+        f32x4 b = {dkacc[db][4 * g] * scale, dkacc[db][4 * g + 1] * scale,
+                   dkacc[db][4 * g + 2] * scale, dkacc[db][4 * g + 3] * scale};
+        *reinterpret_cast<f32x4*>(dvr + d) = a;
+        *reinterpret_cast<f32x4*>(dkr + d) = b;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const void* o_lo, const void* dout, const float* lse, float* dq,
+                           float* dk, float* dv, float* delta, int n_heads, int T,
+                           hipStream_t stream) {
+  const long long rows = (long long)n_heads * T;
+  const unsigned prep_blocks = (unsigned)((rows * 8 + 255) / 256);
+  hipLaunchKernelGGL(attn_bwd_prep_bf16_kernel, dim3(prep_blocks), dim3(256), 0, stream,
+                     static_cast<const bf16*>(o), static_cast<const bf16*>(o_lo),
+                     static_cast<const bf16*>(dout), delta, dq, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_ktiles = (T + kBK - 1) / kBK;
+  const float scale = 0.125f;  // 1/sqrt(64)
+  hipLaunchKernelGGL(attn_bwd_main_bf16_kernel, dim3(tiled_grid(n_heads, n_ktiles)),
+                     dim3(kThreads), 0, stream, static_cast<const bf16*>(q),
+                     static_cast<const bf16*>(k), static_cast<const bf16*>(v),
+                     static_cast<const bf16*>(dout), lse, delta, dq, dk, dv, n_heads, T,
+                     n_ktiles, scale, scale * kLog2e);
+  return hipGetLastError();
+}
+
+}  // namespace gpt_attn

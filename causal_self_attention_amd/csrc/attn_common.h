@@ -1,0 +1,98 @@
+// Device-side building blocks shared by the gfx950 attention kernels:
+// vector types, the bf16 MFMA wrapper and its register layout, conversions,
+// and the launch-side helpers the host code needs.
+//
+// MFMA v_mfma_f32_32x32x16_bf16 (CDNA4), one wave of 64 lanes, lane l,
+// h = l / 32:
+//   A (32 x 16, row-major M x K): lane l holds row l % 32, k = 8h .. 8h+7.
+//   B (16 x 32, K x N):           lane l holds col l % 32, k = 8h .. 8h+7.
+//   C (32 x 32, fp32, 16 regs):   lane l holds col l % 32; register v holds
+//                                 row 8 * (v / 4) + 4h + (v % 4).
+// These layouts are checked on the device by a layout test before any
+// kernel result is trusted.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gpt_attn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef _Float16 f16x4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
+typedef _Float16 f16x2 __attribute__((__vector_size__(2 * sizeof(_Float16))));
+typedef int i32x4 __attribute__((__vector_size__(4 * sizeof(int))));
+typedef int i32x2 __attribute__((__vector_size__(2 * sizeof(int))));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kHeadDim = 64;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Same shapes and lane layout with fp16 operands (11-bit significands): used
+// where one operand is a probability or a score gradient that must be rounded
+// for the matrix core. The other operand is a bf16 input converted exactly.
+__device__ __forceinline__ f32x16 mfma32x32x16_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  i32x4 z = {0, 0, 0, 0};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+// 16-byte global load of 8 bf16, or zeros when !valid.
+__device__ __forceinline__ bf16x8 load_bf16x8(const bf16* p, bool valid) {
+  if (!valid) return zero_bf16x8();
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Pack eight fp32 values into eight bf16 (round to nearest even).
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3,
+                                              float a4, float a5, float a6, float a7) {
+  bf16x8 r = {(bf16)a0, (bf16)a1, (bf16)a2, (bf16)a3, (bf16)a4, (bf16)a5, (bf16)a6, (bf16)a7};
+  return r;
+}
+
+// Pack eight fp32 values into eight fp16 (round to nearest even).
+__device__ __forceinline__ f16x8 pack_f16x8(float a0, float a1, float a2, float a3, float a4,
+                                            float a5, float a6, float a7) {
+  f16x8 r = {(f16)a0, (f16)a1, (f16)a2, (f16)a3, (f16)a4, (f16)a5, (f16)a6, (f16)a7};
+  return r;
+}
+
+// bf16 -> fp16. Exact for finite |x| in [2^-14, 65504] (bf16 carries 8
+// significant bits, fp16 11); smaller magnitudes become fp16 subnormals
+// (absolute error below 2^-25) and larger ones overflow to infinity.
+__device__ __forceinline__ f16 bf16_to_f16(bf16 x) { return (f16)(float)x; }
+
+// Eight consecutive accumulator registers c[base .. base+7] as bf16.
+__device__ __forceinline__ bf16x8 acc_to_bf16x8(const f32x16& c, int base) {
+  return pack_bf16x8(c[base + 0], c[base + 1], c[base + 2], c[base + 3], c[base + 4],
+                     c[base + 5], c[base + 6], c[base + 7]);
+}
+
+// Bit 2 <-> bit 3 swap of a row index inside a 32-row MFMA block. Loading the
+// A operand's row l%32 from source row perm32(l%32) makes accumulator
+// register v = 8c + t of lane half h hold source row 16c + 8h + t: eight
+// consecutive rows per half, exactly the k order the next MFMA's B operand
+// wants, so P / dS never need a lane shuffle.
+__device__ __forceinline__ int perm32(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+}  // namespace gpt_attn

@@ -1,0 +1,57 @@
+// Internal launch interface between the C-ABI layer and the kernel files.
+// Every function enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace gpt_attn {
+
+// Work-item placement shared by the tiled kernels. Workgroups are handed to
+// the 8 XCDs round-robin (workgroup id modulo 8). Each XCD is given a
+// contiguous range of heads so the K/V (or Q/dO) tiles one head's workgroups
+// re-read stay in that XCD's L2; inside the XCD, tiles with the most work are
+// handed out first. The grid is 8 * ceil(heads/8) * tiles; slots beyond an
+// XCD's share exit at once.
+struct TileMap {
+  int head;
+  int tile;
+  bool valid;
+};
+
+__device__ __forceinline__ TileMap map_tile_xcd(int bid, int n_heads, int n_tiles,
+                                                bool descending) {
+  const int xcd = bid & 7;
+  const int slot = bid >> 3;
+  const int base = n_heads >> 3, extra = n_heads & 7;
+  const int nh = base + (xcd < extra ? 1 : 0);
+  const int h0 = xcd * base + (xcd < extra ? xcd : extra);
+  TileMap m;
+  m.valid = slot < nh * n_tiles;
+  if (!m.valid) {
+    m.head = 0;
+    m.tile = 0;
+    return m;
+  }
+  const int t = slot / nh;
+  m.head = h0 + (slot - t * nh);
+  m.tile = descending ? n_tiles - 1 - t : t;
+  return m;
+}
+
+inline unsigned tiled_grid(int n_heads, int n_tiles) {
+  return 8u * (unsigned)((n_heads + 7) / 8) * (unsigned)n_tiles;
+}
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, void* o_lo,
+                           float* lse, int n_heads, int T, hipStream_t stream);
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const void* o_lo, const void* dout, const float* lse, float* dq,
+                           float* dk, float* dv, float* delta, int n_heads, int T,
+                           hipStream_t stream);
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          int n_heads, int T, hipStream_t stream);
+hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                          const float* dout, const float* lse, float* dq, float* dk, float* dv,
+                          float* delta, int n_heads, int T, hipStream_t stream);
+
+}  // namespace gpt_attn

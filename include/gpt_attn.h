@@ -1,0 +1,134 @@
+/*
+ * gpt_attn.h - C ABI of the fused causal self-attention library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation is the causal multi-head attention at the core of nanoGPT's
+ * CausalSelfAttention: PyTorch's fused scaled_dot_product_attention called
+ * with is_causal=True, no mask tensor and the default scale (page "nanoGPT: a
+ * real GPT in two 300-line files", section 2 "How the code works"), whose
+ * written-out equivalent is softmax(Q K^T / sqrt(head size) with the future
+ * set to -inf) V. A position attends to itself and earlier positions only
+ * (same page, section 8 "Self-check"). The backward is the gradient that
+ * autograd computes for it (section 1 "Summary"). The kernels never store the
+ * T x T score matrix, which is what the fused kernels are credited with (page
+ * "The 300-Line LLM Engine: Inside nanoGPT", section "Flat Architecture and
+ * Flash Attention").
+ *
+ * Conventions shared by every entry point
+ *   - Layout: every tensor is contiguous row-major [B, H, T, D]; per-row
+ *     statistics (lse, and the delta vector in the workspace) are [B, H, T].
+ *   - Scale: always 1/sqrt(D). Causal masking is always on: key j is visible
+ *     to query i iff j <= i. There is no mask, scale or dropout argument.
+ *   - Pointers are DEVICE pointers (hipMalloc or torch CUDA tensors) and must
+ *     be 16-byte aligned. The caller owns every buffer; the library allocates
+ *     nothing and keeps no state between calls. Outputs must not alias
+ *     inputs or each other.
+ *   - stream is a hipStream_t (NULL = the default stream). Calls only enqueue
+ *     work and return; results are visible after the caller synchronizes.
+ *   - Sizes: B, H, T >= 0; a call with B*H*T == 0 does nothing and returns
+ *     GPT_ATTN_OK (pointers are not inspected). D must be 64. B*H*T must be
+ *     below 2^31 and B*H*T*D below 2^40.
+ *   - Errors: argument errors are returned before any device work is
+ *     enqueued and leave every buffer untouched. GPT_ATTN_E_HIP means the
+ *     HIP runtime rejected a launch (hipGetLastError); a fault inside a
+ *     kernel surfaces at the caller's next synchronization. No C++
+ *     exception crosses this interface.
+ *   - Thread safety: calls are reentrant. Concurrent calls on different
+ *     streams need distinct output and workspace buffers.
+ */
+#ifndef GPT_ATTN_H
+#define GPT_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GPT_ATTN_ABI_VERSION 1
+
+/* Status codes returned by every int-returning entry point. */
+enum gpt_attn_status {
+  GPT_ATTN_OK = 0,
+  GPT_ATTN_E_INVAL = 1,       /* null pointer, negative or overflowing size, bad dtype code,
+                                 o_lo given with GPT_ATTN_F32 */
+  GPT_ATTN_E_UNSUPPORTED = 2, /* a head dimension D with no kernel (D != 64) */
+  GPT_ATTN_E_ALIGN = 3,       /* a pointer that is not 16-byte aligned */
+  GPT_ATTN_E_WORKSPACE = 4,   /* workspace NULL or smaller than gpt_attn_bwd_workspace_bytes */
+  GPT_ATTN_E_HIP = 5          /* the HIP runtime reported an error when launching */
+};
+
+/* Element type of q, k, v, o and dout. lse, dq, dk, dv are always fp32. */
+enum gpt_attn_dtype {
+  GPT_ATTN_F32 = 0, /* IEEE binary32 inputs, fp32 arithmetic throughout */
+  GPT_ATTN_BF16 = 1 /* bfloat16 inputs; matrix products accumulate in fp32 */
+};
+
+/*
+ * Forward: O = softmax(Q K^T / sqrt(D), causal) V and the log-sum-exp of
+ * each row, LSE_i = ln sum_{j<=i} exp(Q_i . K_j / sqrt(D)) (natural log of
+ * the scaled scores).
+ *
+ *   q, k, v  in   [B,H,T,D] of dtype
+ *   o        out  [B,H,T,D] of dtype (bf16 output is rounded to nearest even)
+ *   o_lo     out  OPTIONAL, bf16 only (must be NULL for GPT_ATTN_F32):
+ *                 [B,H,T,D] bf16 receiving bf16(O - o), the part of the fp32
+ *                 result that rounding o to bf16 dropped. Passing it to
+ *                 gpt_attn_bwd gives the backward an O accurate to ~16 bits,
+ *                 which its delta = rowsum(dO * O) needs when softmax rows
+ *                 are sharp. NULL skips the write.
+ *   lse      out  [B,H,T] fp32; the backward needs it
+ *
+ * For bf16, the P V product rounds P to fp16 and converts V to fp16, which is
+ * exact for |v| in [2^-14, 65504]; inputs beyond fp16's finite range give
+ * non-finite outputs.
+ */
+int gpt_attn_fwd(int dtype, int B, int H, int T, int D, const void* q, const void* k,
+                 const void* v, void* o, void* o_lo, float* lse, void* stream);
+
+/*
+ * Bytes of device workspace gpt_attn_bwd needs for this shape: the fp32
+ * vector delta_i = sum_d dO_id O_id, [B,H,T]. Returns 0 for an invalid shape
+ * or dtype, or an empty one.
+ */
+size_t gpt_attn_bwd_workspace_bytes(int dtype, int B, int H, int T, int D);
+
+/*
+ * Backward: the gradient of sum(dout * O) with respect to Q, K and V,
+ * computed without the T x T matrix: P is recomputed from q, k and lse, and
+ * delta = rowsum(dout * O) is formed first by a separate pass.
+ *
+ *   q, k, v      in   [B,H,T,D] of dtype (the forward's inputs)
+ *   o            in   [B,H,T,D] of dtype (the forward's output)
+ *   o_lo         in   OPTIONAL, bf16 only: the forward's o_lo output; when
+ *                     given, delta uses o + o_lo instead of o. Must be NULL
+ *                     for GPT_ATTN_F32.
+ *   dout         in   [B,H,T,D] of dtype (upstream gradient dL/dO)
+ *   lse          in   [B,H,T] fp32 (the forward's output)
+ *   dq, dk, dv   out  [B,H,T,D] fp32, fully overwritten
+ *   workspace    scratch of at least gpt_attn_bwd_workspace_bytes(...)
+ *                bytes, device memory owned by the caller; contents on entry
+ *                are ignored and on return are unspecified.
+ *
+ * For bf16, the products with a rounded operand (P^T dO, dS^T Q, dS K) round
+ * P and dS to fp16 and convert dout, q, k to fp16 (exact for magnitudes in
+ * [2^-14, 65504]). dk, dv (and o, lse from gpt_attn_fwd) are bitwise
+ * reproducible run to run. dq is accumulated with fp32 atomic adds in the
+ * bf16 path, so its low bits may vary between runs.
+ */
+int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const void* k,
+                 const void* v, const void* o, const void* o_lo, const void* dout,
+                 const float* lse, float* dq, float* dk, float* dv, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char* gpt_attn_status_string(int status);
+
+/* GPT_ATTN_ABI_VERSION of the built library. */
+int gpt_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPT_ATTN_H */

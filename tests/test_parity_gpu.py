@@ -1,0 +1,181 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Inputs come from the seeded generator both sides share. Bars, per output
+tensor: fp32 max-abs <= 1e-5; bf16 max-abs <= 2e-2 and mean-abs <= 5e-3.
+Small shapes are checked element by element in full; the full-size
+workloads are run exactly as the benchmark launches them and checked on
+sampled heads (every element of those heads), plus identities that hold at
+any size on every head.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import causal_self_attention_amd as gattn
+from causal_self_attention_amd.inputs import WORKLOADS, make_inputs, workload_inputs
+from tests.gpu_helpers import announce, assert_parity, errors, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+EDGE_T = [1, 2, 3, 7, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257, 300, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T", EDGE_T)
+def test_small_shapes_full_compare(dtype, T):
+    for (B, H) in [(1, 1), (1, 3)]:
+        announce(f"small dtype={dtype} B={B} H={H} T={T} seed={T}")
+        inp = make_inputs(B, H, T, 64, dtype, seed=T)
+        gpu = run_gpu(inp)
+        ref = run_oracle(inp)
+        assert_parity(errors(gpu, ref), dtype, f"{dtype} B={B} H={H} T={T}")
+
+
+def test_backward_without_o_lo():
+    """The backward also runs from the bf16 O alone (o_lo omitted); delta is
+    then less accurate, which the i.i.d. N(0,1) workload still tolerates."""
+    announce("no o_lo bf16 B=2 H=3 T=333")
+    inp = make_inputs(2, 3, 333, 64, "bf16", seed=6)
+    gpu = run_gpu(inp, keep_o_lo=False)
+    assert_parity(errors(gpu, run_oracle(inp)), "bf16", "no o_lo")
+
+
+def test_sharp_softmax_small():
+    """Q, K drawn at std 4: scores of std 16 stress the running-max rescale."""
+    announce("sharp B=2 H=2 T=200 qk_scale=4")
+    inp = make_inputs(2, 2, 200, 64, "bf16", seed=5, qk_scale=4.0)
+    assert_parity(errors(run_gpu(inp), run_oracle(inp)), "bf16", "sharp")
+
+
+def _sample_heads(n_heads: int, k: int = 4) -> list[int]:
+    picks = {0, n_heads - 1, n_heads // 2, (n_heads * 5) // 7}
+    return sorted(h for h in picks if 0 <= h < n_heads)[:k]
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_full_size(name):
+    w = WORKLOADS[name]
+    announce(f"workload {name} B={w.B} H={w.H} T={w.T} dtype={w.dtype}")
+    inp = workload_inputs(w, seed=0)
+    gpu = run_gpu(inp)
+    n_heads = w.B * w.H
+    heads = list(range(n_heads)) if n_heads * w.T <= 4096 else _sample_heads(n_heads)
+    ref = run_oracle(inp, heads)
+    assert_parity(errors(gpu, ref, heads), w.dtype, f"{name} heads {heads}")
+    # Identities on every head: sum_j dV_j = sum_i dO_i and sum_j dK_j = 0.
+    dv_sum = gpu["dv"].double().sum(2)
+    do_sum = inp["do"].double().sum(2)
+    dk_sum = gpu["dk"].double().sum(2)
+    scale = float(w.T) ** 0.5
+    tol = 1e-4 if w.dtype == "f32" else 2e-2
+    assert float((dv_sum - do_sum).abs().max()) <= tol * scale
+    assert float(dk_sum.abs().max()) <= tol * scale
+    for name_ in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.isfinite(gpu[name_]).all(), name_
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_row_zero_is_first_value_row(dtype):
+    announce(f"row0 dtype={dtype}")
+    inp = make_inputs(2, 3, 129, 64, dtype, seed=3)
+    gpu = run_gpu(inp)
+    assert torch.equal(gpu["o"][:, :, 0, :], inp["v"][:, :, 0, :])
+    # dQ_0 = s dS_00 K_0 with dS_00 = dO_0.V_0 - delta_0 = 0 up to the two
+    # dot products' rounding: the parity bar applies.
+    assert float(gpu["dq"][:, :, 0, :].abs().max()) <= (1e-5 if dtype == "f32" else 1e-3)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_future_keys_do_not_leak(dtype):
+    """Masked weights are exact zeros: changing K, V after position t leaves
+    O and LSE of rows <= t bitwise unchanged."""
+    announce(f"causality dtype={dtype}")
+    inp = make_inputs(1, 2, 300, 64, dtype, seed=8)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o1, l1, _ = gattn.attention_forward(q, k, v)
+    t = 150
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, t + 1:, :] = k2[:, :, t + 1:, :] * 3 + 1
+    v2[:, :, t + 1:, :] = -v2[:, :, t + 1:, :]
+    o2, l2, _ = gattn.attention_forward(q, k2, v2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, :, : t + 1].cpu(), o2[:, :, : t + 1].cpu())
+    assert torch.equal(l1[:, :, : t + 1].cpu(), l2[:, :, : t + 1].cpu())
+    assert not torch.equal(o1[:, :, t + 1:].cpu(), o2[:, :, t + 1:].cpu())
+
+
+def test_equal_keys_give_running_mean():
+    announce("equal keys bf16 B=1 H=2 T=200")
+    inp = make_inputs(1, 2, 200, 64, "bf16", seed=4)
+    inp["k"] = inp["k"][:, :, :1, :].expand_as(inp["k"]).contiguous()
+    gpu = run_gpu(inp)
+    v = inp["v"].double()
+    mean_v = v.cumsum(2) / torch.arange(1, 201, dtype=torch.float64)[:, None]
+    assert float((gpu["o"].double() - mean_v).abs().max()) <= 2e-2
+    assert float(gpu["dq"].abs().max()) <= 2e-2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_run_to_run_determinism(dtype):
+    announce(f"determinism dtype={dtype}")
+    w = WORKLOADS["gpt2_124m_bf16_b12_h12_t1024"] if dtype == "bf16" else \
+        WORKLOADS["shakespeare_char_f32_b1_h6_t256"]
+    inp = workload_inputs(w, seed=1)
+    a, b = run_gpu(inp), run_gpu(inp)
+    for n in ("o", "lse", "dk", "dv"):
+        assert torch.equal(a[n], b[n]), n
+    denom = float(a["dq"].abs().max())
+    assert float((a["dq"] - b["dq"]).abs().max()) <= 1e-6 * max(denom, 1.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_outputs_stay_in_bounds(dtype):
+    """Sentinel regions around every output must be untouched."""
+    announce(f"guard regions dtype={dtype}")
+    B, H, T, D = 1, 3, 77, 64
+    inp = make_inputs(B, H, T, D, dtype, seed=12)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    E, R, pad = B * H * T * D, B * H * T, 256
+    td = q.dtype
+
+    def guarded(n, dt):
+        buf = torch.full((n + 2 * pad,), float("nan"), dtype=dt, device=dev)
+        return buf, buf[pad:pad + n]
+
+    ob, o = guarded(E, td)
+    lob, o_lo = guarded(E, td) if dtype == "bf16" else (None, None)
+    lb, lse = guarded(R, torch.float32)
+    o, lse = o.view(B, H, T, D), lse.view(B, H, T)
+    if o_lo is not None:
+        o_lo = o_lo.view(B, H, T, D)
+    gattn.gpt_attn_fwd(q, k, v, o, o_lo, lse)
+    grads = [guarded(E, torch.float32) for _ in range(3)]
+    wb, ws = guarded(R, torch.float32)
+    gattn.gpt_attn_bwd(q, k, v, o, o_lo, do, lse, *(g[1].view(B, H, T, D) for g in grads), ws)
+    torch.cuda.synchronize()
+    bufs = [ob, lb, wb] + [g[0] for g in grads] + ([lob] if lob is not None else [])
+    for buf in bufs:
+        assert torch.isnan(buf[:pad].float()).all() and torch.isnan(buf[-pad:].float()).all()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+def test_error_statuses_through_binding():
+    dev = torch.device("cuda:0")
+    q = torch.zeros(1, 1, 8, 32, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(gattn.GptAttnError) as ei:
+        gattn.attention_forward(q, q, q)
+    assert ei.value.status == 2  # unsupported head dim
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device=dev)
+    o, lse, _ = gattn.attention_forward(q, q, q)
+    small = torch.zeros(1, dtype=torch.float32, device=dev)
+    with pytest.raises(gattn.GptAttnError) as ei:
+        gattn.attention_backward(q, q, q, o, q, lse, workspace=small)
+    assert ei.value.status == 4
+    # An empty sequence is a no-op.
+    z = torch.zeros(2, 3, 0, 64, dtype=torch.bfloat16, device=dev)
+    o, lse, _ = gattn.attention_forward(z, z, z)
+    assert o.shape == z.shape
