@@ -1,0 +1,236 @@
+"""Benchmark: causal attention forward + backward TFLOP/s on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: gpt_attn_fwd (O, o_lo, LSE), then the backward's
+two phases gpt_attn_bwd_prep (delta, dQ zero-fill) and gpt_attn_bwd_main
+(dQ, dK, dV), all through the C ABI on torch's current stream.
+
+FLOPs are the causal algorithmic count: only the T(T+1)/2 unmasked (query,
+key) pairs per head, 4*D per pair forward (QK^T and PV) and 10*D per pair
+backward (QK^T recompute, dP, dV, dK, dQ).
+
+Prints one JSON line. ``roofline`` describes the dominant kernel (the
+backward main kernel): its algorithmic FLOPs per launch over its average
+launch duration, timed with HIP events on the launch stream inside the timed
+region. ``cpu_baseline`` times the fp64 oracle on a bounded sample of the
+same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "gpt2_124m_bf16_b12_h12_t1024"
+DOMINANT_KERNEL = "attn_bwd_main_bf16_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bwd_main_bf16_gpt2_124m_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "causal_self_attention_amd", "csrc", f)
+                  for f in ("attn_bwd_bf16.hip", "attn_common.h", "attn_launch.h")]
+
+
+def flops(w):
+    pairs = w.B * w.H * w.T * (w.T + 1) // 2
+    return 4 * w.D * pairs, 10 * w.D * pairs
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(n_launch_flop: int):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when it is missing or was taken on other kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, max_heads: int, threads: int):
+    """Oracle (fp64, plain C, threads over heads) on the first max_heads heads
+    of the same inputs: forward plus backward. Scaled to TFLOP/s with the
+    same algorithmic FLOP count as the GPU figure."""
+    import oracle
+    n_heads = w.B * w.H
+    heads = min(max_heads, n_heads)
+    arr = {n: inp[n].double().numpy().reshape(n_heads, w.T, w.D)[:heads].copy()
+           for n in ("q", "k", "v", "do")}
+    oracle._load()
+    t0 = time.perf_counter()
+    oracle.attn_fwd(arr["q"], arr["k"], arr["v"], nthreads=threads)
+    oracle.attn_bwd(arr["q"], arr["k"], arr["v"], arr["do"], nthreads=threads)
+    dt = time.perf_counter() - t0
+    pairs = heads * w.T * (w.T + 1) // 2
+    fl = 14 * w.D * pairs
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": min(threads, heads),
+            "kind": "oracle",
+            "sample": f"{heads} of {n_heads} heads (T={w.T}, D={w.D}), forward + backward, "
+                      f"fp64, {dt:.2f} s wall"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run 5 plain device-to-device copies of this many MiB (the "
+                         "known-size reference for HBM byte counters) and exit")
+    ap.add_argument("--cpu-heads", type=int, default=64,
+                    help="heads of the workload the oracle baseline runs")
+    ap.add_argument("--cpu-threads", type=int, default=16)
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}): the attention heads are independent, so a multi-GPU run is the "
+              f"same kernel on each GPU's share of the heads.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+        return 0
+
+    import causal_self_attention_amd as gattn
+    from causal_self_attention_amd.inputs import WORKLOADS, workload_inputs
+
+    if not os.path.exists(gattn.library_path()):
+        from causal_self_attention_amd import build
+        build.build()
+    w = WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        print("bench.py times the bf16 path; pick a bf16 workload", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    inp = workload_inputs(w, seed=args.seed)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    o_lo = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    ws = torch.empty(gattn.gpt_attn_bwd_workspace_bytes("bf16", w.B, w.H, w.T, w.D) // 4,
+                     dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    n_ev = args.steps
+    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(n_ev)] for name in ("fwd", "prep", "main")}
+
+    def step(i=None):
+        if i is None:
+            gattn.gpt_attn_fwd(q, k, v, o, o_lo, lse, stream)
+            gattn.gpt_attn_bwd_prep(o, o_lo, do, dq, ws, stream)
+            gattn.gpt_attn_bwd_main(q, k, v, do, lse, dq, dk, dv, ws, stream)
+            return
+        a, b = ev["fwd"][i]
+        a.record(stream)
+        gattn.gpt_attn_fwd(q, k, v, o, o_lo, lse, stream)
+        b.record(stream)
+        a, b = ev["prep"][i]
+        a.record(stream)
+        gattn.gpt_attn_bwd_prep(o, o_lo, do, dq, ws, stream)
+        b.record(stream)
+        a, b = ev["main"][i]
+        a.record(stream)
+        gattn.gpt_attn_bwd_main(q, k, v, do, lse, dq, dk, dv, ws, stream)
+        b.record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    avg = {name: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+           for name, pairs in ev.items()}
+    fwd_flop, bwd_flop = flops(w)
+    value = (fwd_flop + bwd_flop) / (ms_per_step * 1e-3) / 1e12
+    if not (torch.isfinite(dq).all() and torch.isfinite(o.float()).all()):
+        print("non-finite outputs", file=sys.stderr)
+        return 1
+
+    main_tflops = bwd_flop / (avg["main"] * 1e-3) / 1e12
+    traffic = load_traffic(bwd_flop)
+    out = {
+        "metric": "causal attn fwd+bwd TFLOP/s and % bf16 MFMA peak, GPT-2 124M shape",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "D": w.D,
+                   "causal": True, "scale": 1.0 / w.D ** 0.5, "seed": args.seed,
+                   "layout": "BHTD", "pct_of_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2)},
+        "fwd": {"ms": round(avg["fwd"], 5),
+                "tflops": round(fwd_flop / (avg["fwd"] * 1e-3) / 1e12, 2),
+                "pct_peak": round(100 * fwd_flop / (avg["fwd"] * 1e-3) / 1e12 /
+                                  PEAK_MFMA_TFLOPS, 2)},
+        "bwd": {"ms": round(avg["prep"] + avg["main"], 5), "prep_ms": round(avg["prep"], 5),
+                "main_ms": round(avg["main"], 5),
+                "tflops": round(bwd_flop / ((avg["prep"] + avg["main"]) * 1e-3) / 1e12, 2),
+                "pct_peak": round(100 * bwd_flop / ((avg["prep"] + avg["main"]) * 1e-3) /
+                                  1e12 / PEAK_MFMA_TFLOPS, 2)},
+        "roofline": {"kernel": DOMINANT_KERNEL, "bound": "mfma",
+                     "achieved": round(main_tflops, 2), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(main_tflops / PEAK_MFMA_TFLOPS, 4),
+                     "avg_launch_ms": round(avg["main"], 5),
+                     "flop_per_launch": bwd_flop, "traffic": traffic},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads, args.cpu_threads)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

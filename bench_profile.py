@@ -1,0 +1,218 @@
+"""rocprofv3 passes behind the benchmark's kernel figures; writes summaries
+into profiles/.
+
+  python bench_profile.py [--out gpurun_out/prof] [--workload NAME]
+
+Summaries are written to <out>/summaries/ (copy them into profiles/ to
+commit them). Runs, each as its own rocprofv3 process over bench.py (the
+program directly after ``--``):
+  1. --kernel-trace --stats: per-kernel call counts and average durations
+     -> profiles/kernel_trace_<workload>.md
+  2. --pmc FETCH_SIZE, then 3. --pmc WRITE_SIZE over the same command, and
+  4./5. the same two counters over a plain device copy of known size (the
+     scale that turns the counters' KiB into bytes)
+     -> profiles/hbm_traffic_<workload>.md and, for the dominant kernel,
+        profiles/attn_bwd_main_bf16_gpt2_124m_traffic.json (read by bench.py,
+        keyed by a hash of the kernel source so a stale figure is dropped).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+CALIB_MIB = 256
+
+
+def portable(cmd):
+    """The command as text, with the interpreter as python3 and paths relative
+    to the repository root."""
+    text = " ".join(cmd).replace(sys.executable, "python3")
+    return text.replace(ROOT + "/", "")
+
+
+def log(msg):
+    print(f"[bench_profile {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+SUMMARIZE_ONLY = False
+
+
+def run_rocprof(flags, prog_args, out_dir, timeout_s):
+    os.makedirs(out_dir, exist_ok=True)
+    cmd = ["timeout", "-s", "KILL", str(timeout_s), "rocprofv3", *flags, "-d", out_dir,
+           "-o", "run", "--output-format", "csv", "--", sys.executable, *prog_args]
+    if SUMMARIZE_ONLY:
+        return cmd, 0
+    log("running: " + " ".join(cmd))
+    env = dict(os.environ, TMPDIR="/tmp")
+    r = subprocess.run(cmd, cwd="/tmp", env=env, capture_output=True, text=True)
+    with open(os.path.join(out_dir, "console.log"), "w") as f:
+        f.write(r.stdout)
+        f.write(r.stderr)
+    log(f"exit {r.returncode}; last output: {r.stdout.strip().splitlines()[-1:]}")
+    # rocprofv3 may exit non-zero after a complete run; the CSVs decide.
+    return cmd, r.returncode
+
+
+def find_csv(out_dir, suffix):
+    hits = sorted(glob.glob(os.path.join(out_dir, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {out_dir}")
+    return hits[-1]
+
+
+def read_rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def col(row, *names):
+    low = {k.lower(): v for k, v in row.items()}
+    for n in names:
+        if n.lower() in low:
+            return low[n.lower()]
+    raise KeyError(f"none of {names} in {list(row)}")
+
+
+KERNELS = ("attn_fwd_bf16_kernel", "attn_bwd_prep_bf16_kernel", "attn_bwd_main_bf16_kernel",
+           "attn_fwd_f32_kernel", "attn_bwd_prep_f32_kernel", "attn_bwd_dkdv_f32_kernel",
+           "attn_bwd_dq_f32_kernel")
+
+
+def short_name(kernel_name):
+    for key in KERNELS:
+        if key in kernel_name:
+            return key
+    return kernel_name.split("(")[0][:80]
+
+
+def counter_per_dispatch(path, counter):
+    """Average counter value per dispatch, per kernel (short name)."""
+    per = {}
+    for row in read_rows(path):
+        if col(row, "Counter_Name") != counter:
+            continue
+        k = short_name(col(row, "Kernel_Name"))
+        per.setdefault(k, []).append(float(col(row, "Counter_Value")))
+    return {k: (sum(v) / len(v), len(v)) for k, v in per.items()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    ap.add_argument("--workload", default=bench.DEFAULT_WORKLOAD)
+    ap.add_argument("--skip-trace", action="store_true")
+    ap.add_argument("--skip-pmc", action="store_true")
+    ap.add_argument("--summarize-only", action="store_true",
+                    help="rebuild the summaries from CSVs already under --out")
+    args = ap.parse_args()
+    global SUMMARIZE_ONLY
+    SUMMARIZE_ONLY = args.summarize_only
+    out = os.path.abspath(args.out)
+    bench_py = os.path.join(ROOT, "bench.py")
+    from causal_self_attention_amd.inputs import WORKLOADS
+    w = WORKLOADS[args.workload]
+    short = args.workload
+    prof_dir = os.path.join(out, "summaries")
+    os.makedirs(prof_dir, exist_ok=True)
+
+    if not args.skip_trace:
+        prog = [bench_py, "--workload", args.workload, "--steps", "20", "--warmup", "5",
+                "--no-cpu-baseline"]
+        cmd, _ = run_rocprof(["--kernel-trace", "--stats"], prog, os.path.join(out, "trace"),
+                             300)
+        stats = read_rows(find_csv(os.path.join(out, "trace"), "kernel_stats.csv"))
+        lines = [f"# Kernel trace: {args.workload}", "",
+                 f"Workload: B={w.B} H={w.H} T={w.T} D={w.D} {w.dtype}, causal; 5 warm-up "
+                 "+ 20 timed steps of bench.py (one step = forward, backward prep, backward "
+                 "main).", "", "Command (run from /tmp with TMPDIR=/tmp; paths relative to the repository root):", "",
+                 "    " + portable(cmd[4:]), "",
+                 "| kernel | calls | avg us | min us | max us | share of GPU time |",
+                 "|---|---|---|---|---|---|"]
+        for row in stats:
+            lines.append("| {} | {} | {:.2f} | {:.2f} | {:.2f} | {:.1f}% |".format(
+                short_name(col(row, "Name", "KernelName", "Kernel_Name")), col(row, "Calls"),
+                float(col(row, "AverageNs")) / 1e3, float(col(row, "MinNs")) / 1e3,
+                float(col(row, "MaxNs")) / 1e3, float(col(row, "Percentage"))))
+        with open(os.path.join(prof_dir, f"kernel_trace_{short}.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        log("kernel trace summary written")
+
+    if args.skip_pmc:
+        return 0
+    prog = [bench_py, "--workload", args.workload, "--steps", "3", "--warmup", "1",
+            "--no-cpu-baseline"]
+    calib = [bench_py, "--calibrate-copy-mib", str(CALIB_MIB)]
+    res, cmds = {}, {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        for label, p in (("attn", prog), ("copy", calib)):
+            d = os.path.join(out, f"pmc_{counter}_{label}")
+            cmd, _ = run_rocprof(["--pmc", counter], p, d, 120)
+            cmds[(counter, label)] = portable(cmd[4:])
+            res[(counter, label)] = counter_per_dispatch(find_csv(d, "counter_collection.csv"),
+                                                         counter)
+    copy_bytes = CALIB_MIB << 20
+
+    def copy_kib(counter):
+        vals = [v for k, (v, n) in res[(counter, "copy")].items()]
+        return max(vals)  # the copy kernel is the only large dispatch in that run
+
+    f_fetch = copy_bytes / (copy_kib("FETCH_SIZE") * 1024.0)
+    f_write = copy_bytes / (copy_kib("WRITE_SIZE") * 1024.0)
+    fwd_flop, bwd_flop = bench.flops(w)
+    E = w.B * w.H * w.T * w.D
+    R = w.B * w.H * w.T
+    algo = {  # compulsory bytes per launch, bf16 inputs, fp32 gradients
+        "attn_fwd_bf16_kernel": 3 * 2 * E + 2 * 2 * E + 4 * R,            # q,k,v in; o, o_lo, lse out
+        "attn_bwd_prep_bf16_kernel": 3 * 2 * E + 4 * R + 4 * E,           # o, o_lo, dout in; delta, dq=0
+        "attn_bwd_main_bf16_kernel": 4 * 2 * E + 8 * R + 3 * 4 * E,       # q,k,v,dout,lse,delta; dq,dk,dv
+    }
+    lines = [f"# HBM traffic per dispatch: {args.workload}", "",
+             f"Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one rocprofv3 --pmc run "
+             f"each), scaled by what the same counters read for a plain {CALIB_MIB} MiB "
+             f"device copy: fetch x{f_fetch:.4f}, write x{f_write:.4f}.", "",
+             "Commands (run from /tmp with TMPDIR=/tmp; paths relative to the repository "
+             "root):", ""]
+    for (c, l), cmd in cmds.items():
+        lines.append(f"    {cmd}")
+    lines += ["", "| kernel | fetch MB | write MB | total MB | algorithmic MB | ratio |",
+              "|---|---|---|---|---|---|"]
+    per_kernel = {}
+    for k in sorted(res[("FETCH_SIZE", "attn")]):
+        fk = res[("FETCH_SIZE", "attn")][k][0] * 1024 * f_fetch
+        wk = res[("WRITE_SIZE", "attn")].get(k, (0.0, 0))[0] * 1024 * f_write
+        per_kernel[k] = (fk, wk)
+        a = algo.get(k)
+        lines.append("| {} | {:.2f} | {:.2f} | {:.2f} | {} | {} |".format(
+            k, fk / 1e6, wk / 1e6, (fk + wk) / 1e6, f"{a / 1e6:.2f}" if a else "-",
+            f"{(fk + wk) / a:.2f}" if a else "-"))
+    with open(os.path.join(prof_dir, f"hbm_traffic_{short}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    dk = bench.DOMINANT_KERNEL
+    if dk in per_kernel and args.workload == bench.DEFAULT_WORKLOAD:
+        fk, wk = per_kernel[dk]
+        rec = {"kernel": dk, "workload": args.workload,
+               "kernel_source_sha256_16": bench.kernel_source_hash(),
+               "fetch_bytes_per_launch": round(fk), "write_bytes_per_launch": round(wk),
+               "hbm_bytes_per_launch": round(fk + wk),
+               "algorithmic_bytes_per_launch": algo[dk],
+               "copy_scale": {"fetch": f_fetch, "write": f_write, "copy_bytes": copy_bytes},
+               "commands": [cmds[k] for k in sorted(cmds)]}
+        with open(os.path.join(prof_dir, os.path.basename(bench.TRAFFIC_FILE)), "w") as f:
+            json.dump(rec, f, indent=1)
+    log("traffic summaries written")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

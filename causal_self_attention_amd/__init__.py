@@ -11,6 +11,8 @@ The names mirror the C entry points:
 
   gpt_attn_fwd(q, k, v, o, o_lo, lse)                -> None (writes o, o_lo, lse)
   gpt_attn_bwd(q, k, v, o, o_lo, dout, lse, dq, dk, dv, workspace) -> None
+  gpt_attn_bwd_prep(o, o_lo, dout, dq, workspace)     -> None (phase 1 of bwd)
+  gpt_attn_bwd_main(q, k, v, dout, lse, dq, dk, dv, workspace) -> None (phase 2)
   gpt_attn_bwd_workspace_bytes(dtype, B, H, T, D)    -> int
   gpt_attn_status_string(status)                     -> str
   gpt_attn_abi_version()                             -> int
@@ -28,8 +30,8 @@ import os
 
 __all__ = [
     "GptAttnError", "library_path", "load_library", "gpt_attn_fwd", "gpt_attn_bwd",
-    "gpt_attn_bwd_workspace_bytes", "gpt_attn_status_string", "gpt_attn_abi_version",
-    "attention_forward", "attention_backward", "DTYPE_CODES",
+    "gpt_attn_bwd_prep", "gpt_attn_bwd_main", "gpt_attn_bwd_workspace_bytes",
+    "gpt_attn_status_string", "gpt_attn_abi_version", "attention_forward", "attention_backward", "DTYPE_CODES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -41,8 +43,9 @@ GPT_ATTN_BF16 = 1
 DTYPE_CODES = {"f32": GPT_ATTN_F32, "bf16": GPT_ATTN_BF16}
 
 #: every symbol include/gpt_attn.h declares
-EXPORTED_SYMBOLS = ("gpt_attn_fwd", "gpt_attn_bwd", "gpt_attn_bwd_workspace_bytes",
-                    "gpt_attn_status_string", "gpt_attn_abi_version")
+EXPORTED_SYMBOLS = ("gpt_attn_fwd", "gpt_attn_bwd", "gpt_attn_bwd_prep", "gpt_attn_bwd_main",
+                    "gpt_attn_bwd_workspace_bytes", "gpt_attn_status_string",
+                    "gpt_attn_abi_version")
 
 
 class GptAttnError(RuntimeError):
@@ -70,6 +73,10 @@ def load_library():
     lib.gpt_attn_bwd.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                  vp]
     lib.gpt_attn_bwd.restype = i
+    lib.gpt_attn_bwd_prep.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
+    lib.gpt_attn_bwd_prep.restype = i
+    lib.gpt_attn_bwd_main.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gpt_attn_bwd_main.restype = i
     lib.gpt_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.gpt_attn_bwd_workspace_bytes.restype = sz
     lib.gpt_attn_status_string.argtypes = [i]
@@ -146,6 +153,31 @@ def gpt_attn_bwd(q, k, v, o, o_lo, dout, lse, dq, dk, dv, workspace, stream=None
                                      _stream(q.device, stream))
     if st != 0:
         raise GptAttnError("gpt_attn_bwd", st)
+
+
+def _ws_bytes(workspace) -> int:
+    return workspace.numel() * workspace.element_size() if workspace is not None else 0
+
+
+def gpt_attn_bwd_prep(o, o_lo, dout, dq, workspace, stream=None) -> None:
+    """Enqueue the backward's preprocess phase (delta, and dq zeroing)."""
+    B, H, T, D = _bhtd(o)
+    st = load_library().gpt_attn_bwd_prep(_dtype_code(o), B, H, T, D, _ptr(o), _ptr(o_lo),
+                                          _ptr(dout), _ptr(dq), _ptr(workspace),
+                                          _ws_bytes(workspace), _stream(o.device, stream))
+    if st != 0:
+        raise GptAttnError("gpt_attn_bwd_prep", st)
+
+
+def gpt_attn_bwd_main(q, k, v, dout, lse, dq, dk, dv, workspace, stream=None) -> None:
+    """Enqueue the backward's main phase (needs gpt_attn_bwd_prep first)."""
+    B, H, T, D = _bhtd(q)
+    st = load_library().gpt_attn_bwd_main(_dtype_code(q), B, H, T, D, _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                          _ptr(workspace), _ws_bytes(workspace),
+                                          _stream(q.device, stream))
+    if st != 0:
+        raise GptAttnError("gpt_attn_bwd_main", st)
 
 
 def attention_forward(q, k, v, stream=None, keep_o_lo: bool = True):

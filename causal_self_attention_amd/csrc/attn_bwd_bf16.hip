@@ -283,17 +283,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
-                           const void* o_lo, const void* dout, const float* lse, float* dq,
-                           float* dk, float* dv, float* delta, int n_heads, int T,
-                           hipStream_t stream) {
+hipError_t launch_bwd_prep_bf16(const void* o, const void* o_lo, const void* dout, float* dq,
+                                float* delta, int n_heads, int T, hipStream_t stream) {
   const long long rows = (long long)n_heads * T;
   const unsigned prep_blocks = (unsigned)((rows * 8 + 255) / 256);
   hipLaunchKernelGGL(attn_bwd_prep_bf16_kernel, dim3(prep_blocks), dim3(256), 0, stream,
                      static_cast<const bf16*>(o), static_cast<const bf16*>(o_lo),
                      static_cast<const bf16*>(dout), delta, dq, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_main_bf16(const void* q, const void* k, const void* v, const void* dout,
+                                const float* lse, const float* delta, float* dq, float* dk,
+                                float* dv, int n_heads, int T, hipStream_t stream) {
   const int n_ktiles = (T + kBK - 1) / kBK;
   const float scale = 0.125f;  // 1/sqrt(64)
   hipLaunchKernelGGL(attn_bwd_main_bf16_kernel, dim3(tiled_grid(n_heads, n_ktiles)),

@@ -245,19 +245,23 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
-                          const float* dout, const float* lse, float* dq, float* dk, float* dv,
-                          float* delta, int n_heads, int T, hipStream_t stream) {
+hipError_t launch_bwd_prep_f32(const float* o, const float* dout, float* delta, int n_heads,
+                               int T, hipStream_t stream) {
   const long long rows = (long long)n_heads * T;
   hipLaunchKernelGGL(attn_bwd_prep_f32_kernel, dim3((unsigned)((rows * 8 + 255) / 256)),
                      dim3(256), 0, stream, o, dout, delta, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_main_f32(const float* q, const float* k, const float* v,
+                               const float* dout, const float* lse, const float* delta,
+                               float* dq, float* dk, float* dv, int n_heads, int T,
+                               hipStream_t stream) {
   const int n_tiles = (T + 31) / 32;
   const dim3 grid((unsigned)n_heads * n_tiles);
   hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel, grid, dim3(64), 0, stream, q, k, v, dout, lse,
                      delta, dk, dv, T, n_tiles, 0.125f);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_bwd_dq_f32_kernel, grid, dim3(64), 0, stream, q, k, v, dout, lse, delta,
                      dq, T, n_tiles, 0.125f);

@@ -44,14 +44,18 @@ inline unsigned tiled_grid(int n_heads, int n_tiles) {
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, void* o_lo,
                            float* lse, int n_heads, int T, hipStream_t stream);
-hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
-                           const void* o_lo, const void* dout, const float* lse, float* dq,
-                           float* dk, float* dv, float* delta, int n_heads, int T,
-                           hipStream_t stream);
+hipError_t launch_bwd_prep_bf16(const void* o, const void* o_lo, const void* dout, float* dq,
+                                float* delta, int n_heads, int T, hipStream_t stream);
+hipError_t launch_bwd_main_bf16(const void* q, const void* k, const void* v, const void* dout,
+                                const float* lse, const float* delta, float* dq, float* dk,
+                                float* dv, int n_heads, int T, hipStream_t stream);
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           int n_heads, int T, hipStream_t stream);
-hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
-                          const float* dout, const float* lse, float* dq, float* dk, float* dv,
-                          float* delta, int n_heads, int T, hipStream_t stream);
+hipError_t launch_bwd_prep_f32(const float* o, const float* dout, float* delta, int n_heads,
+                               int T, hipStream_t stream);
+hipError_t launch_bwd_main_f32(const float* q, const float* k, const float* v,
+                               const float* dout, const float* lse, const float* delta,
+                               float* dq, float* dk, float* dv, int n_heads, int T,
+                               hipStream_t stream);
 
 }  // namespace gpt_attn

@@ -85,6 +85,53 @@ size_t gpt_attn_bwd_workspace_bytes(int dtype, int B, int H, int T, int D) {
   return (size_t)rows * sizeof(float);
 }
 
+int gpt_attn_bwd_prep(int dtype, int B, int H, int T, int D, const void* o, const void* o_lo,
+                      const void* dout, float* dq, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  long long rows = 0;
+  const int st = check_shape(dtype, B, H, T, D, &rows);
+  if (st != GPT_ATTN_OK) return st;
+  if (rows == 0) return GPT_ATTN_OK;
+  if (!o || !dout || (dtype == GPT_ATTN_BF16 && !dq)) return GPT_ATTN_E_INVAL;
+  if (o_lo && dtype != GPT_ATTN_BF16) return GPT_ATTN_E_INVAL;
+  if (!aligned16(o) || !aligned16(o_lo) || !aligned16(dout) || !aligned16(dq))
+    return GPT_ATTN_E_ALIGN;
+  if (!workspace || workspace_bytes < (size_t)rows * sizeof(float)) return GPT_ATTN_E_WORKSPACE;
+  if (!aligned16(workspace)) return GPT_ATTN_E_ALIGN;
+  float* delta = static_cast<float*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int heads = B * H;
+  if (dtype == GPT_ATTN_BF16)
+    return launch_status(gpt_attn::launch_bwd_prep_bf16(o, o_lo, dout, dq, delta, heads, T, s));
+  return launch_status(gpt_attn::launch_bwd_prep_f32(static_cast<const float*>(o),
+                                                     static_cast<const float*>(dout), delta,
+                                                     heads, T, s));
+}
+
+int gpt_attn_bwd_main(int dtype, int B, int H, int T, int D, const void* q, const void* k,
+                      const void* v, const void* dout, const float* lse, float* dq, float* dk,
+                      float* dv, const void* workspace, size_t workspace_bytes, void* stream) {
+  long long rows = 0;
+  const int st = check_shape(dtype, B, H, T, D, &rows);
+  if (st != GPT_ATTN_OK) return st;
+  if (rows == 0) return GPT_ATTN_OK;
+  if (!q || !k || !v || !dout || !lse || !dq || !dk || !dv) return GPT_ATTN_E_INVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(lse) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return GPT_ATTN_E_ALIGN;
+  if (!workspace || workspace_bytes < (size_t)rows * sizeof(float)) return GPT_ATTN_E_WORKSPACE;
+  if (!aligned16(workspace)) return GPT_ATTN_E_ALIGN;
+  const float* delta = static_cast<const float*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int heads = B * H;
+  if (dtype == GPT_ATTN_BF16)
+    return launch_status(
+        gpt_attn::launch_bwd_main_bf16(q, k, v, dout, lse, delta, dq, dk, dv, heads, T, s));
+  return launch_status(gpt_attn::launch_bwd_main_f32(
+      static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+      static_cast<const float*>(dout), lse, delta, dq, dk, dv, heads, T, s));
+}
+
 int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const void* k,
                  const void* v, const void* o, const void* o_lo, const void* dout,
                  const float* lse, float* dq, float* dk, float* dv, void* workspace,
@@ -93,6 +140,7 @@ int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const voi
   const int st = check_shape(dtype, B, H, T, D, &rows);
   if (st != GPT_ATTN_OK) return st;
   if (rows == 0) return GPT_ATTN_OK;
+  // Validate everything both phases need before enqueuing either.
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return GPT_ATTN_E_INVAL;
   if (o_lo && dtype != GPT_ATTN_BF16) return GPT_ATTN_E_INVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
@@ -100,16 +148,11 @@ int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const voi
     return GPT_ATTN_E_ALIGN;
   if (!workspace || workspace_bytes < (size_t)rows * sizeof(float)) return GPT_ATTN_E_WORKSPACE;
   if (!aligned16(workspace)) return GPT_ATTN_E_ALIGN;
-  const int heads = B * H;
-  float* delta = static_cast<float*>(workspace);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == GPT_ATTN_BF16)
-    return launch_status(
-        gpt_attn::launch_bwd_bf16(q, k, v, o, o_lo, dout, lse, dq, dk, dv, delta, heads, T, s));
-  return launch_status(gpt_attn::launch_bwd_f32(
-      static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-      static_cast<const float*>(o), static_cast<const float*>(dout), lse, dq, dk, dv, delta,
-      heads, T, s));
+  const int r = gpt_attn_bwd_prep(dtype, B, H, T, D, o, o_lo, dout, dq, workspace,
+                                  workspace_bytes, stream);
+  if (r != GPT_ATTN_OK) return r;
+  return gpt_attn_bwd_main(dtype, B, H, T, D, q, k, v, dout, lse, dq, dk, dv, workspace,
+                           workspace_bytes, stream);
 }
 
 }  // extern "C"

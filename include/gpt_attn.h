@@ -121,6 +121,27 @@ int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const voi
                  const float* lse, float* dq, float* dk, float* dv, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/*
+ * The two phases of gpt_attn_bwd as separate calls, for callers that
+ * schedule or time them apart. gpt_attn_bwd(...) is exactly
+ * gpt_attn_bwd_prep(...) followed by gpt_attn_bwd_main(...) on one stream.
+ *
+ * gpt_attn_bwd_prep: the preprocess pass. Writes delta_i = sum_d dout_id O_id
+ *   (O = o, or o + o_lo when o_lo is given) into the first B*H*T floats of
+ *   workspace; for GPT_ATTN_BF16 it also zero-fills dq, which the main phase
+ *   accumulates into (dq may be NULL for GPT_ATTN_F32 and is not touched).
+ * gpt_attn_bwd_main: everything else. Reads delta from workspace, which must
+ *   hold the prep phase's result for the same o and dout (and, for
+ *   GPT_ATTN_BF16, dq must still hold the prep phase's zeros). Writes dq, dk,
+ *   dv. Arguments mean what they mean for gpt_attn_bwd.
+ */
+int gpt_attn_bwd_prep(int dtype, int B, int H, int T, int D, const void* o, const void* o_lo,
+                      const void* dout, float* dq, void* workspace, size_t workspace_bytes,
+                      void* stream);
+int gpt_attn_bwd_main(int dtype, int B, int H, int T, int D, const void* q, const void* k,
+                      const void* v, const void* dout, const float* lse, float* dq, float* dk,
+                      float* dv, const void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. Never NULL. */
 const char* gpt_attn_status_string(int status);
 
