@@ -37,8 +37,7 @@ namespace {
 constexpr int kBK = 128;      // keys per workgroup
 constexpr int kBQ = 64;       // queries per step
 constexpr int kThreads = 256;
-constexpr int kRowQ = 72;     // padded row of a 64-wide 16-bit LDS tile
-constexpr int kRowK = 136;    // padded row of a 128-wide 16-bit LDS tile
+constexpr int kRowQ = 72;     // padded row of a 64-wide 16-bit LDS tile (144 bytes)
 
 __global__ __launch_bounds__(256) void attn_bwd_prep_bf16_kernel(
     const bf16* __restrict__ o, const bf16* __restrict__ o_lo, const bf16* __restrict__ dout,
@@ -69,25 +68,61 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_bf16_kernel(
   if (row < rows && part == 0) delta[row] = acc;
 }
 
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
+// Stage one 64-query tile: rows of Q and dO already loaded (bf16, two 16-byte
+// chunks per tensor per thread) are converted to fp16 and written row-major;
+// threads 0..63 also write LSE*log2e and delta for the tile's rows.
+__device__ __forceinline__ void bwd_store_tile(f16* sQ, f16* sdO, float* sL, float* sD,
+                                               const bf16x8 (&xq)[2], const bf16x8 (&xd)[2],
+                                               float l2, float dl, int tid) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int c = tid + kThreads * p;  // 0..511: row c/8, 8 dims at (c%8)*8
+    const int row = c >> 3, col = (c & 7) * 8;
+    *reinterpret_cast<f16x8*>(&sQ[row * kRowQ + col]) = bf16x8_to_f16x8(xq[p]);
+    *reinterpret_cast<f16x8*>(&sdO[row * kRowQ + col]) = bf16x8_to_f16x8(xd[p]);
+  }
+  if (tid < kBQ) {
+    sL[tid] = l2;
+    sD[tid] = dl;
+  }
+}
+
+__device__ __forceinline__ void bwd_load_tile(const bf16* qh, const bf16* doh, const float* lse,
+                                              const float* delta, int qs, int T, int tid,
+                                              bf16x8 (&xq)[2], bf16x8 (&xd)[2], float& l2,
+                                              float& dl) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int c = tid + kThreads * p;
+    const int r = qs + (c >> 3), col = (c & 7) * 8;
+    xq[p] = load_bf16x8(qh + (size_t)r * kHeadDim + col, r < T);
+    xd[p] = load_bf16x8(doh + (size_t)r * kHeadDim + col, r < T);
+  }
+  const int r = qs + tid;
+  const bool ok = tid < kBQ && r < T;
+  l2 = ok ? lse[r] * kLog2e : 0.f;
+  dl = ok ? delta[r] : 0.f;
+}
+
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_main_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, float* __restrict__ dq, float* __restrict__ dk,
     float* __restrict__ dv, int n_heads, int T, int n_ktiles, float scale, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) bf16 Qs[kBQ * kRowQ];        // [q][d]
-  __shared__ __attribute__((aligned(16))) bf16 dOs[kBQ * kRowQ];       // [q][d]
-  __shared__ __attribute__((aligned(16))) f16 Qt[kHeadDim * kRowQ];    // [d][q]
-  __shared__ __attribute__((aligned(16))) f16 dOt[kHeadDim * kRowQ];   // [d][q]
-  __shared__ __attribute__((aligned(16))) f16 Kt[kHeadDim * kRowK];    // [d][key]
-  __shared__ __attribute__((aligned(16))) f16 dSs[kBQ * kRowK];        // [q][key]
-  __shared__ __attribute__((aligned(16))) float lse2s[kBQ];
-  __shared__ __attribute__((aligned(16))) float dels[kBQ];
+  // All tiles fp16, row-major; transposed operands come from lds_operand_tr.
+  __shared__ __attribute__((aligned(16))) f16 sK[kBK * kRowQ];          // [key][d]
+  __shared__ __attribute__((aligned(16))) f16 sQ[2][kBQ * kRowQ];       // [q][d]
+  __shared__ __attribute__((aligned(16))) f16 sdO[2][kBQ * kRowQ];      // [q][d]
+  __shared__ __attribute__((aligned(16))) f16 sdS[kBK * kRowQ];         // [key][q]
+  __shared__ __attribute__((aligned(16))) float sL[2][kBQ];             // LSE * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[2][kBQ];             // delta
 
   const TileMap tm = map_tile_xcd(blockIdx.x, n_heads, n_ktiles, false);
   if (!tm.valid) return;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
 
   const size_t hoff = (size_t)tm.head * (size_t)T * kHeadDim;
@@ -96,31 +131,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
   const bf16* kh = k + hoff;
   const bf16* vh = v + hoff;
   const bf16* doh = dout + hoff;
+  const float* lseh = lse + roff;
+  const float* delh = delta + roff;
 
   const int k0 = tm.tile * kBK;
   const int kw0 = k0 + wave * 32;
   const int my_key = kw0 + l32;  // the key column this lane owns
 
-  // K and V of this wave's 32 keys as B operands (lane: its key, 8 dims).
-  bf16x8 kf[4], vf[4];
+  // K and V of this wave's 32 keys as fp16 B operands (lane: its key, 8 dims).
+  f16x8 kf[4], vf[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    kf[kk] = load_bf16x8(kh + (size_t)my_key * kHeadDim + kk * 16 + 8 * hf, my_key < T);
-    vf[kk] = load_bf16x8(vh + (size_t)my_key * kHeadDim + kk * 16 + 8 * hf, my_key < T);
+    kf[kk] = bf16x8_to_f16x8(
+        load_bf16x8(kh + (size_t)my_key * kHeadDim + kk * 16 + 8 * hf, my_key < T));
+    vf[kk] = bf16x8_to_f16x8(
+        load_bf16x8(vh + (size_t)my_key * kHeadDim + kk * 16 + 8 * hf, my_key < T));
   }
-
-  // K^T of all 128 keys for the dQ product: thread takes key pair and 8 dims.
+  // All 128 keys of K, row-major fp16, for the dQ product.
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int c = tid + kThreads * p;          // 0..511
-    const int j = 2 * (c & 63), d0 = (c >> 6) * 8;
-    const bf16x8 x0 = load_bf16x8(kh + (size_t)(k0 + j) * kHeadDim + d0, k0 + j < T);
-    const bf16x8 x1 = load_bf16x8(kh + (size_t)(k0 + j + 1) * kHeadDim + d0, k0 + j + 1 < T);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      f16x2 pr = {bf16_to_f16(x0[t]), bf16_to_f16(x1[t])};
-      *reinterpret_cast<f16x2*>(&Kt[(d0 + t) * kRowK + j]) = pr;
-    }
+  for (int p = 0; p < 4; ++p) {
+    const int c = tid + kThreads * p;  // 0..1023: key c/8, 8 dims at (c%8)*8
+    const int row = c >> 3, col = (c & 7) * 8;
+    *reinterpret_cast<f16x8*>(&sK[row * kRowQ + col]) = bf16x8_to_f16x8(
+        load_bf16x8(kh + (size_t)(k0 + row) * kHeadDim + col, k0 + row < T));
   }
 
   f32x16 dvacc[2], dkacc[2];
@@ -132,42 +165,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
       dkacc[db][r] = 0.f;
     }
 
-  for (int qs = k0; qs < T; qs += kBQ) {
-    // ---- stage Q and dO tiles (row-major and transposed), LSE*log2e, delta
-    {
-      const int qa = 2 * (tid & 31), d0 = (tid >> 5) * 8;
-      const int r0 = qs + qa, r1 = qs + qa + 1;
-      const bf16x8 x0 = load_bf16x8(qh + (size_t)r0 * kHeadDim + d0, r0 < T);
-      const bf16x8 x1 = load_bf16x8(qh + (size_t)r1 * kHeadDim + d0, r1 < T);
-      const bf16x8 y0 = load_bf16x8(doh + (size_t)r0 * kHeadDim + d0, r0 < T);
-      const bf16x8 y1 = load_bf16x8(doh + (size_t)r1 * kHeadDim + d0, r1 < T);
-      *reinterpret_cast<bf16x8*>(&Qs[qa * kRowQ + d0]) = x0;
-      *reinterpret_cast<bf16x8*>(&Qs[(qa + 1) * kRowQ + d0]) = x1;
-      *reinterpret_cast<bf16x8*>(&dOs[qa * kRowQ + d0]) = y0;
-      *reinterpret_cast<bf16x8*>(&dOs[(qa + 1) * kRowQ + d0]) = y1;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        f16x2 pq = {bf16_to_f16(x0[t]), bf16_to_f16(x1[t])};
-        f16x2 pd = {bf16_to_f16(y0[t]), bf16_to_f16(y1[t])};
-        *reinterpret_cast<f16x2*>(&Qt[(d0 + t) * kRowQ + qa]) = pq;
-        *reinterpret_cast<f16x2*>(&dOt[(d0 + t) * kRowQ + qa]) = pd;
-      }
-      if (tid < kBQ) {
-        const int r = qs + tid;
-        lse2s[tid] = r < T ? lse[roff + r] * kLog2e : 0.f;
-        dels[tid] = r < T ? delta[roff + r] : 0.f;
-      }
-    }
-    __syncthreads();
+  bf16x8 xq[2], xd[2];
+  float l2 = 0.f, dl = 0.f;
+  bwd_load_tile(qh, doh, lseh, delh, k0, T, tid, xq, xd, l2, dl);
+  bwd_store_tile(sQ[0], sdO[0], sL[0], sD[0], xq, xd, l2, dl, tid);
+  __syncthreads();
 
-    // ---- per wave: S, P, dP, dS for its 32 keys x 64 queries
-    f16x8 pbf[2][2], dsbf[2][2];
-    bool act[2];
+  int buf = 0;
+  for (int qs = k0; qs < T; qs += kBQ, buf ^= 1) {
+    // Prefetch the next tile into registers while this one is computed.
+    const bool has_next = qs + kBQ < T;
+    if (has_next) bwd_load_tile(qh, doh, lseh, delh, qs + kBQ, T, tid, xq, xd, l2, dl);
+
+    const f16* cQ = sQ[buf];
+    const f16* cdO = sdO[buf];
+    const float* cL = sL[buf];
+    const float* cD = sD[buf];
+
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const int qb0 = qs + mb * 32;
-      act[mb] = (qb0 < T) && (kw0 < T) && (kw0 <= qb0 + 31);
-      if (!act[mb]) continue;
+      // Wave-uniform: does this 32x32 block hold any visible (key <= query) pair?
+      if (!(qb0 < T && kw0 < T && kw0 <= qb0 + 31)) continue;
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -177,56 +196,49 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
       const int arow = (mb * 32 + perm32(l32)) * kRowQ + 8 * hf;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(&Qs[arow + kk * 16]), kf[kk], s);
-        dp = mfma32x32x16(*reinterpret_cast<const bf16x8*>(&dOs[arow + kk * 16]), vf[kk], dp);
+        s = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cQ[arow + kk * 16]), kf[kk], s);
+        dp = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cdO[arow + kk * 16]), vf[kk], dp);
       }
       const bool need_mask = (qb0 < kw0 + 31) || (kw0 + 32 > T) || (qb0 + 32 > T);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         // Register 8c + t of half hf is query qb0 + 16c + 8hf + t.
         const int qoff = mb * 32 + 16 * c + 8 * hf;
-        const f32x4 L0 = *reinterpret_cast<const f32x4*>(&lse2s[qoff]);
-        const f32x4 L1 = *reinterpret_cast<const f32x4*>(&lse2s[qoff + 4]);
-        const f32x4 E0 = *reinterpret_cast<const f32x4*>(&dels[qoff]);
-        const f32x4 E1 = *reinterpret_cast<const f32x4*>(&dels[qoff + 4]);
+        const f32x4 L0 = *reinterpret_cast<const f32x4*>(&cL[qoff]);
+        const f32x4 L1 = *reinterpret_cast<const f32x4*>(&cL[qoff + 4]);
+        const f32x4 E0 = *reinterpret_cast<const f32x4*>(&cD[qoff]);
+        const f32x4 E1 = *reinterpret_cast<const f32x4*>(&cD[qoff + 4]);
         float p[8], ds[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const float lse2 = t < 4 ? L0[t] : L1[t - 4];
           const float del = t < 4 ? E0[t] : E1[t - 4];
-          const int qi = qs + qoff + t;
           float pv = fast_exp2(fmaf(s[8 * c + t], scale_log2, -lse2));
-          if (need_mask && (my_key > qi || my_key >= T || qi >= T)) pv = 0.f;
+          if (need_mask) {
+            const int qi = qs + qoff + t;
+            if (my_key > qi || my_key >= T || qi >= T) pv = 0.f;
+          }
           p[t] = pv;
           ds[t] = pv * (dp[8 * c + t] - del);
         }
-        pbf[mb][c] = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-        dsbf[mb][c] = pack_f16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) dSs[(qoff + t) * kRowK + wave * 32 + l32] = dsbf[mb][c][t];
-      }
-    }
-
-    // ---- dV^T += dO^T P, dK^T += Q^T dS (k steps of 16 queries)
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      if (!act[mb]) continue;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
+        const f16x8 pf = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+        const f16x8 dsf = pack_f16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+        // dS^T row of this lane's key: 8 consecutive queries, one 16-byte write.
+        *reinterpret_cast<f16x8*>(&sdS[(wave * 32 + l32) * kRowQ + qoff]) = dsf;
+        // dV^T += dO^T P and dK^T += Q^T dS over these 16 queries.
         const int ks = 2 * mb + c;
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          const int aoff = (db * 32 + l32) * kRowQ + ks * 16 + 8 * hf;
-          dvacc[db] = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&dOt[aoff]), pbf[mb][c],
+          dvacc[db] = mfma32x32x16_f16(lds_operand_tr(cdO, kRowQ, ks * 16, db * 32, lane), pf,
                                        dvacc[db]);
-          dkacc[db] = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&Qt[aoff]), dsbf[mb][c],
+          dkacc[db] = mfma32x32x16_f16(lds_operand_tr(cQ, kRowQ, ks * 16, db * 32, lane), dsf,
                                        dkacc[db]);
         }
       }
     }
     __syncthreads();
 
-    // ---- dQ block (queries 32qb.., dims 32db..) = dS K over the 128 keys
+    // dQ block (queries 32qb.., dims 32db..) = dS K over the 128 keys.
     {
       const int qb = wave >> 1, db = wave & 1;
       const int qb0 = qs + qb * 32;
@@ -242,11 +254,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
           const int kws = k0 + (ks >> 1) * 32;
           if (kws >= T || kws > qb0 + 31) continue;
           any = true;
-          const f16x8 a =
-              *reinterpret_cast<const f16x8*>(&dSs[(qb * 32 + l32) * kRowK + ks * 16 + 8 * hf]);
-          const f16x8 b =
-              *reinterpret_cast<const f16x8*>(&Kt[(db * 32 + l32) * kRowK + ks * 16 + 8 * hf]);
-          acc = mfma32x32x16_f16(a, b, acc);
+          acc = mfma32x32x16_f16(lds_operand_tr(sdS, kRowQ, ks * 16, qb * 32, lane),
+                                 lds_operand_tr(sK, kRowQ, ks * 16, db * 32, lane), acc);
         }
         if (any) {
           float* dqh = dq + hoff;
@@ -259,6 +268,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
         }
       }
     }
+    if (has_next) bwd_store_tile(sQ[buf ^ 1], sdO[buf ^ 1], sL[buf ^ 1], sD[buf ^ 1], xq, xd, l2,
+                                 dl, tid);
     __syncthreads();
   }
 

@@ -95,4 +95,50 @@ __device__ __forceinline__ int perm32(int r) {
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// Eight bf16 -> eight fp16 (see bf16_to_f16).
+__device__ __forceinline__ f16x8 bf16x8_to_f16x8(bf16x8 x) {
+  return pack_f16x8((float)x[0], (float)x[1], (float)x[2], (float)x[3], (float)x[4],
+                    (float)x[5], (float)x[6], (float)x[7]);
+}
+
+__device__ __forceinline__ f16x8 zero_f16x8() {
+  i32x4 z = {0, 0, 0, 0};
+  return __builtin_bit_cast(f16x8, z);
+}
+
+// ds_read_b64_tr_b16 (CDNA4): each lane supplies the LDS address of four
+// consecutive 16-bit elements; inside every group of 16 lanes the 16 x 4
+// block is transposed, so that lane i of the group receives element i of the
+// four rows that lanes 4e..4e+3 (e = 0..3) addressed. (Characterised on the
+// device with an in-bounds probe.)
+__device__ __forceinline__ f16x4 lds_read_tr16(const f16* p) {
+#if __HIP_DEVICE_COMPILE__
+  typedef __fp16 half4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+  typedef _Float16 __attribute__((address_space(3))) lds_f16;
+  typedef half4 __attribute__((address_space(3))) lds_half4;
+  return __builtin_bit_cast(f16x4,
+                            __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_half4*)((lds_f16*)p)));
+#else
+  (void)p;
+  f16x4 z = {};
+  return z;
+#endif
+}
+
+// MFMA 32x32x16 operand whose k index runs down the rows of an LDS tile
+// stored [k][n] (n contiguous, row stride ld elements, rows 8-byte aligned):
+// lane l receives tile[k0 + 8h + t][n0 + l % 32], t = 0..7, h = l / 32 --
+// i.e. the A operand of a product whose M index is the tile's column, or the
+// B operand whose N index is. Two transposing reads of four rows each.
+__device__ __forceinline__ f16x8 lds_operand_tr(const f16* tile, int ld, int k0, int n0,
+                                                int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int row = k0 + 8 * (g >> 1) + (i >> 2);
+  const int col = n0 + 16 * (g & 1) + 4 * (i & 3);
+  const f16x4 lo = lds_read_tr16(tile + row * ld + col);
+  const f16x4 hi = lds_read_tr16(tile + (row + 4) * ld + col);
+  f16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return r;
+}
+
 }  // namespace gpt_attn
