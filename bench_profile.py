@@ -32,6 +32,18 @@ import bench  # noqa: E402
 
 CALIB_MIB = 256
 
+# SQ counter passes (at most 8 SQ and 2 GRBM counters per rocprofv3 run).
+SQ_PASSES = [
+    ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+     "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"],
+    ["SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_LDS",
+     "SQ_ACTIVE_INST_VALU", "SQ_LDS_IDX_ACTIVE", "SQ_ACTIVE_INST_ANY",
+     "SQ_VALU_MFMA_COEXEC_CYCLES"],
+    ["SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_VALU_CVT", "SQ_INSTS_SALU", "SQ_ACTIVE_INST_VMEM",
+     "SQ_INSTS_VMEM_RD", "SQ_LDS_ADDR_CONFLICT", "SQ_INSTS_LDS_LOAD_BANDWIDTH",
+     "SQ_INSTS_BRANCH"],
+]
+
 
 def portable(cmd):
     """The command as text, with the interpreter as python3 and paths relative
@@ -113,6 +125,8 @@ def main():
     ap.add_argument("--workload", default=bench.DEFAULT_WORKLOAD)
     ap.add_argument("--skip-trace", action="store_true")
     ap.add_argument("--skip-pmc", action="store_true")
+    ap.add_argument("--sq", action="store_true",
+                    help="run only the SQ counter passes -> sq_counters_<workload>.md")
     ap.add_argument("--summarize-only", action="store_true",
                     help="rebuild the summaries from CSVs already under --out")
     args = ap.parse_args()
@@ -125,6 +139,36 @@ def main():
     short = args.workload
     prof_dir = os.path.join(out, "summaries")
     os.makedirs(prof_dir, exist_ok=True)
+
+    if args.sq:
+        prog = [bench_py, "--workload", args.workload, "--steps", "2", "--warmup", "1",
+                "--no-cpu-baseline"]
+        table, cmds = {}, []
+        for i, counters in enumerate(SQ_PASSES):
+            d = os.path.join(out, f"sq_pass{i}")
+            cmd, _ = run_rocprof(["--pmc", *counters], prog, d, 60)
+            cmds.append(portable(cmd[4:]))
+            path = find_csv(d, "counter_collection.csv")
+            for c in counters:
+                for kname, (val, n) in counter_per_dispatch(path, c).items():
+                    if kname in KERNELS:
+                        table.setdefault(kname, {})[c] = val
+        lines = [f"# SQ counters per dispatch: {args.workload}", "",
+                 "Average per dispatch over the profiled steps (values as rocprofv3 reports "
+                 "them, summed over the counter's instances).", "",
+                 "Commands (run from /tmp with TMPDIR=/tmp; paths relative to the repository "
+                 "root):", ""] + [f"    {c}" for c in cmds] + [""]
+        names = sorted(table)
+        lines.append("| counter | " + " | ".join(names) + " |")
+        lines.append("|---|" + "---|" * len(names))
+        for counters in SQ_PASSES:
+            for c in counters:
+                lines.append(f"| {c} | " + " | ".join(
+                    f"{table[k].get(c, float('nan')):.4g}" for k in names) + " |")
+        with open(os.path.join(prof_dir, f"sq_counters_{short}.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        log("SQ counter summary written")
+        return 0
 
     if not args.skip_trace:
         prog = [bench_py, "--workload", args.workload, "--steps", "20", "--warmup", "5",

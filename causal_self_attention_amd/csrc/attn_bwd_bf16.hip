@@ -68,40 +68,87 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_bf16_kernel(
   if (row < rows && part == 0) delta[row] = acc;
 }
 
-// Stage one 64-query tile: rows of Q and dO already loaded (bf16, two 16-byte
-// chunks per tensor per thread) are converted to fp16 and written row-major;
-// threads 0..63 also write LSE*log2e and delta for the tile's rows.
-__device__ __forceinline__ void bwd_store_tile(f16* sQ, f16* sdO, float* sL, float* sD,
-                                               const bf16x8 (&xq)[2], const bf16x8 (&xd)[2],
-                                               float l2, float dl, int tid) {
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int c = tid + kThreads * p;  // 0..511: row c/8, 8 dims at (c%8)*8
-    const int row = c >> 3, col = (c & 7) * 8;
-    *reinterpret_cast<f16x8*>(&sQ[row * kRowQ + col]) = bf16x8_to_f16x8(xq[p]);
-    *reinterpret_cast<f16x8*>(&sdO[row * kRowQ + col]) = bf16x8_to_f16x8(xd[p]);
-  }
-  if (tid < kBQ) {
-    sL[tid] = l2;
-    sD[tid] = dl;
-  }
-}
+// Loading a 64-query tile is split in two so the global loads can be issued
+// a whole step ahead: bwd_load_tile only issues raw loads (rows clamped to
+// T-1, so every address is valid, and nothing is computed from the results);
+// bwd_store_tile, a step later, zeroes rows past T, converts to fp16 and
+// writes the LDS buffers. Each thread moves two 16-byte chunks of Q and of dO
+// (row c/8, dims (c%8)*8 for c = tid, tid+256); threads 0..63 also move the
+// LSE and delta of row tid.
+struct TileRegs {
+  bf16x8 q[2], d[2];
+  float lse, del;
+};
 
 __device__ __forceinline__ void bwd_load_tile(const bf16* qh, const bf16* doh, const float* lse,
                                               const float* delta, int qs, int T, int tid,
-                                              bf16x8 (&xq)[2], bf16x8 (&xd)[2], float& l2,
-                                              float& dl) {
+                                              TileRegs& r) {
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int c = tid + kThreads * p;
-    const int r = qs + (c >> 3), col = (c & 7) * 8;
-    xq[p] = load_bf16x8(qh + (size_t)r * kHeadDim + col, r < T);
-    xd[p] = load_bf16x8(doh + (size_t)r * kHeadDim + col, r < T);
+    const int row = min(qs + (c >> 3), T - 1), col = (c & 7) * 8;
+    r.q[p] = *reinterpret_cast<const bf16x8*>(qh + (size_t)row * kHeadDim + col);
+    r.d[p] = *reinterpret_cast<const bf16x8*>(doh + (size_t)row * kHeadDim + col);
   }
-  const int r = qs + tid;
-  const bool ok = tid < kBQ && r < T;
-  l2 = ok ? lse[r] * kLog2e : 0.f;
-  dl = ok ? delta[r] : 0.f;
+  const int row = min(qs + (tid & (kBQ - 1)), T - 1);
+  r.lse = lse[row];
+  r.del = delta[row];
+}
+
+__device__ __forceinline__ void bwd_store_tile(f16* sQ, f16* sdO, float* sL, float* sD,
+                                               const TileRegs& r, int qs, int T, int tid) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int c = tid + kThreads * p;
+    const int row = c >> 3, col = (c & 7) * 8;
+    const bool ok = qs + row < T;
+    *reinterpret_cast<f16x8*>(&sQ[row * kRowQ + col]) =
+        ok ? bf16x8_to_f16x8(r.q[p]) : zero_f16x8();
+    *reinterpret_cast<f16x8*>(&sdO[row * kRowQ + col]) =
+        ok ? bf16x8_to_f16x8(r.d[p]) : zero_f16x8();
+  }
+  if (tid < kBQ) {
+    const bool ok = qs + tid < T;
+    sL[tid] = ok ? r.lse * kLog2e : 0.f;
+    sD[tid] = ok ? r.del : 0.f;
+  }
+}
+
+// P = exp2(S log2(e)/8 - LSE log2(e)) and dS = P (dP - delta) for the 16
+// (query, key) pairs of one lane in one 32x32 block, as fp16. Register
+// 8c + t of half hf is query q0 + 16c + 8hf + t; the lane's key is key0 + l32.
+template <int KIND>
+__device__ __forceinline__ void bwd_p_ds(const f32x16& s, const f32x16& dp, const float* cL,
+                                         const float* cD, int qoff0, int q0, int key0, int T,
+                                         int l32, int hf, float scale_log2, f16x8 (&pf)[2],
+                                         f16x8 (&dsf)[2]) {
+  const int key = key0 + l32;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int qoff = qoff0 + 16 * c + 8 * hf;
+    const f32x4 L0 = *reinterpret_cast<const f32x4*>(&cL[qoff]);
+    const f32x4 L1 = *reinterpret_cast<const f32x4*>(&cL[qoff + 4]);
+    const f32x4 E0 = *reinterpret_cast<const f32x4*>(&cD[qoff]);
+    const f32x4 E1 = *reinterpret_cast<const f32x4*>(&cD[qoff + 4]);
+    float p[8], ds[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float lse2 = t < 4 ? L0[t] : L1[t - 4];
+      const float del = t < 4 ? E0[t] : E1[t - 4];
+      float pv = fast_exp2(fmaf(s[8 * c + t], scale_log2, -lse2));
+      if (KIND == kDiag) {
+        // key0 == q0: visible iff l32 <= 16c + 8hf + t.
+        pv = (l32 - 8 * hf > 16 * c + t) ? 0.f : pv;
+      } else if (KIND == kGeneral) {
+        const int qi = q0 + 16 * c + 8 * hf + t;
+        pv = (key > qi || key >= T || qi >= T) ? 0.f : pv;
+      }
+      p[t] = pv;
+      ds[t] = pv * (dp[8 * c + t] - del);
+    }
+    pf[c] = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+    dsf[c] = pack_f16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+  }
 }
 
 __global__ __launch_bounds__(kThreads, 2) void attn_bwd_main_bf16_kernel(
@@ -165,17 +212,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_main_bf16_kernel(
       dkacc[db][r] = 0.f;
     }
 
-  bf16x8 xq[2], xd[2];
-  float l2 = 0.f, dl = 0.f;
-  bwd_load_tile(qh, doh, lseh, delh, k0, T, tid, xq, xd, l2, dl);
-  bwd_store_tile(sQ[0], sdO[0], sL[0], sD[0], xq, xd, l2, dl, tid);
+  TileRegs nxt;
+  bwd_load_tile(qh, doh, lseh, delh, k0, T, tid, nxt);
+  bwd_store_tile(sQ[0], sdO[0], sL[0], sD[0], nxt, k0, T, tid);
   __syncthreads();
 
   int buf = 0;
   for (int qs = k0; qs < T; qs += kBQ, buf ^= 1) {
     // Prefetch the next tile into registers while this one is computed.
     const bool has_next = qs + kBQ < T;
-    if (has_next) bwd_load_tile(qh, doh, lseh, delh, qs + kBQ, T, tid, xq, xd, l2, dl);
+    if (has_next) bwd_load_tile(qh, doh, lseh, delh, qs + kBQ, T, tid, nxt);
 
     const f16* cQ = sQ[buf];
     const f16* cdO = sdO[buf];
@@ -185,60 +231,57 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_main_bf16_kernel(
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const int qb0 = qs + mb * 32;
-      // Wave-uniform: does this 32x32 block hold any visible (key <= query) pair?
-      if (!(qb0 < T && kw0 < T && kw0 <= qb0 + 31)) continue;
-      f32x16 s, dp;
+      const int kind = block_kind(kw0, qb0, T);
+      f16x8 pf[2], dsf[2];
+      if (kind == kEmpty) {
+        pf[0] = pf[1] = dsf[0] = dsf[1] = zero_f16x8();
+      } else {
+        f32x16 s, dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
-      const int arow = (mb * 32 + perm32(l32)) * kRowQ + 8 * hf;
+        for (int r = 0; r < 16; ++r) {
+          s[r] = 0.f;
+          dp[r] = 0.f;
+        }
+        const int arow = (mb * 32 + perm32(l32)) * kRowQ + 8 * hf;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        s = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cQ[arow + kk * 16]), kf[kk], s);
-        dp = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cdO[arow + kk * 16]), vf[kk], dp);
+        for (int kk = 0; kk < 4; ++kk) {
+          s = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cQ[arow + kk * 16]), kf[kk], s);
+          dp = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cdO[arow + kk * 16]), vf[kk],
+                                dp);
+        }
+        if (kind == kFull)
+          bwd_p_ds<kFull>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, scale_log2, pf, dsf);
+        else if (kind == kDiag)
+          bwd_p_ds<kDiag>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, scale_log2, pf, dsf);
+        else
+          bwd_p_ds<kGeneral>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, scale_log2, pf, dsf);
       }
-      const bool need_mask = (qb0 < kw0 + 31) || (kw0 + 32 > T) || (qb0 + 32 > T);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        // Register 8c + t of half hf is query qb0 + 16c + 8hf + t.
-        const int qoff = mb * 32 + 16 * c + 8 * hf;
-        const f32x4 L0 = *reinterpret_cast<const f32x4*>(&cL[qoff]);
-        const f32x4 L1 = *reinterpret_cast<const f32x4*>(&cL[qoff + 4]);
-        const f32x4 E0 = *reinterpret_cast<const f32x4*>(&cD[qoff]);
-        const f32x4 E1 = *reinterpret_cast<const f32x4*>(&cD[qoff + 4]);
-        float p[8], ds[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float lse2 = t < 4 ? L0[t] : L1[t - 4];
-          const float del = t < 4 ? E0[t] : E1[t - 4];
-          float pv = fast_exp2(fmaf(s[8 * c + t], scale_log2, -lse2));
-          if (need_mask) {
-            const int qi = qs + qoff + t;
-            if (my_key > qi || my_key >= T || qi >= T) pv = 0.f;
-          }
-          p[t] = pv;
-          ds[t] = pv * (dp[8 * c + t] - del);
-        }
-        const f16x8 pf = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-        const f16x8 dsf = pack_f16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
         // dS^T row of this lane's key: 8 consecutive queries, one 16-byte write.
-        *reinterpret_cast<f16x8*>(&sdS[(wave * 32 + l32) * kRowQ + qoff]) = dsf;
+        *reinterpret_cast<f16x8*>(&sdS[(wave * 32 + l32) * kRowQ + mb * 32 + 16 * c + 8 * hf]) =
+            dsf[c];
         // dV^T += dO^T P and dK^T += Q^T dS over these 16 queries.
         const int ks = 2 * mb + c;
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          dvacc[db] = mfma32x32x16_f16(lds_operand_tr(cdO, kRowQ, ks * 16, db * 32, lane), pf,
+          dvacc[db] = mfma32x32x16_f16(lds_operand_tr(cdO, kRowQ, ks * 16, db * 32, lane), pf[c],
                                        dvacc[db]);
-          dkacc[db] = mfma32x32x16_f16(lds_operand_tr(cQ, kRowQ, ks * 16, db * 32, lane), dsf,
+          dkacc[db] = mfma32x32x16_f16(lds_operand_tr(cQ, kRowQ, ks * 16, db * 32, lane), dsf[c],
                                        dkacc[db]);
         }
       }
     }
+    // Stage the prefetched tile into the other buffer now, before this step's
+    // dQ atomics are issued: a wait for the prefetch loads here covers only
+    // loads and the previous step's atomics. The buffer was last read in the
+    // previous step, before its first barrier.
+    if (has_next)
+      bwd_store_tile(sQ[buf ^ 1], sdO[buf ^ 1], sL[buf ^ 1], sD[buf ^ 1], nxt, qs + kBQ, T, tid);
     __syncthreads();
 
-    // dQ block (queries 32qb.., dims 32db..) = dS K over the 128 keys.
+    // dQ block (queries 32qb.., dims 32db..) = dS K over the 128 keys. Every
+    // wave wrote its dS rows (zeros where nothing is visible).
     {
       const int qb = wave >> 1, db = wave & 1;
       const int qb0 = qs + qb * 32;
@@ -246,30 +289,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_main_bf16_kernel(
         f32x16 acc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-        bool any = false;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          // Keys k0 + 16ks .. +15 belong to wave ks/2; skip the blocks that
-          // wave left out (wholly in the future of these queries or past T).
-          const int kws = k0 + (ks >> 1) * 32;
-          if (kws >= T || kws > qb0 + 31) continue;
-          any = true;
+        for (int ks = 0; ks < 8; ++ks)
           acc = mfma32x32x16_f16(lds_operand_tr(sdS, kRowQ, ks * 16, qb * 32, lane),
                                  lds_operand_tr(sK, kRowQ, ks * 16, db * 32, lane), acc);
-        }
-        if (any) {
-          float* dqh = dq + hoff;
+        float* dqh = dq + hoff + (size_t)qb0 * kHeadDim + db * 32 + l32;
+        if (qb0 + 32 <= T) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            atomicAdd(dqh + (size_t)(8 * (r >> 2) + 4 * hf + (r & 3)) * kHeadDim, acc[r] * scale);
+        } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int qi = qb0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (qi < T)
-              atomicAdd(dqh + (size_t)qi * kHeadDim + db * 32 + l32, acc[r] * scale);
+            const int qr = 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (qb0 + qr < T) atomicAdd(dqh + (size_t)qr * kHeadDim, acc[r] * scale);
           }
         }
       }
     }
-    if (has_next) bwd_store_tile(sQ[buf ^ 1], sdO[buf ^ 1], sL[buf ^ 1], sD[buf ^ 1], xq, xd, l2,
-                                 dl, tid);
+    // No vector-memory wait after the atomics: the next step's dS writes only
+    // need every wave to be past its dQ reads.
     __syncthreads();
   }
 

@@ -95,6 +95,35 @@ __device__ __forceinline__ int perm32(int r) {
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// Sum of the eight fp16 values of v added to acc (two-element dot products
+// with (1, 1), fp32 accumulation).
+__device__ __forceinline__ float sum_f16x8(f16x8 v, float acc) {
+  const f16x2 one = {(f16)1.0f, (f16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 pair = {v[2 * i], v[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2(pair, one, acc, false);
+  }
+  return acc;
+}
+
+// True when pred holds on any lane of the wave (wave-uniform result).
+__device__ __forceinline__ bool wave_any(bool pred) { return __any(pred); }
+
+// Kinds of 32-key x 32-query block, decided once per block (wave-uniform):
+// every key <= every query (no mask), the aligned diagonal block (key0 ==
+// q0, mask is a fixed triangle), no visible pair at all, or a block at the
+// end of the sequence (general mask).
+enum BlockKind { kFull = 0, kDiag = 1, kEmpty = 2, kGeneral = 3 };
+
+__device__ __forceinline__ int block_kind(int key0, int q0, int T) {
+  if (key0 > q0 + 31 || key0 >= T || q0 >= T) return kEmpty;
+  const bool in_range = key0 + 32 <= T && q0 + 32 <= T;
+  if (in_range && key0 + 31 <= q0) return kFull;
+  if (in_range && key0 == q0) return kDiag;
+  return kGeneral;
+}
+
 // Eight bf16 -> eight fp16 (see bf16_to_f16).
 __device__ __forceinline__ f16x8 bf16x8_to_f16x8(bf16x8 x) {
   return pack_f16x8((float)x[0], (float)x[1], (float)x[2], (float)x[3], (float)x[4],

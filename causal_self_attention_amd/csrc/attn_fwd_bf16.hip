@@ -20,7 +20,9 @@
 // exactly, which keeps O accurate enough for the backward's
 // delta = rowsum(dO * O). K rows are loaded in the perm32 order so the
 // accumulator registers already hold P in the MFMA B-operand order. V is
-// staged transposed so its A operand is one 16-byte LDS read.
+// staged row-major and read transposed (ds_read_b64_tr_b16). The next K/V
+// tile's global loads are issued before the current tile is computed and
+// land in a second LDS buffer.
 //
 // Outputs: O rounded to bf16, optionally the bf16 rounding of what that
 // dropped (o_lo = bf16(O - o)), and LSE in fp32.
@@ -34,19 +36,136 @@ constexpr int kBM = 128;     // queries per workgroup
 constexpr int kBN = 64;      // keys per staged tile
 constexpr int kThreads = 256;
 constexpr int kRow = 72;     // padded LDS row, bf16 elements (64 + 8)
+constexpr float kMaxSlack = 8.f;  // lazy-rescale threshold, log2 units
+
+// K/V tile loads are issued one tile ahead: fwd_load_tile only issues raw
+// 16-byte loads (rows clamped to T-1 so every address is valid);
+// fwd_store_tile zeroes rows past T and writes K (bf16) and V (fp16,
+// converted) row-major into an LDS buffer. Thread c moves chunk c and c+256
+// of each 64 x 64 tile: row c/8, dims (c%8)*8.
+struct KVRegs {
+  bf16x8 k[2], v[2];
+};
+
+__device__ __forceinline__ void fwd_load_tile(const bf16* kh, const bf16* vh, int k0, int T,
+                                              int tid, KVRegs& r) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int c = tid + kThreads * p;
+    const int row = min(k0 + (c >> 3), T - 1), col = (c & 7) * 8;
+    r.k[p] = *reinterpret_cast<const bf16x8*>(kh + (size_t)row * kHeadDim + col);
+    r.v[p] = *reinterpret_cast<const bf16x8*>(vh + (size_t)row * kHeadDim + col);
+  }
+}
+
+__device__ __forceinline__ void fwd_store_tile(bf16* Ks, f16* Vs, const KVRegs& r, int k0, int T,
+                                               int tid) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int c = tid + kThreads * p;
+    const int row = c >> 3, col = (c & 7) * 8;
+    const bool ok = k0 + row < T;
+    *reinterpret_cast<bf16x8*>(&Ks[row * kRow + col]) = ok ? r.k[p] : zero_bf16x8();
+    *reinterpret_cast<f16x8*>(&Vs[row * kRow + col]) =
+        ok ? bf16x8_to_f16x8(r.v[p]) : zero_f16x8();
+  }
+}
+
+// Per-wave state of the online softmax.
+struct FwdState {
+  f32x16 oacc[2];  // O^T accumulators: lane = query, registers = dims
+  float m_run;     // reference max, scaled log2 units (lazily updated)
+  float l_run;     // this lane's partial row sum
+};
+
+// One 64-key tile for one wave. MASKED = false: every key of the tile
+// precedes every query of the wave and lies below T (no compares at all).
+// MASKED = true: keys after the lane's query or at/after T get -inf through
+// branch-free selects against one per-lane limit.
+template <bool MASKED>
+__device__ __forceinline__ void fwd_tile(const bf16* cK, const f16* cV, const bf16x8 (&qf)[4],
+                                         int k0, int my_q, int T, int l32, int hf, int lane,
+                                         float scale_log2, FwdState& st) {
+  // Scores S^T = K Q^T for the two 32-key halves; register v = 8c + t of half
+  // hf holds key k0 + 32kb + 16c + 8hf + t (perm32 order) for query my_q.
+  f32x16 s[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const bf16* arow = &cK[(kb * 32 + perm32(l32)) * kRow + 8 * hf];
+    s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(arow), qf[0], f32x16{});
+#pragma unroll
+    for (int kk = 1; kk < 4; ++kk)
+      s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(arow + kk * 16), qf[kk], s[kb]);
+  }
+  if (MASKED) {
+    // Visible iff k0 + 32kb + 16c + 8hf + t <= min(my_q, T - 1).
+    const int lim = min(my_q, T - 1) - k0 - 8 * hf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        s[kb][r] = (32 * kb + 16 * (r >> 3) + (r & 7) > lim) ? -INFINITY : s[kb][r];
+  }
+
+  // Lazy running max: the reference m_run moves only when some row's max
+  // rises by more than kMaxSlack (log2 units); otherwise the exponentials
+  // below may reach 2^kMaxSlack, which the fp32 sums and fp16 P hold exactly
+  // as well, and the final division by l removes the reference. Most tiles
+  // skip the rescale of O and l (wave-uniform branch).
+  float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  mx = fmaxf(mx, wave_xor32(mx)) * scale_log2;
+  if (wave_any(mx > st.m_run + kMaxSlack)) {
+    const float m_new = fmaxf(st.m_run, mx);
+    const float alpha = fast_exp2(st.m_run - m_new);
+    st.m_run = m_new;
+    st.l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
+  }
+
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float p[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) p[t] = fast_exp2(fmaf(s[kb][8 * c + t], scale_log2, -st.m_run));
+      const f16x8 pb = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      // The row sum uses the fp16 weights the MFMA multiplies by.
+      st.l_run = sum_f16x8(pb, st.l_run);
+      const int ks = 2 * kb + c;  // 16-key step inside the tile
+      // O^T += V^T P^T: the A operand (lane: dim, 8 consecutive keys) is a
+      // transposing read of the row-major V tile.
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+        st.oacc[db] = mfma32x32x16_f16(lds_operand_tr(cV, kRow, ks * 16, db * 32, lane), pb,
+                                       st.oacc[db]);
+    }
+  }
+}
 
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, bf16* __restrict__ o_lo, float* __restrict__ lse, int n_heads, int T,
     int n_qtiles, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kBN * kRow];       // [key][d]
-  __shared__ __attribute__((aligned(16))) f16 Vt[kHeadDim * kRow];   // [d][key], fp16
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBN * kRow];  // [key][d], bf16
+  __shared__ __attribute__((aligned(16))) f16 Vs[2][kBN * kRow];   // [key][d], fp16
+  // Q of the 128 queries, staged once: the fragments are read from LDS so no
+  // global load inside the tile loop's dependence chain targets them.
+  __shared__ __attribute__((aligned(16))) bf16 Qs[kBM * kRow];     // [query][d]
 
   const TileMap tm = map_tile_xcd(blockIdx.x, n_heads, n_qtiles, true);
   if (!tm.valid) return;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
 
   const size_t hoff = (size_t)tm.head * (size_t)T * kHeadDim;
@@ -58,114 +177,68 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + l32;  // the query column this lane owns
 
+  KVRegs nxt;
+  fwd_load_tile(kh, vh, 0, T, tid, nxt);
+  {
+    bf16x8 xq[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int c = tid + kThreads * p;  // 0..1023: query c/8, dims (c%8)*8
+      const int row = min(q0 + (c >> 3), T - 1);
+      xq[p] = *reinterpret_cast<const bf16x8*>(qh + (size_t)row * kHeadDim + (c & 7) * 8);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int c = tid + kThreads * p;
+      const int row = c >> 3, col = (c & 7) * 8;
+      *reinterpret_cast<bf16x8*>(&Qs[row * kRow + col]) =
+          q0 + row < T ? xq[p] : zero_bf16x8();
+    }
+  }
+
+  FwdState st;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.oacc[db][r] = 0.f;
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+
+  const int kv_end = min(T, q0 + kBM);
+  const int n_kt = (kv_end + kBN - 1) / kBN;
+  // Tiles [0, n_full) need no mask for any wave of the workgroup: all their
+  // keys precede query q0 (and hence every query here) and lie below T.
+  const int n_full = min(q0, T) / kBN;
+
+  fwd_store_tile(Ks[0], Vs[0], nxt, 0, T, tid);
+  __syncthreads();
   // Q^T as the B operand: lane holds d = 16*kk + 8*hf .. +7 of its query.
   bf16x8 qf[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
-    qf[kk] = load_bf16x8(qh + (size_t)my_q * kHeadDim + kk * 16 + 8 * hf, my_q < T);
+    qf[kk] = *reinterpret_cast<const bf16x8*>(&Qs[(wave * 32 + l32) * kRow + kk * 16 + 8 * hf]);
 
-  f32x16 oacc[2];
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = -INFINITY;  // running max, in scaled log2 units
-  float l_run = 0.f;        // this lane's partial row sum
-
-  const int kv_end = min(T, q0 + kBM);
-  const int n_kt = (kv_end + kBN - 1) / kBN;
-
-  for (int kt = 0; kt < n_kt; ++kt) {
+  int buf = 0;
+  int kt = 0;
+  for (; kt < n_full; ++kt, buf ^= 1) {
     const int k0 = kt * kBN;
+    const bool has_next = kt + 1 < n_kt;
+    if (has_next) fwd_load_tile(kh, vh, k0 + kBN, T, tid, nxt);
+    fwd_tile<false>(Ks[buf], Vs[buf], qf, k0, my_q, T, l32, hf, lane, scale_log2, st);
+    if (has_next) fwd_store_tile(Ks[buf ^ 1], Vs[buf ^ 1], nxt, k0 + kBN, T, tid);
     __syncthreads();
-    // Stage K rows [k0, k0+64) row-major.
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int c = tid + kThreads * p;
-      const int row = c >> 3, col = (c & 7) * 8;
-      const int key = k0 + row;
-      *reinterpret_cast<bf16x8*>(&Ks[row * kRow + col]) =
-          load_bf16x8(kh + (size_t)key * kHeadDim + col, key < T);
-    }
-    // Stage V transposed: this thread takes rows j, j+1 and 8 dims.
-    {
-      const int j = 2 * (tid & 31), d0 = (tid >> 5) * 8;
-      const bf16x8 v0 = load_bf16x8(vh + (size_t)(k0 + j) * kHeadDim + d0, k0 + j < T);
-      const bf16x8 v1 = load_bf16x8(vh + (size_t)(k0 + j + 1) * kHeadDim + d0, k0 + j + 1 < T);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        f16x2 pr = {bf16_to_f16(v0[t]), bf16_to_f16(v1[t])};
-        *reinterpret_cast<f16x2*>(&Vt[(d0 + t) * kRow + j]) = pr;
-      }
-    }
+  }
+  for (; kt < n_kt; ++kt, buf ^= 1) {
+    const int k0 = kt * kBN;
+    const bool has_next = kt + 1 < n_kt;
+    if (has_next) fwd_load_tile(kh, vh, k0 + kBN, T, tid, nxt);
+    fwd_tile<true>(Ks[buf], Vs[buf], qf, k0, my_q, T, l32, hf, lane, scale_log2, st);
+    if (has_next) fwd_store_tile(Ks[buf ^ 1], Vs[buf ^ 1], nxt, k0 + kBN, T, tid);
     __syncthreads();
-
-    f32x16 s[2];
-    bool act[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int kbs = k0 + kb * 32;
-      act[kb] = (kbs <= qw0 + 31) && (kbs < T);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      if (act[kb]) {
-        const bf16* arow = &Ks[(kb * 32 + perm32(l32)) * kRow + 8 * hf];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(arow + kk * 16), qf[kk], s[kb]);
-      }
-    }
-
-    // Mask and row max. Register v = 8c + t of half hf holds key
-    // kbs + 16c + 8hf + t (perm32 order).
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (!act[kb]) continue;
-      const int kbs = k0 + kb * 32;
-      const bool need_mask = (kbs + 31 > qw0) || (kbs + 32 > T);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kbs + 16 * (r >> 3) + 8 * hf + (r & 7);
-        if (need_mask && (key > my_q || key >= T)) s[kb][r] = -INFINITY;
-        mx = fmaxf(mx, s[kb][r]);
-      }
-    }
-    mx = fmaxf(mx, wave_xor32(mx));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (!act[kb]) continue;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        float p[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          p[t] = fast_exp2(fmaf(s[kb][8 * c + t], scale_log2, -m_new));
-          l_run += p[t];
-        }
-        const f16x8 pb = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-        const int ks = 2 * kb + c;  // 16-key step inside the tile
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const f16x8 a =
-              *reinterpret_cast<const f16x8*>(&Vt[(db * 32 + l32) * kRow + ks * 16 + 8 * hf]);
-          oacc[db] = mfma32x32x16_f16(a, pb, oacc[db]);
-        }
-      }
-    }
   }
 
   // Epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2.
-  const float l_tot = l_run + wave_xor32(l_run);
+  const float l_tot = st.l_run + wave_xor32(st.l_run);
   const float inv = 1.f / l_tot;
   if (my_q < T) {
     bf16* orow = o + hoff + (size_t)my_q * kHeadDim;
@@ -178,14 +251,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         bf16x4 hi, lo;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          x[t] = oacc[db][4 * g + t] * inv;
+          x[t] = st.oacc[db][4 * g + t] * inv;
           hi[t] = (bf16)x[t];
           lo[t] = (bf16)(x[t] - (float)hi[t]);
         }
         *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * g + 4 * hf) = hi;
         if (lrow) *reinterpret_cast<bf16x4*>(lrow + db * 32 + 8 * g + 4 * hf) = lo;
       }
-    if (hf == 0) lse[(size_t)tm.head * T + my_q] = (m_run + fast_log2(l_tot)) * kLn2;
+    if (hf == 0) lse[(size_t)tm.head * T + my_q] = (st.m_run + fast_log2(l_tot)) * kLn2;
   }
 }
 
