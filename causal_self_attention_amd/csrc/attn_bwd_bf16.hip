@@ -14,15 +14,18 @@
 //
 // Kernel 1 (prep) forms delta from the stored O (plus its low part o_lo
 // when the forward kept it, which restores fp32 accuracy) and zeroes dQ.
-// Kernel 2 (main): a workgroup of 4 waves owns 128 consecutive keys of one
+// Kernel 2 (main): a workgroup of 8 waves owns 256 consecutive keys of one
 // head (32 per wave) and keeps their K, V fragments and dK, dV accumulators
 // in registers. It walks the 64-query tiles from its diagonal to the end of
-// the sequence; per tile it stages Q and dO in LDS both row-major in bf16
-// (for the S = Q K^T and dP = dO V^T products) and transposed in fp16 (for
-// dK^T += Q^T dS and dV^T += dO^T P), recomputes P from the saved LSE, forms
-// dS, and writes dS to LDS. Each wave then forms one 32x32 block of the
-// tile's dQ = dS K over all 128 keys from LDS and adds it into the fp32 dQ
-// with atomic adds.
+// the sequence; each tile of Q and dO is staged once in LDS as row-major fp16
+// (waves 4..7 prefetch the next tile a step ahead into a second buffer), and
+// the transposed operands (Q^T, dO^T for dK^T += Q^T dS and dV^T += dO^T P)
+// come from transposing LDS reads. Per tile each wave recomputes P from the
+// saved LSE, forms dS and writes its dS^T rows to LDS; then dQ = dS K over
+// the 256 keys is formed as four 32x32 blocks, each split into two key
+// halves whose sums meet in LDS, and waves 0..3 add the result into the fp32
+// dQ with atomic adds (which the memory side performs; 256 keys per
+// workgroup keep their number at T/256 per dQ element).
 //
 // Precision: S = Q K^T and dP = dO V^T multiply bf16 inputs exactly. The
 // three products with a rounded operand (dV += P^T dO, dK += dS^T Q,
@@ -34,9 +37,10 @@
 namespace gpt_attn {
 namespace {
 
-constexpr int kBK = 128;      // keys per workgroup
+constexpr int kBK = 256;      // keys per workgroup (8 waves x 32)
 constexpr int kBQ = 64;       // queries per step
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kLoaders = 256; // threads of waves 4..7: they alone load Q/dO tiles
 constexpr int kRowQ = 72;     // padded row of a 64-wide 16-bit LDS tile (144 bytes)
 
 __global__ __launch_bounds__(256) void attn_bwd_prep_bf16_kernel(
@@ -72,9 +76,10 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_bf16_kernel(
 // a whole step ahead: bwd_load_tile only issues raw loads (rows clamped to
 // T-1, so every address is valid, and nothing is computed from the results);
 // bwd_store_tile, a step later, zeroes rows past T, converts to fp16 and
-// writes the LDS buffers. Each thread moves two 16-byte chunks of Q and of dO
-// (row c/8, dims (c%8)*8 for c = tid, tid+256); threads 0..63 also move the
-// LSE and delta of row tid.
+// writes the LDS buffers. Only the 256 threads of waves 4..7 take part (tid
+// below is their index 0..255): each moves two 16-byte chunks of Q and of dO
+// (row c/8, dims (c%8)*8 for c = tid, tid+256), and those with tid < 64 also
+// move the LSE and delta of row tid.
 struct TileRegs {
   bf16x8 q[2], d[2];
   float lse, del;
@@ -85,7 +90,7 @@ __device__ __forceinline__ void bwd_load_tile(const bf16* qh, const bf16* doh, c
                                               TileRegs& r) {
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const int c = tid + kThreads * p;
+    const int c = tid + kLoaders * p;
     const int row = min(qs + (c >> 3), T - 1), col = (c & 7) * 8;
     r.q[p] = *reinterpret_cast<const bf16x8*>(qh + (size_t)row * kHeadDim + col);
     r.d[p] = *reinterpret_cast<const bf16x8*>(doh + (size_t)row * kHeadDim + col);
@@ -99,7 +104,7 @@ __device__ __forceinline__ void bwd_store_tile(f16* sQ, f16* sdO, float* sL, flo
                                                const TileRegs& r, int qs, int T, int tid) {
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const int c = tid + kThreads * p;
+    const int c = tid + kLoaders * p;
     const int row = c >> 3, col = (c & 7) * 8;
     const bool ok = qs + row < T;
     *reinterpret_cast<f16x8*>(&sQ[row * kRowQ + col]) =
@@ -151,7 +156,7 @@ __device__ __forceinline__ void bwd_p_ds(const f32x16& s, const f32x16& dp, cons
   }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void attn_bwd_main_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, float* __restrict__ dq, float* __restrict__ dk,
@@ -161,6 +166,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_main_bf16_kernel(
   __shared__ __attribute__((aligned(16))) f16 sQ[2][kBQ * kRowQ];       // [q][d]
   __shared__ __attribute__((aligned(16))) f16 sdO[2][kBQ * kRowQ];      // [q][d]
   __shared__ __attribute__((aligned(16))) f16 sdS[kBK * kRowQ];         // [key][q]
+  __shared__ __attribute__((aligned(16))) float sPart[4][16][64];       // dQ half sums
   __shared__ __attribute__((aligned(16))) float sL[2][kBQ];             // LSE * log2(e)
   __shared__ __attribute__((aligned(16))) float sD[2][kBQ];             // delta
 
@@ -171,6 +177,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_main_bf16_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
+  // Waves 4..7 load the query tiles; waves 0..3 issue the dQ atomics. No wave
+  // does both, so a wait for a prefetched tile never waits on atomics too.
+  const bool loader = wave >= 4;
+  const int ltid = tid - kLoaders;
 
   const size_t hoff = (size_t)tm.head * (size_t)T * kHeadDim;
   const size_t roff = (size_t)tm.head * (size_t)T;
@@ -194,10 +204,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_main_bf16_kernel(
     vf[kk] = bf16x8_to_f16x8(
         load_bf16x8(vh + (size_t)my_key * kHeadDim + kk * 16 + 8 * hf, my_key < T));
   }
-  // All 128 keys of K, row-major fp16, for the dQ product.
+  // All 256 keys of K, row-major fp16, for the dQ product.
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const int c = tid + kThreads * p;  // 0..1023: key c/8, 8 dims at (c%8)*8
+    const int c = tid + kThreads * p;  // 0..2047: key c/8, 8 dims at (c%8)*8
     const int row = c >> 3, col = (c & 7) * 8;
     *reinterpret_cast<f16x8*>(&sK[row * kRowQ + col]) = bf16x8_to_f16x8(
         load_bf16x8(kh + (size_t)(k0 + row) * kHeadDim + col, k0 + row < T));
@@ -213,15 +223,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_main_bf16_kernel(
     }
 
   TileRegs nxt;
-  bwd_load_tile(qh, doh, lseh, delh, k0, T, tid, nxt);
-  bwd_store_tile(sQ[0], sdO[0], sL[0], sD[0], nxt, k0, T, tid);
+  if (loader) {
+    bwd_load_tile(qh, doh, lseh, delh, k0, T, ltid, nxt);
+    bwd_store_tile(sQ[0], sdO[0], sL[0], sD[0], nxt, k0, T, ltid);
+  }
   __syncthreads();
 
   int buf = 0;
   for (int qs = k0; qs < T; qs += kBQ, buf ^= 1) {
     // Prefetch the next tile into registers while this one is computed.
     const bool has_next = qs + kBQ < T;
-    if (has_next) bwd_load_tile(qh, doh, lseh, delh, qs + kBQ, T, tid, nxt);
+    if (loader && has_next) bwd_load_tile(qh, doh, lseh, delh, qs + kBQ, T, ltid, nxt);
 
     const f16* cQ = sQ[buf];
     const f16* cdO = sdO[buf];
@@ -272,44 +284,54 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_main_bf16_kernel(
         }
       }
     }
-    // Stage the prefetched tile into the other buffer now, before this step's
-    // dQ atomics are issued: a wait for the prefetch loads here covers only
-    // loads and the previous step's atomics. The buffer was last read in the
-    // previous step, before its first barrier.
-    if (has_next)
-      bwd_store_tile(sQ[buf ^ 1], sdO[buf ^ 1], sL[buf ^ 1], sD[buf ^ 1], nxt, qs + kBQ, T, tid);
+    // Stage the prefetched tile into the other buffer, last read in the
+    // previous step before its first barrier.
+    if (loader && has_next)
+      bwd_store_tile(sQ[buf ^ 1], sdO[buf ^ 1], sL[buf ^ 1], sD[buf ^ 1], nxt, qs + kBQ, T, ltid);
     __syncthreads();
 
-    // dQ block (queries 32qb.., dims 32db..) = dS K over the 128 keys. Every
-    // wave wrote its dS rows (zeros where nothing is visible).
-    {
-      const int qb = wave >> 1, db = wave & 1;
-      const int qb0 = qs + qb * 32;
-      if (qb0 < T) {
-        f32x16 acc;
+    // dQ of the 64-query tile = dS K over the 256 keys, as four 32x32 blocks
+    // (queries 32qb.., dims 32db..). Wave w takes block w % 4 over key half
+    // w / 4 (8 steps of 16 keys); waves 4..7 pass their half sums to waves
+    // 0..3 through LDS, which add them into dQ with atomics. Every wave wrote
+    // its dS rows (zeros where nothing is visible).
+    const int blk = wave & 3, khalf = wave >> 2;
+    const int qb = blk >> 1, db = blk & 1;
+    const int qb0 = qs + qb * 32;
+    f32x16 acc;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    if (qb0 < T) {
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-          acc = mfma32x32x16_f16(lds_operand_tr(sdS, kRowQ, ks * 16, qb * 32, lane),
-                                 lds_operand_tr(sK, kRowQ, ks * 16, db * 32, lane), acc);
-        float* dqh = dq + hoff + (size_t)qb0 * kHeadDim + db * 32 + l32;
-        if (qb0 + 32 <= T) {
+      for (int j = 0; j < 8; ++j) {
+        const int ks = 8 * khalf + j;
+        acc = mfma32x32x16_f16(lds_operand_tr(sdS, kRowQ, ks * 16, qb * 32, lane),
+                               lds_operand_tr(sK, kRowQ, ks * 16, db * 32, lane), acc);
+      }
+      if (khalf == 1) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            atomicAdd(dqh + (size_t)(8 * (r >> 2) + 4 * hf + (r & 3)) * kHeadDim, acc[r] * scale);
-        } else {
+        for (int r = 0; r < 16; ++r) sPart[blk][r][lane] = acc[r];
+      }
+    }
+    __syncthreads();
+    if (khalf == 0 && qb0 < T) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qr = 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (qb0 + qr < T) atomicAdd(dqh + (size_t)qr * kHeadDim, acc[r] * scale);
-          }
+      for (int r = 0; r < 16; ++r) acc[r] += sPart[blk][r][lane];
+      float* dqh = dq + hoff + (size_t)qb0 * kHeadDim + db * 32 + l32;
+      if (qb0 + 32 <= T) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          atomicAdd(dqh + (size_t)(8 * (r >> 2) + 4 * hf + (r & 3)) * kHeadDim, acc[r] * scale);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qr = 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (qb0 + qr < T) atomicAdd(dqh + (size_t)qr * kHeadDim, acc[r] * scale);
         }
       }
     }
-    // No vector-memory wait after the atomics: the next step's dS writes only
-    // need every wave to be past its dQ reads.
-    __syncthreads();
+    // The next step's dS and half-sum writes come after its first barrier,
+    // which every wave reaches only after the reads above.
   }
 
   // ---- epilogue: dV, dK = s * acc (lane: its key; 4 consecutive dims per store)
@@ -317,14 +339,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_main_bf16_kernel(
     float* dvr = dv + hoff + (size_t)my_key * kHeadDim;
     float* dkr = dk + hoff + (size_t)my_key * kHeadDim;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db2 = 0; db2 < 2; ++db2)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + 8 * g + 4 * hf;
-        f32x4 a = {dvacc[db][4 * g], dvacc[db][4 * g + 1], dvacc[db][4 * g + 2],
-                   dvacc[db][4 * g + 3]};
-        f32x4 b = {dkacc[db][4 * g] * scale, dkacc[db][4 * g + 1] * scale,
-                   dkacc[db][4 * g + 2] * scale, dkacc[db][4 * g + 3] * scale};
+        const int d = db2 * 32 + 8 * g + 4 * hf;
+        f32x4 a = {dvacc[db2][4 * g], dvacc[db2][4 * g + 1], dvacc[db2][4 * g + 2],
+                   dvacc[db2][4 * g + 3]};
+        f32x4 b = {dkacc[db2][4 * g] * scale, dkacc[db2][4 * g + 1] * scale,
+                   dkacc[db2][4 * g + 2] * scale, dkacc[db2][4 * g + 3] * scale};
         *reinterpret_cast<f32x4*>(dvr + d) = a;
         *reinterpret_cast<f32x4*>(dkr + d) = b;
       }
