@@ -154,11 +154,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, bf16* __restrict__ o_lo, float* __restrict__ lse, int n_heads, int T,
     int n_qtiles, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBN * kRow];  // [key][d], bf16
-  __shared__ __attribute__((aligned(16))) f16 Vs[2][kBN * kRow];   // [key][d], fp16
-  // Q of the 128 queries, staged once: the fragments are read from LDS so no
-  // global load inside the tile loop's dependence chain targets them.
-  __shared__ __attribute__((aligned(16))) bf16 Qs[kBM * kRow];     // [query][d]
+  // LDS: two K/V tile buffers (K bf16, V fp16, both [key][d]). Buffer 1 also
+  // holds the 128 x 64 Q tile during the prologue: Q fragments are read from
+  // LDS so no global load inside the tile loop's dependence chain targets
+  // them, and buffer 1 is first written after every wave has read them.
+  __shared__ __attribute__((aligned(16))) bf16 lds_raw[2 * 2 * kBN * kRow];
+  auto Kbuf = [&](int b) { return lds_raw + 2 * b * kBN * kRow; };
+  auto Vbuf = [&](int b) { return reinterpret_cast<f16*>(lds_raw + (2 * b + 1) * kBN * kRow); };
+  bf16* Qs = Kbuf(1);  // [query][d], 128 rows: spans K and V of buffer 1
+  static_assert(kBM * kRow <= 2 * kBN * kRow, "Q tile must fit in buffer 1");
 
   const TileMap tm = map_tile_xcd(blockIdx.x, n_heads, n_qtiles, true);
   if (!tm.valid) return;
@@ -210,13 +214,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   // keys precede query q0 (and hence every query here) and lie below T.
   const int n_full = min(q0, T) / kBN;
 
-  fwd_store_tile(Ks[0], Vs[0], nxt, 0, T, tid);
+  fwd_store_tile(Kbuf(0), Vbuf(0), nxt, 0, T, tid);
   __syncthreads();
   // Q^T as the B operand: lane holds d = 16*kk + 8*hf .. +7 of its query.
   bf16x8 qf[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
     qf[kk] = *reinterpret_cast<const bf16x8*>(&Qs[(wave * 32 + l32) * kRow + kk * 16 + 8 * hf]);
+  __syncthreads();  // every wave holds its Q fragments: buffer 1 is free
 
   int buf = 0;
   int kt = 0;
@@ -224,16 +229,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const int k0 = kt * kBN;
     const bool has_next = kt + 1 < n_kt;
     if (has_next) fwd_load_tile(kh, vh, k0 + kBN, T, tid, nxt);
-    fwd_tile<false>(Ks[buf], Vs[buf], qf, k0, my_q, T, l32, hf, lane, scale_log2, st);
-    if (has_next) fwd_store_tile(Ks[buf ^ 1], Vs[buf ^ 1], nxt, k0 + kBN, T, tid);
+    fwd_tile<false>(Kbuf(buf), Vbuf(buf), qf, k0, my_q, T, l32, hf, lane, scale_log2, st);
+    if (has_next) fwd_store_tile(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid);
     __syncthreads();
   }
   for (; kt < n_kt; ++kt, buf ^= 1) {
     const int k0 = kt * kBN;
     const bool has_next = kt + 1 < n_kt;
     if (has_next) fwd_load_tile(kh, vh, k0 + kBN, T, tid, nxt);
-    fwd_tile<true>(Ks[buf], Vs[buf], qf, k0, my_q, T, l32, hf, lane, scale_log2, st);
-    if (has_next) fwd_store_tile(Ks[buf ^ 1], Vs[buf ^ 1], nxt, k0 + kBN, T, tid);
+    fwd_tile<true>(Kbuf(buf), Vbuf(buf), qf, k0, my_q, T, l32, hf, lane, scale_log2, st);
+    if (has_next) fwd_store_tile(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid);
     __syncthreads();
   }
 
