@@ -3,7 +3,10 @@
 One step = one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: gpt_attn_fwd (O, o_lo, LSE), then the backward's
 two phases gpt_attn_bwd_prep (delta, dQ zero-fill) and gpt_attn_bwd_main
-(dQ, dK, dV), all through the C ABI on torch's current stream.
+(dQ, dK, dV), all through the C ABI on torch's current stream. With
+``--layout fused`` the same step runs through the strided entry points on the
+attention layer's own buffers: q, k, v read from one [B, T, 3C] projection
+output, dO from and O into [B, T, C], fp32 dQ, dK, dV into one [B, T, 3C].
 
 FLOPs are the causal algorithmic count: only the T(T+1)/2 unmasked (query,
 key) pairs per head, 4*D per pair forward (QK^T and PV) and 10*D per pair
@@ -99,6 +102,9 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-heads", type=int, default=64,
                     help="heads of the workload the oracle baseline runs")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--layout", choices=("bhtd", "fused"), default="bhtd",
+                    help="bhtd: contiguous [B, H, T, D] operands; fused: views of the "
+                         "projection's [B, T, 3C] output and of [B, T, C] buffers")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -133,13 +139,33 @@ def main(argv=None) -> int:
         return 2
     dev = torch.device("cuda:0")
     inp = workload_inputs(w, seed=args.seed)
-    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
-    o = torch.empty_like(q)
-    o_lo = torch.empty_like(q)
+    fused = args.layout == "fused"
+    if fused:
+        C = w.H * w.D
+        qkv = torch.empty(w.B, w.T, 3 * C, dtype=torch.bfloat16, device=dev)
+        q, k, v = gattn.split_qkv_heads(qkv, w.H)
+        for view, name in ((q, "q"), (k, "k"), (v, "v")):
+            view.copy_(inp[name].to(dev))
+        do = gattn.merged_heads_view(torch.empty(w.B, w.T, C, dtype=torch.bfloat16,
+                                                 device=dev), w.H)
+        do.copy_(inp["do"].to(dev))
+        o = gattn.merged_heads_view(torch.empty(w.B, w.T, C, dtype=torch.bfloat16,
+                                                device=dev), w.H)
+        dq, dk, dv = gattn.split_qkv_heads(
+            torch.empty(w.B, w.T, 3 * C, dtype=torch.float32, device=dev), w.H)
+        fwd_call = gattn.gpt_attn_fwd_strided
+        prep_call = gattn.gpt_attn_bwd_prep_strided
+        main_call = gattn.gpt_attn_bwd_main_strided
+    else:
+        q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+        o = torch.empty_like(q)
+        dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        dk = torch.empty_like(dq)
+        dv = torch.empty_like(dq)
+        fwd_call, prep_call, main_call = (gattn.gpt_attn_fwd, gattn.gpt_attn_bwd_prep,
+                                          gattn.gpt_attn_bwd_main)
+    o_lo = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
-    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    dk = torch.empty_like(dq)
-    dv = torch.empty_like(dq)
     ws = torch.empty(gattn.gpt_attn_bwd_workspace_bytes("bf16", w.B, w.H, w.T, w.D) // 4,
                      dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -150,21 +176,21 @@ def main(argv=None) -> int:
 
     def step(i=None):
         if i is None:
-            gattn.gpt_attn_fwd(q, k, v, o, o_lo, lse, stream)
-            gattn.gpt_attn_bwd_prep(o, o_lo, do, dq, ws, stream)
-            gattn.gpt_attn_bwd_main(q, k, v, do, lse, dq, dk, dv, ws, stream)
+            fwd_call(q, k, v, o, o_lo, lse, stream)
+            prep_call(o, o_lo, do, dq, ws, stream)
+            main_call(q, k, v, do, lse, dq, dk, dv, ws, stream)
             return
         a, b = ev["fwd"][i]
         a.record(stream)
-        gattn.gpt_attn_fwd(q, k, v, o, o_lo, lse, stream)
+        fwd_call(q, k, v, o, o_lo, lse, stream)
         b.record(stream)
         a, b = ev["prep"][i]
         a.record(stream)
-        gattn.gpt_attn_bwd_prep(o, o_lo, do, dq, ws, stream)
+        prep_call(o, o_lo, do, dq, ws, stream)
         b.record(stream)
         a, b = ev["main"][i]
         a.record(stream)
-        gattn.gpt_attn_bwd_main(q, k, v, do, lse, dq, dk, dv, ws, stream)
+        main_call(q, k, v, do, lse, dq, dk, dv, ws, stream)
         b.record(stream)
 
     for _ in range(args.warmup):
@@ -193,7 +219,7 @@ def main(argv=None) -> int:
         return 1
 
     main_tflops = bwd_flop / (avg["main"] * 1e-3) / 1e12
-    traffic = load_traffic(bwd_flop)
+    traffic = None if fused else load_traffic(bwd_flop)
     out = {
         "metric": "causal attn fwd+bwd TFLOP/s and % bf16 MFMA peak, GPT-2 124M shape",
         "value": round(value, 2),
@@ -209,7 +235,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "D": w.D,
                    "causal": True, "scale": 1.0 / w.D ** 0.5, "seed": args.seed,
-                   "layout": "BHTD", "pct_of_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2)},
+                   "layout": "B,T,3C views" if fused else "BHTD", "pct_of_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2)},
         "fwd": {"ms": round(avg["fwd"], 5),
                 "tflops": round(fwd_flop / (avg["fwd"] * 1e-3) / 1e12, 2),
                 "pct_peak": round(100 * fwd_flop / (avg["fwd"] * 1e-3) / 1e12 /

@@ -17,11 +17,17 @@ The names mirror the C entry points:
   gpt_attn_status_string(status)                     -> str
   gpt_attn_abi_version()                             -> int
 
-plus two allocating conveniences, ``attention_forward`` and
-``attention_backward``. Tensors are [B, H, T, D] contiguous; q, k, v, o, dout
-are float32 or bfloat16; lse [B, H, T] and dq, dk, dv are float32. o_lo
-(bf16 only, may be None) is the bf16 low part of the forward's fp32 O, which
-the backward uses for an accurate delta = rowsum(dO * O).
+and the strided forms gpt_attn_fwd_strided, gpt_attn_bwd_strided,
+gpt_attn_bwd_prep_strided, gpt_attn_bwd_main_strided (same arguments; each
+tensor's own strides become its gpt_attn_layout), plus two allocating
+conveniences, ``attention_forward`` and ``attention_backward``, and the view
+helpers ``split_qkv_heads`` / ``merged_heads_view`` for the fused [B, T, 3C]
+projection layout. Tensors are logically [B, H, T, D]: contiguous for the
+plain calls, any layout with unit stride along D for the strided ones; q, k,
+v, o, dout are float32 or bfloat16; lse [B, H, T] (contiguous) and dq, dk,
+dv are float32. o_lo (bf16 only, may be None) is the bf16 low part of the
+forward's fp32 O, which the backward uses for an accurate
+delta = rowsum(dO * O).
 """
 from __future__ import annotations
 
@@ -31,7 +37,10 @@ import os
 __all__ = [
     "GptAttnError", "library_path", "load_library", "gpt_attn_fwd", "gpt_attn_bwd",
     "gpt_attn_bwd_prep", "gpt_attn_bwd_main", "gpt_attn_bwd_workspace_bytes",
-    "gpt_attn_status_string", "gpt_attn_abi_version", "attention_forward", "attention_backward", "DTYPE_CODES",
+    "gpt_attn_status_string", "gpt_attn_abi_version", "gpt_attn_fwd_strided",
+    "gpt_attn_bwd_strided", "gpt_attn_bwd_prep_strided", "gpt_attn_bwd_main_strided",
+    "attention_forward", "attention_backward", "split_qkv_heads", "merged_heads_view",
+    "DTYPE_CODES", "GptAttnLayout",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,8 +53,18 @@ DTYPE_CODES = {"f32": GPT_ATTN_F32, "bf16": GPT_ATTN_BF16}
 
 #: every symbol include/gpt_attn.h declares
 EXPORTED_SYMBOLS = ("gpt_attn_fwd", "gpt_attn_bwd", "gpt_attn_bwd_prep", "gpt_attn_bwd_main",
-                    "gpt_attn_bwd_workspace_bytes", "gpt_attn_status_string",
-                    "gpt_attn_abi_version")
+                    "gpt_attn_fwd_strided", "gpt_attn_bwd_strided", "gpt_attn_bwd_prep_strided",
+                    "gpt_attn_bwd_main_strided", "gpt_attn_bwd_workspace_bytes",
+                    "gpt_attn_status_string", "gpt_attn_abi_version")
+
+ABI_VERSION = 2
+
+
+class GptAttnLayout(ctypes.Structure):
+    """struct gpt_attn_layout: element strides (batch, head, row) of a
+    logically [B, H, T, D] operand whose D elements are contiguous."""
+    _fields_ = [("batch", ctypes.c_longlong), ("head", ctypes.c_longlong),
+                ("row", ctypes.c_longlong)]
 
 
 class GptAttnError(RuntimeError):
@@ -77,6 +96,19 @@ def load_library():
     lib.gpt_attn_bwd_prep.restype = i
     lib.gpt_attn_bwd_main.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gpt_attn_bwd_main.restype = i
+    lp = ctypes.POINTER(GptAttnLayout)
+    lib.gpt_attn_fwd_strided.argtypes = [i, i, i, i, i, vp, lp, vp, lp, vp, lp, vp, lp, vp, lp,
+                                         vp, vp]
+    lib.gpt_attn_fwd_strided.restype = i
+    lib.gpt_attn_bwd_strided.argtypes = [i, i, i, i, i, vp, lp, vp, lp, vp, lp, vp, lp, vp, lp,
+                                         vp, lp, vp, vp, lp, vp, lp, vp, lp, vp, sz, vp]
+    lib.gpt_attn_bwd_strided.restype = i
+    lib.gpt_attn_bwd_prep_strided.argtypes = [i, i, i, i, i, vp, lp, vp, lp, vp, lp, vp, lp, vp,
+                                              sz, vp]
+    lib.gpt_attn_bwd_prep_strided.restype = i
+    lib.gpt_attn_bwd_main_strided.argtypes = [i, i, i, i, i, vp, lp, vp, lp, vp, lp, vp, lp, vp,
+                                              vp, lp, vp, lp, vp, lp, vp, sz, vp]
+    lib.gpt_attn_bwd_main_strided.restype = i
     lib.gpt_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.gpt_attn_bwd_workspace_bytes.restype = sz
     lib.gpt_attn_status_string.argtypes = [i]
@@ -119,6 +151,29 @@ def _ptr(t):
     if not t.is_contiguous():
         raise ValueError("expected a contiguous tensor")
     return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+
+
+def _sptr(t):
+    """Pointer and gpt_attn_layout of a logically [B, H, T, D] view (unit
+    stride along D), or (None, None) for None."""
+    if t is None:
+        return None, None
+    if not t.is_cuda:
+        raise ValueError("expected a CUDA (HIP) device tensor")
+    if t.dim() != 4:
+        raise ValueError(f"expected a [B, H, T, D] view, got shape {tuple(t.shape)}")
+    if t.numel() == 0:
+        return None, None
+    if t.stride(3) != 1:
+        raise ValueError("the D dimension must be contiguous (stride 1)")
+    lay = GptAttnLayout(t.stride(0), t.stride(1), t.stride(2))
+    return ctypes.c_void_p(t.data_ptr()), ctypes.byref(lay)
+
+
+def _same_shape(ref, *ts):
+    for t in ts:
+        if t is not None and tuple(t.shape) != tuple(ref.shape):
+            raise ValueError(f"shape {tuple(t.shape)} differs from {tuple(ref.shape)}")
 
 
 def _stream(device, stream):
@@ -180,30 +235,125 @@ def gpt_attn_bwd_main(q, k, v, dout, lse, dq, dk, dv, workspace, stream=None) ->
         raise GptAttnError("gpt_attn_bwd_main", st)
 
 
-def attention_forward(q, k, v, stream=None, keep_o_lo: bool = True):
-    """Allocate O (dtype of q), LSE (fp32) and, for bf16 with keep_o_lo, the
-    low part o_lo; run the forward; return (o, lse, o_lo) (o_lo may be None)."""
+# ---- strided forms ------------------------------------------------------------
+
+def gpt_attn_fwd_strided(q, k, v, o, o_lo, lse, stream=None) -> None:
+    """gpt_attn_fwd on [B, H, T, D] views of any layout with unit D stride."""
+    B, H, T, D = _bhtd(q)
+    _same_shape(q, k, v, o, o_lo)
+    args = []
+    for t in (q, k, v, o, o_lo):
+        args.extend(_sptr(t))
+    st = load_library().gpt_attn_fwd_strided(_dtype_code(q), B, H, T, D, *args, _ptr(lse),
+                                             _stream(q.device, stream))
+    if st != 0:
+        raise GptAttnError("gpt_attn_fwd_strided", st)
+
+
+def gpt_attn_bwd_strided(q, k, v, o, o_lo, dout, lse, dq, dk, dv, workspace,
+                         stream=None) -> None:
+    """gpt_attn_bwd on [B, H, T, D] views of any layout with unit D stride."""
+    B, H, T, D = _bhtd(q)
+    _same_shape(q, k, v, o, o_lo, dout, dq, dk, dv)
+    args = []
+    for t in (q, k, v, o, o_lo, dout):
+        args.extend(_sptr(t))
+    args.append(_ptr(lse))
+    for t in (dq, dk, dv):
+        args.extend(_sptr(t))
+    st = load_library().gpt_attn_bwd_strided(_dtype_code(q), B, H, T, D, *args, _ptr(workspace),
+                                             _ws_bytes(workspace), _stream(q.device, stream))
+    if st != 0:
+        raise GptAttnError("gpt_attn_bwd_strided", st)
+
+
+def gpt_attn_bwd_prep_strided(o, o_lo, dout, dq, workspace, stream=None) -> None:
+    """gpt_attn_bwd_prep on [B, H, T, D] views (unit D stride)."""
+    B, H, T, D = _bhtd(o)
+    _same_shape(o, o_lo, dout, dq)
+    args = []
+    for t in (o, o_lo, dout, dq):
+        args.extend(_sptr(t))
+    st = load_library().gpt_attn_bwd_prep_strided(_dtype_code(o), B, H, T, D, *args,
+                                                  _ptr(workspace), _ws_bytes(workspace),
+                                                  _stream(o.device, stream))
+    if st != 0:
+        raise GptAttnError("gpt_attn_bwd_prep_strided", st)
+
+
+def gpt_attn_bwd_main_strided(q, k, v, dout, lse, dq, dk, dv, workspace, stream=None) -> None:
+    """gpt_attn_bwd_main on [B, H, T, D] views (unit D stride)."""
+    B, H, T, D = _bhtd(q)
+    _same_shape(q, k, v, dout, dq, dk, dv)
+    args = []
+    for t in (q, k, v, dout):
+        args.extend(_sptr(t))
+    args.append(_ptr(lse))
+    for t in (dq, dk, dv):
+        args.extend(_sptr(t))
+    st = load_library().gpt_attn_bwd_main_strided(_dtype_code(q), B, H, T, D, *args,
+                                                  _ptr(workspace), _ws_bytes(workspace),
+                                                  _stream(q.device, stream))
+    if st != 0:
+        raise GptAttnError("gpt_attn_bwd_main_strided", st)
+
+
+# ---- views of the fused projection layout ---------------------------------------
+
+def split_qkv_heads(qkv, n_head: int):
+    """[B, T, 3C] projection output -> q, k, v as [B, H, T, D] views (no copy):
+    the layer's single linear map produces q, k, v for every token, split
+    into n_head groups of D = C / n_head."""
+    if qkv.dim() != 3 or qkv.shape[2] % (3 * n_head):
+        raise ValueError(f"expected [B, T, 3C] with C divisible by {n_head}")
+    B, T, C3 = qkv.shape
+    C = C3 // 3
+    return tuple(t.view(B, T, n_head, C // n_head).transpose(1, 2)
+                 for t in qkv.split(C, dim=2))
+
+
+def merged_heads_view(y, n_head: int):
+    """[B, T, C] buffer -> the [B, H, T, D] view that writes heads merged back."""
+    if y.dim() != 3 or y.shape[2] % n_head:
+        raise ValueError(f"expected [B, T, C] with C divisible by {n_head}")
+    B, T, C = y.shape
+    return y.view(B, T, n_head, C // n_head).transpose(1, 2)
+
+
+def attention_forward(q, k, v, stream=None, keep_o_lo: bool = True, out=None):
+    """Run the forward on [B, H, T, D] views (any layout with unit D stride).
+    O goes to ``out`` (a view of that shape, e.g. merged_heads_view of a
+    [B, T, C] buffer) or a new contiguous tensor; LSE (fp32) and, for bf16
+    with keep_o_lo, the low part o_lo are allocated. Returns (o, lse, o_lo)."""
     import torch
     for t in (k, v):
         if t.shape != q.shape or t.dtype != q.dtype:
             raise ValueError("q, k, v must share shape and dtype")
-    o = torch.empty_like(q)
-    o_lo = torch.empty_like(q) if (keep_o_lo and q.dtype == torch.bfloat16) else None
-    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
-    gpt_attn_fwd(q, k, v, o, o_lo, lse, stream)
+    shape = tuple(q.shape)
+    o = torch.empty(shape, dtype=q.dtype, device=q.device) if out is None else out
+    o_lo = (torch.empty(shape, dtype=q.dtype, device=q.device)
+            if (keep_o_lo and q.dtype == torch.bfloat16) else None)
+    lse = torch.empty(shape[:-1], dtype=torch.float32, device=q.device)
+    gpt_attn_fwd_strided(q, k, v, o, o_lo, lse, stream)
     return o, lse, o_lo
 
 
-def attention_backward(q, k, v, o, dout, lse, o_lo=None, stream=None, workspace=None):
-    """Allocate fp32 dQ, dK, dV (and the workspace unless given), run the
-    backward, return (dq, dk, dv)."""
+def attention_backward(q, k, v, o, dout, lse, o_lo=None, stream=None, workspace=None,
+                       grads=None):
+    """Run the backward on [B, H, T, D] views (any layout with unit D stride).
+    dQ, dK, dV (fp32) go to ``grads`` = (dq, dk, dv) views when given (e.g.
+    split_qkv_heads of an fp32 [B, T, 3C] buffer), else to new tensors; the
+    workspace is allocated unless given. Returns (dq, dk, dv)."""
     import torch
     B, H, T, D = _bhtd(q)
-    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    dk = torch.empty_like(dq)
-    dv = torch.empty_like(dq)
+    if grads is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        dk = torch.empty_like(dq)
+        dv = torch.empty_like(dq)
+    else:
+        dq, dk, dv = grads
     if workspace is None:
         nbytes = gpt_attn_bwd_workspace_bytes(_dtype_code(q), B, H, T, D)
         workspace = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device=q.device)
-    gpt_attn_bwd(q, k, v, o, o_lo, dout, lse, dq, dk, dv, workspace, stream)
+    gpt_attn_bwd_strided(q, k, v, o, o_lo, dout, lse, dq, dk, dv, workspace, stream)
     return dq, dk, dv

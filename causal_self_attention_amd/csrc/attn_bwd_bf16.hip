@@ -43,33 +43,39 @@ constexpr int kThreads = 512;
 constexpr int kLoaders = 256; // threads of waves 4..7: they alone load Q/dO tiles
 constexpr int kRowQ = 72;     // padded row of a 64-wide 16-bit LDS tile (144 bytes)
 
-__global__ __launch_bounds__(256) void attn_bwd_prep_bf16_kernel(
-    const bf16* __restrict__ o, const bf16* __restrict__ o_lo, const bf16* __restrict__ dout,
-    float* __restrict__ delta, float* __restrict__ dq, long long rows) {
+// Eight threads per (head, row): row r of the flattened [B*H, T] index space
+// is head r / T, position r % T.
+__global__ __launch_bounds__(256) void attn_bwd_prep_bf16_kernel(const BwdArgs a, int rows) {
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = gid >> 3;
+  const int row = (int)(gid >> 3);  // rows < 2^31
   const int part = (int)(gid & 7);
   float acc = 0.f;
   if (row < rows) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + row * kHeadDim + part * 8);
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dout + row * kHeadDim + part * 8);
-    if (o_lo) {
-      const bf16x8 c = *reinterpret_cast<const bf16x8*>(o_lo + row * kHeadDim + part * 8);
+    const int hd = row / a.T, t = row - hd * a.T;
+    const bf16* o = static_cast<const bf16*>(a.o) + head_base(a.lo, hd, a.H) + t * a.lo.t;
+    const bf16* dout = static_cast<const bf16*>(a.dout) + head_base(a.ldo, hd, a.H) + t * a.ldo.t;
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + part * 8);
+    const bf16x8 y = *reinterpret_cast<const bf16x8*>(dout + part * 8);
+    if (a.o_lo) {
+      const bf16* o_lo =
+          static_cast<const bf16*>(a.o_lo) + head_base(a.llo, hd, a.H) + t * a.llo.t;
+      const bf16x8 c = *reinterpret_cast<const bf16x8*>(o_lo + part * 8);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc = fmaf((float)a[t] + (float)c[t], (float)b[t], acc);
+      for (int i = 0; i < 8; ++i) acc = fmaf((float)x[i] + (float)c[i], (float)y[i], acc);
     } else {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc = fmaf((float)a[t], (float)b[t], acc);
+      for (int i = 0; i < 8; ++i) acc = fmaf((float)x[i], (float)y[i], acc);
     }
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    f32x4* dst = reinterpret_cast<f32x4*>(dq + row * kHeadDim + part * 8);
+    f32x4* dst = reinterpret_cast<f32x4*>(a.dq + head_base(a.ldq, hd, a.H) + t * a.ldq.t +
+                                          part * 8);
     dst[0] = z;
     dst[1] = z;
   }
   acc += __shfl_xor(acc, 1, 64);
   acc += __shfl_xor(acc, 2, 64);
   acc += __shfl_xor(acc, 4, 64);
-  if (row < rows && part == 0) delta[row] = acc;
+  if (row < rows && part == 0) a.delta[row] = acc;
 }
 
 // Loading a 64-query tile is split in two so the global loads can be issued
@@ -85,15 +91,15 @@ struct TileRegs {
   float lse, del;
 };
 
-__device__ __forceinline__ void bwd_load_tile(const bf16* qh, const bf16* doh, const float* lse,
-                                              const float* delta, int qs, int T, int tid,
-                                              TileRegs& r) {
+__device__ __forceinline__ void bwd_load_tile(const bf16* qh, int ldq, const bf16* doh, int lddo,
+                                              const float* lse, const float* delta, int qs, int T,
+                                              int tid, TileRegs& r) {
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int c = tid + kLoaders * p;
     const int row = min(qs + (c >> 3), T - 1), col = (c & 7) * 8;
-    r.q[p] = *reinterpret_cast<const bf16x8*>(qh + (size_t)row * kHeadDim + col);
-    r.d[p] = *reinterpret_cast<const bf16x8*>(doh + (size_t)row * kHeadDim + col);
+    r.q[p] = *reinterpret_cast<const bf16x8*>(qh + row * ldq + col);
+    r.d[p] = *reinterpret_cast<const bf16x8*>(doh + row * lddo + col);
   }
   const int row = min(qs + (tid & (kBQ - 1)), T - 1);
   r.lse = lse[row];
@@ -156,11 +162,11 @@ __device__ __forceinline__ void bwd_p_ds(const f32x16& s, const f32x16& dp, cons
   }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const bf16* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, float* __restrict__ dq, float* __restrict__ dk,
-    float* __restrict__ dv, int n_heads, int T, int n_ktiles, float scale, float scale_log2) {
+// Row strides inside one head are 32-bit (the host checks T * stride < 2^31);
+// head offsets are 64-bit.
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(const BwdArgs a,
+                                                                         int n_ktiles, float scale,
+                                                                         float scale_log2) {
   // All tiles fp16, row-major; transposed operands come from lds_operand_tr.
   __shared__ __attribute__((aligned(16))) f16 sK[kBK * kRowQ];          // [key][d]
   __shared__ __attribute__((aligned(16))) f16 sQ[2][kBQ * kRowQ];       // [q][d]
@@ -170,7 +176,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
   __shared__ __attribute__((aligned(16))) float sL[2][kBQ];             // LSE * log2(e)
   __shared__ __attribute__((aligned(16))) float sD[2][kBQ];             // delta
 
-  const TileMap tm = map_tile_xcd(blockIdx.x, n_heads, n_ktiles, false);
+  const int T = a.T;
+  const TileMap tm = map_tile_xcd(blockIdx.x, a.n_heads, n_ktiles, false);
   if (!tm.valid) return;
 
   const int tid = threadIdx.x;
@@ -182,14 +189,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
   const bool loader = wave >= 4;
   const int ltid = tid - kLoaders;
 
-  const size_t hoff = (size_t)tm.head * (size_t)T * kHeadDim;
   const size_t roff = (size_t)tm.head * (size_t)T;
-  const bf16* qh = q + hoff;
-  const bf16* kh = k + hoff;
-  const bf16* vh = v + hoff;
-  const bf16* doh = dout + hoff;
-  const float* lseh = lse + roff;
-  const float* delh = delta + roff;
+  const bf16* __restrict__ qh = static_cast<const bf16*>(a.q) + head_base(a.lq, tm.head, a.H);
+  const bf16* __restrict__ kh = static_cast<const bf16*>(a.k) + head_base(a.lk, tm.head, a.H);
+  const bf16* __restrict__ vh = static_cast<const bf16*>(a.v) + head_base(a.lv, tm.head, a.H);
+  const bf16* __restrict__ doh =
+      static_cast<const bf16*>(a.dout) + head_base(a.ldo, tm.head, a.H);
+  const int ldq = (int)a.lq.t, ldk = (int)a.lk.t, ldv = (int)a.lv.t, lddo = (int)a.ldo.t;
+  const float* lseh = a.lse + roff;
+  const float* delh = a.delta + roff;
 
   const int k0 = tm.tile * kBK;
   const int kw0 = k0 + wave * 32;
@@ -200,9 +208,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     kf[kk] = bf16x8_to_f16x8(
-        load_bf16x8(kh + (size_t)my_key * kHeadDim + kk * 16 + 8 * hf, my_key < T));
+        load_bf16x8(kh + my_key * ldk + kk * 16 + 8 * hf, my_key < T));
     vf[kk] = bf16x8_to_f16x8(
-        load_bf16x8(vh + (size_t)my_key * kHeadDim + kk * 16 + 8 * hf, my_key < T));
+        load_bf16x8(vh + my_key * ldv + kk * 16 + 8 * hf, my_key < T));
   }
   // All 256 keys of K, row-major fp16, for the dQ product.
 #pragma unroll
@@ -210,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
     const int c = tid + kThreads * p;  // 0..2047: key c/8, 8 dims at (c%8)*8
     const int row = c >> 3, col = (c & 7) * 8;
     *reinterpret_cast<f16x8*>(&sK[row * kRowQ + col]) = bf16x8_to_f16x8(
-        load_bf16x8(kh + (size_t)(k0 + row) * kHeadDim + col, k0 + row < T));
+        load_bf16x8(kh + (k0 + row) * ldk + col, k0 + row < T));
   }
 
   f32x16 dvacc[2], dkacc[2];
@@ -224,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
 
   TileRegs nxt;
   if (loader) {
-    bwd_load_tile(qh, doh, lseh, delh, k0, T, ltid, nxt);
+    bwd_load_tile(qh, ldq, doh, lddo, lseh, delh, k0, T, ltid, nxt);
     bwd_store_tile(sQ[0], sdO[0], sL[0], sD[0], nxt, k0, T, ltid);
   }
   __syncthreads();
@@ -233,7 +241,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
   for (int qs = k0; qs < T; qs += kBQ, buf ^= 1) {
     // Prefetch the next tile into registers while this one is computed.
     const bool has_next = qs + kBQ < T;
-    if (loader && has_next) bwd_load_tile(qh, doh, lseh, delh, qs + kBQ, T, ltid, nxt);
+    if (loader && has_next) bwd_load_tile(qh, ldq, doh, lddo, lseh, delh, qs + kBQ, T, ltid, nxt);
 
     const f16* cQ = sQ[buf];
     const f16* cdO = sdO[buf];
@@ -317,16 +325,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
     if (khalf == 0 && qb0 < T) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] += sPart[blk][r][lane];
-      float* dqh = dq + hoff + (size_t)qb0 * kHeadDim + db * 32 + l32;
+      const int lddq = (int)a.ldq.t;
+      float* dqh = a.dq + head_base(a.ldq, tm.head, a.H) + qb0 * lddq + db * 32 + l32;
       if (qb0 + 32 <= T) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          atomicAdd(dqh + (size_t)(8 * (r >> 2) + 4 * hf + (r & 3)) * kHeadDim, acc[r] * scale);
+          atomicAdd(dqh + (8 * (r >> 2) + 4 * hf + (r & 3)) * lddq, acc[r] * scale);
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qr = 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (qb0 + qr < T) atomicAdd(dqh + (size_t)qr * kHeadDim, acc[r] * scale);
+          if (qb0 + qr < T) atomicAdd(dqh + qr * lddq, acc[r] * scale);
         }
       }
     }
@@ -336,45 +345,37 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(
 
   // ---- epilogue: dV, dK = s * acc (lane: its key; 4 consecutive dims per store)
   if (my_key < T) {
-    float* dvr = dv + hoff + (size_t)my_key * kHeadDim;
-    float* dkr = dk + hoff + (size_t)my_key * kHeadDim;
+    float* dvr = a.dv + head_base(a.ldv, tm.head, a.H) + my_key * a.ldv.t;
+    float* dkr = a.dk + head_base(a.ldk, tm.head, a.H) + my_key * a.ldk.t;
 #pragma unroll
     for (int db2 = 0; db2 < 2; ++db2)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = db2 * 32 + 8 * g + 4 * hf;
-        f32x4 a = {dvacc[db2][4 * g], dvacc[db2][4 * g + 1], dvacc[db2][4 * g + 2],
+        f32x4 x = {dvacc[db2][4 * g], dvacc[db2][4 * g + 1], dvacc[db2][4 * g + 2],
                    dvacc[db2][4 * g + 3]};
-        f32x4 b = {dkacc[db2][4 * g] * scale, dkacc[db2][4 * g + 1] * scale,
+        f32x4 y = {dkacc[db2][4 * g] * scale, dkacc[db2][4 * g + 1] * scale,
                    dkacc[db2][4 * g + 2] * scale, dkacc[db2][4 * g + 3] * scale};
-        *reinterpret_cast<f32x4*>(dvr + d) = a;
-        *reinterpret_cast<f32x4*>(dkr + d) = b;
+        *reinterpret_cast<f32x4*>(dvr + d) = x;
+        *reinterpret_cast<f32x4*>(dkr + d) = y;
       }
   }
 }
 
 }  // namespace
 
-hipError_t launch_bwd_prep_bf16(const void* o, const void* o_lo, const void* dout, float* dq,
-                                float* delta, int n_heads, int T, hipStream_t stream) {
-  const long long rows = (long long)n_heads * T;
-  const unsigned prep_blocks = (unsigned)((rows * 8 + 255) / 256);
-  hipLaunchKernelGGL(attn_bwd_prep_bf16_kernel, dim3(prep_blocks), dim3(256), 0, stream,
-                     static_cast<const bf16*>(o), static_cast<const bf16*>(o_lo),
-                     static_cast<const bf16*>(dout), delta, dq, rows);
+hipError_t launch_bwd_prep_bf16(const BwdArgs& a, hipStream_t stream) {
+  const int rows = a.n_heads * a.T;
+  const unsigned prep_blocks = (unsigned)(((long long)rows * 8 + 255) / 256);
+  hipLaunchKernelGGL(attn_bwd_prep_bf16_kernel, dim3(prep_blocks), dim3(256), 0, stream, a, rows);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_main_bf16(const void* q, const void* k, const void* v, const void* dout,
-                                const float* lse, const float* delta, float* dq, float* dk,
-                                float* dv, int n_heads, int T, hipStream_t stream) {
-  const int n_ktiles = (T + kBK - 1) / kBK;
+hipError_t launch_bwd_main_bf16(const BwdArgs& a, hipStream_t stream) {
+  const int n_ktiles = (a.T + kBK - 1) / kBK;
   const float scale = 0.125f;  // 1/sqrt(64)
-  hipLaunchKernelGGL(attn_bwd_main_bf16_kernel, dim3(tiled_grid(n_heads, n_ktiles)),
-                     dim3(kThreads), 0, stream, static_cast<const bf16*>(q),
-                     static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-                     static_cast<const bf16*>(dout), lse, delta, dq, dk, dv, n_heads, T,
-                     n_ktiles, scale, scale * kLog2e);
+  hipLaunchKernelGGL(attn_bwd_main_bf16_kernel, dim3(tiled_grid(a.n_heads, n_ktiles)),
+                     dim3(kThreads), 0, stream, a, n_ktiles, scale, scale * kLog2e);
   return hipGetLastError();
 }
 

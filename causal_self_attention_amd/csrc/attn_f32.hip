@@ -14,7 +14,8 @@
 // first; then dK, dV with two threads per key (32 dims each) looping over
 // the query tiles at and after the key, and dQ with two threads per query
 // looping over the key tiles up to the query. Nothing is accumulated with
-// atomics, so every output is bitwise reproducible.
+// atomics, so every output is bitwise reproducible. Operands are addressed
+// through per-tensor element strides (D contiguous), like the bf16 path.
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -23,21 +24,31 @@ namespace {
 
 constexpr int kD = kHeadDim;
 
-__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ o, float* __restrict__ lse, int T, int n_tiles, float scale) {
+__device__ __forceinline__ const float* fptr(const void* base, const Layout& L, int hd, int H) {
+  return static_cast<const float*>(base) + head_base(L, hd, H);
+}
+__device__ __forceinline__ float* fptr_w(void* base, const Layout& L, int hd, int H) {
+  return static_cast<float*>(base) + head_base(L, hd, H);
+}
+
+__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const FwdArgs a, int n_tiles,
+                                                          float scale) {
   __shared__ float Ks[64 * kD];
   __shared__ float Vs[64 * kD];
+  const int T = a.T;
   const int tid = threadIdx.x;
   const int head = blockIdx.x / n_tiles;
   const int q0 = (blockIdx.x % n_tiles) * 64;
   const int i = q0 + tid;
-  const size_t hoff = (size_t)head * T * kD;
+  const float* qh = fptr(a.q, a.lq, head, a.H);
+  const float* kh = fptr(a.k, a.lk, head, a.H);
+  const float* vh = fptr(a.v, a.lv, head, a.H);
+  const long long ldq = a.lq.t, ldk = a.lk.t, ldv = a.lv.t;
 
   float qr[kD], acc[kD];
 #pragma unroll
   for (int d = 0; d < kD; ++d) {
-    qr[d] = i < T ? q[hoff + (size_t)i * kD + d] : 0.f;
+    qr[d] = i < T ? qh[i * ldq + d] : 0.f;
     acc[d] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
@@ -45,10 +56,10 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
   for (int k0 = 0; k0 < kv_end; k0 += 64) {
     __syncthreads();
     for (int e = tid; e < 64 * kD; e += 64) {
-      const int r = e / kD;
+      const int r = e / kD, d = e % kD;
       const bool ok = k0 + r < T;
-      Ks[e] = ok ? k[hoff + (size_t)k0 * kD + e] : 0.f;
-      Vs[e] = ok ? v[hoff + (size_t)k0 * kD + e] : 0.f;
+      Ks[e] = ok ? kh[(k0 + r) * ldk + d] : 0.f;
+      Vs[e] = ok ? vh[(k0 + r) * ldv + d] : 0.f;
     }
     __syncthreads();
     float sc[64];
@@ -78,71 +89,71 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
   }
   if (i < T) {
     const float inv = 1.f / l;
+    float* orow = fptr_w(a.o, a.lo, head, a.H) + i * a.lo.t;
 #pragma unroll
-    for (int d = 0; d < kD; ++d) o[hoff + (size_t)i * kD + d] = acc[d] * inv;
-    lse[(size_t)head * T + i] = m + logf(l);
+    for (int d = 0; d < kD; ++d) orow[d] = acc[d] * inv;
+    a.lse[(size_t)head * T + i] = m + logf(l);
   }
 }
 
-__global__ __launch_bounds__(256) void attn_bwd_prep_f32_kernel(
-    const float* __restrict__ o, const float* __restrict__ dout, float* __restrict__ delta,
-    long long rows) {
+// Eight threads per (head, row); row r of [B*H, T] is head r / T, position r % T.
+__global__ __launch_bounds__(256) void attn_bwd_prep_f32_kernel(const BwdArgs a, int rows) {
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = gid >> 3;
+  const int row = (int)(gid >> 3);
   const int part = (int)(gid & 7);
   float acc = 0.f;
   if (row < rows) {
+    const int hd = row / a.T, t = row - hd * a.T;
+    const float* o = fptr(a.o, a.lo, hd, a.H) + t * a.lo.t + part * 8;
+    const float* dout = fptr(a.dout, a.ldo, hd, a.H) + t * a.ldo.t + part * 8;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const long long e = row * kD + part * 8 + t;
-      acc = fmaf(o[e], dout[e], acc);
-    }
+    for (int e = 0; e < 8; ++e) acc = fmaf(o[e], dout[e], acc);
   }
   acc += __shfl_xor(acc, 1, 64);
   acc += __shfl_xor(acc, 2, 64);
   acc += __shfl_xor(acc, 4, 64);
-  if (row < rows && part == 0) delta[row] = acc;
+  if (row < rows && part == 0) a.delta[row] = acc;
 }
 
 // dK, dV: thread pair (key j, half) holds 32 dims of K_j, V_j, dK_j, dV_j.
-__global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const float* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv, int T,
-    int n_tiles, float scale) {
+__global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(const BwdArgs a, int n_tiles,
+                                                               float scale) {
   __shared__ float Qs[32 * kD];
   __shared__ float dOs[32 * kD];
   __shared__ float lses[32];
   __shared__ float dels[32];
+  const int T = a.T;
   const int tid = threadIdx.x;
   const int head = blockIdx.x / n_tiles;
   const int k0 = (blockIdx.x % n_tiles) * 32;
   const int j = k0 + (tid >> 1);
   const int half = tid & 1;
-  const size_t hoff = (size_t)head * T * kD;
+  const float* qh = fptr(a.q, a.lq, head, a.H);
+  const float* kh = fptr(a.k, a.lk, head, a.H);
+  const float* vh = fptr(a.v, a.lv, head, a.H);
+  const float* doh = fptr(a.dout, a.ldo, head, a.H);
   const size_t roff = (size_t)head * T;
 
   float kr[32], vr[32], dka[32], dva[32];
 #pragma unroll
   for (int d = 0; d < 32; ++d) {
-    const size_t e = hoff + (size_t)j * kD + half * 32 + d;
-    kr[d] = j < T ? k[e] : 0.f;
-    vr[d] = j < T ? v[e] : 0.f;
+    kr[d] = j < T ? kh[j * a.lk.t + half * 32 + d] : 0.f;
+    vr[d] = j < T ? vh[j * a.lv.t + half * 32 + d] : 0.f;
     dka[d] = 0.f;
     dva[d] = 0.f;
   }
   for (int qs = k0; qs < T; qs += 32) {
     __syncthreads();
     for (int e = tid; e < 32 * kD; e += 64) {
-      const int r = e / kD;
+      const int r = e / kD, d = e % kD;
       const bool ok = qs + r < T;
-      Qs[e] = ok ? q[hoff + (size_t)qs * kD + e] : 0.f;
-      dOs[e] = ok ? dout[hoff + (size_t)qs * kD + e] : 0.f;
+      Qs[e] = ok ? qh[(qs + r) * a.lq.t + d] : 0.f;
+      dOs[e] = ok ? doh[(qs + r) * a.ldo.t + d] : 0.f;
     }
     if (tid < 32) {
       const bool ok = qs + tid < T;
-      lses[tid] = ok ? lse[roff + qs + tid] : 0.f;
-      dels[tid] = ok ? delta[roff + qs + tid] : 0.f;
+      lses[tid] = ok ? a.lse[roff + qs + tid] : 0.f;
+      dels[tid] = ok ? a.delta[roff + qs + tid] : 0.f;
     }
     __syncthreads();
     for (int ii = 0; ii < 32; ++ii) {
@@ -167,48 +178,50 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(
     }
   }
   if (j < T) {
+    float* dkr = fptr_w(a.dk, a.ldk, head, a.H) + j * a.ldk.t + half * 32;
+    float* dvr = fptr_w(a.dv, a.ldv, head, a.H) + j * a.ldv.t + half * 32;
 #pragma unroll
     for (int d = 0; d < 32; ++d) {
-      const size_t e = hoff + (size_t)j * kD + half * 32 + d;
-      dk[e] = dka[d] * scale;
-      dv[e] = dva[d];
+      dkr[d] = dka[d] * scale;
+      dvr[d] = dva[d];
     }
   }
 }
 
 // dQ: thread pair (query i, half) holds 32 dims of Q_i, dO_i, dQ_i.
-__global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const float* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, float* __restrict__ dq, int T, int n_tiles, float scale) {
+__global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(const BwdArgs a, int n_tiles,
+                                                             float scale) {
   __shared__ float Ks[32 * kD];
   __shared__ float Vs[32 * kD];
+  const int T = a.T;
   const int tid = threadIdx.x;
   const int head = blockIdx.x / n_tiles;
   const int q0 = (blockIdx.x % n_tiles) * 32;
   const int i = q0 + (tid >> 1);
   const int half = tid & 1;
-  const size_t hoff = (size_t)head * T * kD;
+  const float* qh = fptr(a.q, a.lq, head, a.H);
+  const float* kh = fptr(a.k, a.lk, head, a.H);
+  const float* vh = fptr(a.v, a.lv, head, a.H);
+  const float* doh = fptr(a.dout, a.ldo, head, a.H);
   const size_t roff = (size_t)head * T;
 
   float qr[32], dor[32], dqa[32];
 #pragma unroll
   for (int d = 0; d < 32; ++d) {
-    const size_t e = hoff + (size_t)i * kD + half * 32 + d;
-    qr[d] = i < T ? q[e] : 0.f;
-    dor[d] = i < T ? dout[e] : 0.f;
+    qr[d] = i < T ? qh[i * a.lq.t + half * 32 + d] : 0.f;
+    dor[d] = i < T ? doh[i * a.ldo.t + half * 32 + d] : 0.f;
     dqa[d] = 0.f;
   }
-  const float lse_i = i < T ? lse[roff + i] : 0.f;
-  const float del_i = i < T ? delta[roff + i] : 0.f;
+  const float lse_i = i < T ? a.lse[roff + i] : 0.f;
+  const float del_i = i < T ? a.delta[roff + i] : 0.f;
   const int kv_end = min(T, q0 + 32);
   for (int k0 = 0; k0 < kv_end; k0 += 32) {
     __syncthreads();
     for (int e = tid; e < 32 * kD; e += 64) {
-      const int r = e / kD;
+      const int r = e / kD, d = e % kD;
       const bool ok = k0 + r < T;
-      Ks[e] = ok ? k[hoff + (size_t)k0 * kD + e] : 0.f;
-      Vs[e] = ok ? v[hoff + (size_t)k0 * kD + e] : 0.f;
+      Ks[e] = ok ? kh[(k0 + r) * a.lk.t + d] : 0.f;
+      Vs[e] = ok ? vh[(k0 + r) * a.lv.t + d] : 0.f;
     }
     __syncthreads();
     for (int jj = 0; jj < 32; ++jj) {
@@ -230,41 +243,35 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(
     }
   }
   if (i < T) {
+    float* dqr = fptr_w(a.dq, a.ldq, head, a.H) + i * a.ldq.t + half * 32;
 #pragma unroll
-    for (int d = 0; d < 32; ++d) dq[hoff + (size_t)i * kD + half * 32 + d] = dqa[d] * scale;
+    for (int d = 0; d < 32; ++d) dqr[d] = dqa[d] * scale;
   }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          int n_heads, int T, hipStream_t stream) {
-  const int n_tiles = (T + 63) / 64;
-  hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3((unsigned)n_heads * n_tiles), dim3(64), 0, stream,
-                     q, k, v, o, lse, T, n_tiles, 0.125f);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
+  const int n_tiles = (a.T + 63) / 64;
+  hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3((unsigned)a.n_heads * n_tiles), dim3(64), 0,
+                     stream, a, n_tiles, 0.125f);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_prep_f32(const float* o, const float* dout, float* delta, int n_heads,
-                               int T, hipStream_t stream) {
-  const long long rows = (long long)n_heads * T;
-  hipLaunchKernelGGL(attn_bwd_prep_f32_kernel, dim3((unsigned)((rows * 8 + 255) / 256)),
-                     dim3(256), 0, stream, o, dout, delta, rows);
+hipError_t launch_bwd_prep_f32(const BwdArgs& a, hipStream_t stream) {
+  const int rows = a.n_heads * a.T;
+  hipLaunchKernelGGL(attn_bwd_prep_f32_kernel, dim3((unsigned)(((long long)rows * 8 + 255) / 256)),
+                     dim3(256), 0, stream, a, rows);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_main_f32(const float* q, const float* k, const float* v,
-                               const float* dout, const float* lse, const float* delta,
-                               float* dq, float* dk, float* dv, int n_heads, int T,
-                               hipStream_t stream) {
-  const int n_tiles = (T + 31) / 32;
-  const dim3 grid((unsigned)n_heads * n_tiles);
-  hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel, grid, dim3(64), 0, stream, q, k, v, dout, lse,
-                     delta, dk, dv, T, n_tiles, 0.125f);
+hipError_t launch_bwd_main_f32(const BwdArgs& a, hipStream_t stream) {
+  const int n_tiles = (a.T + 31) / 32;
+  const dim3 grid((unsigned)a.n_heads * n_tiles);
+  hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel, grid, dim3(64), 0, stream, a, n_tiles, 0.125f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dq_f32_kernel, grid, dim3(64), 0, stream, q, k, v, dout, lse, delta,
-                     dq, T, n_tiles, 0.125f);
+  hipLaunchKernelGGL(attn_bwd_dq_f32_kernel, grid, dim3(64), 0, stream, a, n_tiles, 0.125f);
   return hipGetLastError();
 }
 

@@ -47,14 +47,14 @@ struct KVRegs {
   bf16x8 k[2], v[2];
 };
 
-__device__ __forceinline__ void fwd_load_tile(const bf16* kh, const bf16* vh, int k0, int T,
-                                              int tid, KVRegs& r) {
+__device__ __forceinline__ void fwd_load_tile(const bf16* kh, int ldk, const bf16* vh, int ldv,
+                                              int k0, int T, int tid, KVRegs& r) {
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int c = tid + kThreads * p;
     const int row = min(k0 + (c >> 3), T - 1), col = (c & 7) * 8;
-    r.k[p] = *reinterpret_cast<const bf16x8*>(kh + (size_t)row * kHeadDim + col);
-    r.v[p] = *reinterpret_cast<const bf16x8*>(vh + (size_t)row * kHeadDim + col);
+    r.k[p] = *reinterpret_cast<const bf16x8*>(kh + row * ldk + col);
+    r.v[p] = *reinterpret_cast<const bf16x8*>(vh + row * ldv + col);
   }
 }
 
@@ -150,10 +150,10 @@ __device__ __forceinline__ void fwd_tile(const bf16* cK, const f16* cV, const bf
   }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    bf16* __restrict__ o, bf16* __restrict__ o_lo, float* __restrict__ lse, int n_heads, int T,
-    int n_qtiles, float scale_log2) {
+// Row strides inside one head are 32-bit (the host checks T * stride < 2^31);
+// head offsets are 64-bit.
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdArgs a, int n_qtiles,
+                                                                    float scale_log2) {
   // LDS: two K/V tile buffers (K bf16, V fp16, both [key][d]). Buffer 1 also
   // holds the 128 x 64 Q tile during the prologue: Q fragments are read from
   // LDS so no global load inside the tile loop's dependence chain targets
@@ -164,7 +164,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   bf16* Qs = Kbuf(1);  // [query][d], 128 rows: spans K and V of buffer 1
   static_assert(kBM * kRow <= 2 * kBN * kRow, "Q tile must fit in buffer 1");
 
-  const TileMap tm = map_tile_xcd(blockIdx.x, n_heads, n_qtiles, true);
+  const int T = a.T;
+  const TileMap tm = map_tile_xcd(blockIdx.x, a.n_heads, n_qtiles, true);
   if (!tm.valid) return;
 
   const int tid = threadIdx.x;
@@ -172,24 +173,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
 
-  const size_t hoff = (size_t)tm.head * (size_t)T * kHeadDim;
-  const bf16* qh = q + hoff;
-  const bf16* kh = k + hoff;
-  const bf16* vh = v + hoff;
+  const bf16* __restrict__ qh = static_cast<const bf16*>(a.q) + head_base(a.lq, tm.head, a.H);
+  const bf16* __restrict__ kh = static_cast<const bf16*>(a.k) + head_base(a.lk, tm.head, a.H);
+  const bf16* __restrict__ vh = static_cast<const bf16*>(a.v) + head_base(a.lv, tm.head, a.H);
+  const int ldq = (int)a.lq.t, ldk = (int)a.lk.t, ldv = (int)a.lv.t;
 
   const int q0 = tm.tile * kBM;
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + l32;  // the query column this lane owns
 
   KVRegs nxt;
-  fwd_load_tile(kh, vh, 0, T, tid, nxt);
+  fwd_load_tile(kh, ldk, vh, ldv, 0, T, tid, nxt);
   {
     bf16x8 xq[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int c = tid + kThreads * p;  // 0..1023: query c/8, dims (c%8)*8
       const int row = min(q0 + (c >> 3), T - 1);
-      xq[p] = *reinterpret_cast<const bf16x8*>(qh + (size_t)row * kHeadDim + (c & 7) * 8);
+      xq[p] = *reinterpret_cast<const bf16x8*>(qh + row * ldq + (c & 7) * 8);
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   for (; kt < n_full; ++kt, buf ^= 1) {
     const int k0 = kt * kBN;
     const bool has_next = kt + 1 < n_kt;
-    if (has_next) fwd_load_tile(kh, vh, k0 + kBN, T, tid, nxt);
+    if (has_next) fwd_load_tile(kh, ldk, vh, ldv, k0 + kBN, T, tid, nxt);
     fwd_tile<false>(Kbuf(buf), Vbuf(buf), qf, k0, my_q, T, l32, hf, lane, scale_log2, st);
     if (has_next) fwd_store_tile(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid);
     __syncthreads();
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   for (; kt < n_kt; ++kt, buf ^= 1) {
     const int k0 = kt * kBN;
     const bool has_next = kt + 1 < n_kt;
-    if (has_next) fwd_load_tile(kh, vh, k0 + kBN, T, tid, nxt);
+    if (has_next) fwd_load_tile(kh, ldk, vh, ldv, k0 + kBN, T, tid, nxt);
     fwd_tile<true>(Kbuf(buf), Vbuf(buf), qf, k0, my_q, T, l32, hf, lane, scale_log2, st);
     if (has_next) fwd_store_tile(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid);
     __syncthreads();
@@ -246,8 +247,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const float l_tot = st.l_run + wave_xor32(st.l_run);
   const float inv = 1.f / l_tot;
   if (my_q < T) {
-    bf16* orow = o + hoff + (size_t)my_q * kHeadDim;
-    bf16* lrow = o_lo ? o_lo + hoff + (size_t)my_q * kHeadDim : nullptr;
+    bf16* orow = static_cast<bf16*>(a.o) + head_base(a.lo, tm.head, a.H) + my_q * (int)a.lo.t;
+    bf16* lrow = a.o_lo ? static_cast<bf16*>(a.o_lo) + head_base(a.llo, tm.head, a.H) +
+                              my_q * (int)a.llo.t
+                        : nullptr;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -263,20 +266,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * g + 4 * hf) = hi;
         if (lrow) *reinterpret_cast<bf16x4*>(lrow + db * 32 + 8 * g + 4 * hf) = lo;
       }
-    if (hf == 0) lse[(size_t)tm.head * T + my_q] = (st.m_run + fast_log2(l_tot)) * kLn2;
+    if (hf == 0) a.lse[(size_t)tm.head * T + my_q] = (st.m_run + fast_log2(l_tot)) * kLn2;
   }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, void* o_lo,
-                           float* lse, int n_heads, int T, hipStream_t stream) {
-  const int n_qtiles = (T + kBM - 1) / kBM;
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
+  const int n_qtiles = (a.T + kBM - 1) / kBM;
   const float scale_log2 = 0.125f * kLog2e;  // 1/sqrt(64) * log2(e)
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(tiled_grid(n_heads, n_qtiles)), dim3(kThreads),
-                     0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                     static_cast<const bf16*>(v), static_cast<bf16*>(o), static_cast<bf16*>(o_lo),
-                     lse, n_heads, T, n_qtiles, scale_log2);
+  hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(tiled_grid(a.n_heads, n_qtiles)), dim3(kThreads),
+                     0, stream, a, n_qtiles, scale_log2);
   return hipGetLastError();
 }
 

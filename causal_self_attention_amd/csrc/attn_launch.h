@@ -42,20 +42,51 @@ inline unsigned tiled_grid(int n_heads, int n_tiles) {
   return 8u * (unsigned)((n_heads + 7) / 8) * (unsigned)n_tiles;
 }
 
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, void* o_lo,
-                           float* lse, int n_heads, int T, hipStream_t stream);
-hipError_t launch_bwd_prep_bf16(const void* o, const void* o_lo, const void* dout, float* dq,
-                                float* delta, int n_heads, int T, hipStream_t stream);
-hipError_t launch_bwd_main_bf16(const void* q, const void* k, const void* v, const void* dout,
-                                const float* lse, const float* delta, float* dq, float* dk,
-                                float* dv, int n_heads, int T, hipStream_t stream);
-hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          int n_heads, int T, hipStream_t stream);
-hipError_t launch_bwd_prep_f32(const float* o, const float* dout, float* delta, int n_heads,
-                               int T, hipStream_t stream);
-hipError_t launch_bwd_main_f32(const float* q, const float* k, const float* v,
-                               const float* dout, const float* lse, const float* delta,
-                               float* dq, float* dk, float* dv, int n_heads, int T,
-                               hipStream_t stream);
+// Element strides of one [B, H, T, D] operand whose last (D) dimension is
+// contiguous: element (b, h, t, d) lives at b*b_ + h*h_ + t*t_ + d.
+struct Layout {
+  long long b, h, t;
+};
+
+// Offset in elements of head hd = b*H + h.
+__host__ __device__ __forceinline__ long long head_base(const Layout& L, int hd, int H) {
+  return (long long)(hd / H) * L.b + (long long)(hd % H) * L.h;
+}
+
+// Kernel arguments, passed by value. q, k, v, o, o_lo, dout are the input
+// dtype; lse, delta, dq, dk, dv fp32. lse and delta are contiguous [B, H, T].
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  void* o_lo;  // may be null (bf16 only)
+  float* lse;
+  Layout lq, lk, lv, lo, llo;
+  int n_heads, H, T;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* o_lo;  // may be null (bf16 only)
+  const void* dout;
+  const float* lse;
+  float* delta;
+  float* dq;
+  float* dk;
+  float* dv;
+  Layout lq, lk, lv, lo, llo, ldo, ldq, ldk, ldv;
+  int n_heads, H, T;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_prep_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_main_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_prep_f32(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_main_f32(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace gpt_attn

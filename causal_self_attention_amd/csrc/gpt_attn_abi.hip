@@ -8,12 +8,18 @@
 
 namespace {
 
+using gpt_attn::Layout;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Shape and dtype checks shared by every entry point. On success *rows is
-// B*H*T (possibly 0 for an empty call).
-int check_shape(int dtype, int B, int H, int T, int D, long long* rows) {
+struct Shape {
+  int dtype, B, H, T, D;
+  long long rows;  // B*H*T
+  long long esize; // bytes per element of q, k, v, o, dout
+};
+
+// Shape and dtype checks shared by every entry point.
+int check_shape(int dtype, int B, int H, int T, int D, Shape* s) {
   if (dtype != GPT_ATTN_F32 && dtype != GPT_ATTN_BF16) return GPT_ATTN_E_INVAL;
   if (B < 0 || H < 0 || T < 0 || D <= 0) return GPT_ATTN_E_INVAL;
   if (D != 64) return GPT_ATTN_E_UNSUPPORTED;
@@ -27,11 +33,155 @@ int check_shape(int dtype, int B, int H, int T, int D, long long* rows) {
     const long long tiles = ((long long)T + 31) / 32;
     if (8LL * ((heads + 7) / 8) * tiles >= (1LL << 31)) return GPT_ATTN_E_INVAL;
   }
-  *rows = r;
+  s->dtype = dtype;
+  s->B = B;
+  s->H = H;
+  s->T = T;
+  s->D = D;
+  s->rows = r;
+  s->esize = dtype == GPT_ATTN_BF16 ? 2 : 4;
+  return GPT_ATTN_OK;
+}
+
+// The layout a descriptor names, or the contiguous [B, H, T, D] one for NULL.
+Layout resolve(const gpt_attn_layout* l, const Shape& s) {
+  if (!l) {
+    const long long row = s.D, head = row * s.T, batch = head * s.H;
+    return Layout{batch, head, row};
+  }
+  return Layout{l->batch, l->head, l->row};
+}
+
+// Checks one operand's layout (see the header for the rules). esize is the
+// operand's element size in bytes; output operands must not overlap
+// themselves.
+int check_layout(const Layout& L, const Shape& s, long long esize, bool output) {
+  const long long st[3] = {L.b, L.h, L.t};
+  const long long ext[3] = {s.B, s.H, s.T};
+  const long long unit = 16 / esize;  // elements per 16 bytes
+  __int128 span = s.D;                // elements from the first to past the last
+  for (int i = 0; i < 3; ++i) {
+    if (st[i] < 0) return GPT_ATTN_E_LAYOUT;
+    if (ext[i] > 1) {
+      if (st[i] % unit != 0) return GPT_ATTN_E_LAYOUT;
+      span += (__int128)st[i] * (ext[i] - 1);
+    }
+  }
+  if (span >= ((__int128)1 << 48)) return GPT_ATTN_E_LAYOUT;
+  // The kernels address rows inside one head with 32-bit offsets.
+  if ((long long)(s.T - 1) * L.t + s.D > INT32_MAX) return GPT_ATTN_E_LAYOUT;
+  if (output) {
+    // Sufficient condition for distinct addresses: with the dimensions of
+    // extent > 1 sorted by stride (D first: stride 1, extent D), each stride
+    // exceeds the largest offset the smaller ones reach.
+    long long ds[4] = {1, 0, 0, 0}, de[4] = {s.D, 0, 0, 0};
+    int n = 1;
+    for (int i = 0; i < 3; ++i)
+      if (ext[i] > 1) {
+        ds[n] = st[i];
+        de[n] = ext[i];
+        ++n;
+      }
+    for (int i = 1; i < n; ++i)
+      for (int j = i; j > 0 && ds[j] < ds[j - 1]; --j) {
+        const long long a = ds[j], b = de[j];
+        ds[j] = ds[j - 1];
+        de[j] = de[j - 1];
+        ds[j - 1] = a;
+        de[j - 1] = b;
+      }
+    __int128 reach = 0;
+    for (int i = 0; i < n; ++i) {
+      if ((__int128)ds[i] <= reach) return GPT_ATTN_E_LAYOUT;
+      reach += (__int128)ds[i] * (de[i] - 1);
+    }
+  }
   return GPT_ATTN_OK;
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? GPT_ATTN_OK : GPT_ATTN_E_HIP; }
+
+#define GA_TRY(expr)                       \
+  do {                                     \
+    const int st_ = (expr);                \
+    if (st_ != GPT_ATTN_OK) return st_;    \
+  } while (0)
+
+int check_workspace(const void* workspace, size_t bytes, const Shape& s) {
+  if (!workspace || bytes < (size_t)s.rows * sizeof(float)) return GPT_ATTN_E_WORKSPACE;
+  if (!aligned16(workspace)) return GPT_ATTN_E_ALIGN;
+  return GPT_ATTN_OK;
+}
+
+// Validated arguments of the backward phases. which: 1 = prep, 2 = main,
+// 3 = both.
+int bwd_args(const Shape& s, int which, const void* q, const gpt_attn_layout* lq, const void* k,
+             const gpt_attn_layout* lk, const void* v, const gpt_attn_layout* lv, const void* o,
+             const gpt_attn_layout* lo, const void* o_lo, const gpt_attn_layout* llo,
+             const void* dout, const gpt_attn_layout* ldo, const float* lse, float* dq,
+             const gpt_attn_layout* ldq, float* dk, const gpt_attn_layout* ldk, float* dv,
+             const gpt_attn_layout* ldv, const void* workspace, size_t workspace_bytes,
+             gpt_attn::BwdArgs* a) {
+  const bool prep = which & 1, main = which & 2;
+  const bool bf16 = s.dtype == GPT_ATTN_BF16;
+  if (!dout) return GPT_ATTN_E_INVAL;
+  if (prep && (!o || (bf16 && !dq))) return GPT_ATTN_E_INVAL;
+  if (main && (!q || !k || !v || !lse || !dq || !dk || !dv)) return GPT_ATTN_E_INVAL;
+  if (o_lo && !bf16) return GPT_ATTN_E_INVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(o_lo) ||
+      !aligned16(dout) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return GPT_ATTN_E_ALIGN;
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->o = o;
+  a->o_lo = prep ? o_lo : nullptr;
+  a->dout = dout;
+  a->lse = lse;
+  a->delta = static_cast<float*>(const_cast<void*>(workspace));
+  a->dq = dq;
+  a->dk = dk;
+  a->dv = dv;
+  a->lq = resolve(lq, s);
+  a->lk = resolve(lk, s);
+  a->lv = resolve(lv, s);
+  a->lo = resolve(lo, s);
+  a->llo = resolve(llo, s);
+  a->ldo = resolve(ldo, s);
+  a->ldq = resolve(ldq, s);
+  a->ldk = resolve(ldk, s);
+  a->ldv = resolve(ldv, s);
+  GA_TRY(check_layout(a->ldo, s, s.esize, false));
+  if (prep) {
+    GA_TRY(check_layout(a->lo, s, s.esize, false));
+    if (o_lo) GA_TRY(check_layout(a->llo, s, 2, false));
+  }
+  if (prep || main) {
+    if (dq) GA_TRY(check_layout(a->ldq, s, 4, true));
+  }
+  if (main) {
+    GA_TRY(check_layout(a->lq, s, s.esize, false));
+    GA_TRY(check_layout(a->lk, s, s.esize, false));
+    GA_TRY(check_layout(a->lv, s, s.esize, false));
+    GA_TRY(check_layout(a->ldk, s, 4, true));
+    GA_TRY(check_layout(a->ldv, s, 4, true));
+  }
+  GA_TRY(check_workspace(workspace, workspace_bytes, s));
+  a->n_heads = s.B * s.H;
+  a->H = s.H;
+  a->T = s.T;
+  return GPT_ATTN_OK;
+}
+
+int run_prep(const Shape& s, const gpt_attn::BwdArgs& a, hipStream_t st) {
+  return launch_status(s.dtype == GPT_ATTN_BF16 ? gpt_attn::launch_bwd_prep_bf16(a, st)
+                                                : gpt_attn::launch_bwd_prep_f32(a, st));
+}
+
+int run_main(const Shape& s, const gpt_attn::BwdArgs& a, hipStream_t st) {
+  return launch_status(s.dtype == GPT_ATTN_BF16 ? gpt_attn::launch_bwd_main_bf16(a, st)
+                                                : gpt_attn::launch_bwd_main_f32(a, st));
+}
 
 }  // namespace
 
@@ -53,106 +203,137 @@ const char* gpt_attn_status_string(int status) {
       return "workspace missing or smaller than gpt_attn_bwd_workspace_bytes";
     case GPT_ATTN_E_HIP:
       return "HIP runtime error at kernel launch";
+    case GPT_ATTN_E_LAYOUT:
+      return "bad layout (negative or misaligned stride, overlapping output, or offsets "
+             "beyond the supported range)";
     default:
       return "unknown status";
   }
 }
 
-int gpt_attn_fwd(int dtype, int B, int H, int T, int D, const void* q, const void* k,
-                 const void* v, void* o, void* o_lo, float* lse, void* stream) {
-  long long rows = 0;
-  const int st = check_shape(dtype, B, H, T, D, &rows);
-  if (st != GPT_ATTN_OK) return st;
-  if (rows == 0) return GPT_ATTN_OK;
+int gpt_attn_fwd_strided(int dtype, int B, int H, int T, int D, const void* q,
+                         const gpt_attn_layout* lq, const void* k, const gpt_attn_layout* lk,
+                         const void* v, const gpt_attn_layout* lv, void* o,
+                         const gpt_attn_layout* lo, void* o_lo, const gpt_attn_layout* llo,
+                         float* lse, void* stream) {
+  Shape s;
+  GA_TRY(check_shape(dtype, B, H, T, D, &s));
+  if (s.rows == 0) return GPT_ATTN_OK;
   if (!q || !k || !v || !o || !lse) return GPT_ATTN_E_INVAL;
   if (o_lo && dtype != GPT_ATTN_BF16) return GPT_ATTN_E_INVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
       !aligned16(o_lo))
     return GPT_ATTN_E_ALIGN;
-  const int heads = B * H;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == GPT_ATTN_BF16)
-    return launch_status(gpt_attn::launch_fwd_bf16(q, k, v, o, o_lo, lse, heads, T, s));
-  return launch_status(gpt_attn::launch_fwd_f32(static_cast<const float*>(q),
-                                                static_cast<const float*>(k),
-                                                static_cast<const float*>(v),
-                                                static_cast<float*>(o), lse, heads, T, s));
+  gpt_attn::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.o_lo = o_lo;
+  a.lse = lse;
+  a.lq = resolve(lq, s);
+  a.lk = resolve(lk, s);
+  a.lv = resolve(lv, s);
+  a.lo = resolve(lo, s);
+  a.llo = resolve(llo, s);
+  GA_TRY(check_layout(a.lq, s, s.esize, false));
+  GA_TRY(check_layout(a.lk, s, s.esize, false));
+  GA_TRY(check_layout(a.lv, s, s.esize, false));
+  GA_TRY(check_layout(a.lo, s, s.esize, true));
+  if (o_lo) GA_TRY(check_layout(a.llo, s, 2, true));
+  a.n_heads = B * H;
+  a.H = H;
+  a.T = T;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launch_status(dtype == GPT_ATTN_BF16 ? gpt_attn::launch_fwd_bf16(a, st)
+                                              : gpt_attn::launch_fwd_f32(a, st));
+}
+
+int gpt_attn_fwd(int dtype, int B, int H, int T, int D, const void* q, const void* k,
+                 const void* v, void* o, void* o_lo, float* lse, void* stream) {
+  return gpt_attn_fwd_strided(dtype, B, H, T, D, q, nullptr, k, nullptr, v, nullptr, o, nullptr,
+                              o_lo, nullptr, lse, stream);
 }
 
 size_t gpt_attn_bwd_workspace_bytes(int dtype, int B, int H, int T, int D) {
-  long long rows = 0;
-  if (check_shape(dtype, B, H, T, D, &rows) != GPT_ATTN_OK) return 0;
-  return (size_t)rows * sizeof(float);
+  Shape s;
+  if (check_shape(dtype, B, H, T, D, &s) != GPT_ATTN_OK) return 0;
+  return (size_t)s.rows * sizeof(float);
+}
+
+int gpt_attn_bwd_prep_strided(int dtype, int B, int H, int T, int D, const void* o,
+                              const gpt_attn_layout* lo, const void* o_lo,
+                              const gpt_attn_layout* llo, const void* dout,
+                              const gpt_attn_layout* ldo, float* dq, const gpt_attn_layout* ldq,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  GA_TRY(check_shape(dtype, B, H, T, D, &s));
+  if (s.rows == 0) return GPT_ATTN_OK;
+  gpt_attn::BwdArgs a;
+  GA_TRY(bwd_args(s, 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, o, lo, o_lo, llo,
+                  dout, ldo, nullptr, dq, ldq, nullptr, nullptr, nullptr, nullptr, workspace,
+                  workspace_bytes, &a));
+  return run_prep(s, a, static_cast<hipStream_t>(stream));
+}
+
+int gpt_attn_bwd_main_strided(int dtype, int B, int H, int T, int D, const void* q,
+                              const gpt_attn_layout* lq, const void* k, const gpt_attn_layout* lk,
+                              const void* v, const gpt_attn_layout* lv, const void* dout,
+                              const gpt_attn_layout* ldo, const float* lse, float* dq,
+                              const gpt_attn_layout* ldq, float* dk, const gpt_attn_layout* ldk,
+                              float* dv, const gpt_attn_layout* ldv, const void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  Shape s;
+  GA_TRY(check_shape(dtype, B, H, T, D, &s));
+  if (s.rows == 0) return GPT_ATTN_OK;
+  gpt_attn::BwdArgs a;
+  GA_TRY(bwd_args(s, 2, q, lq, k, lk, v, lv, nullptr, nullptr, nullptr, nullptr, dout, ldo, lse,
+                  dq, ldq, dk, ldk, dv, ldv, workspace, workspace_bytes, &a));
+  return run_main(s, a, static_cast<hipStream_t>(stream));
+}
+
+int gpt_attn_bwd_strided(int dtype, int B, int H, int T, int D, const void* q,
+                         const gpt_attn_layout* lq, const void* k, const gpt_attn_layout* lk,
+                         const void* v, const gpt_attn_layout* lv, const void* o,
+                         const gpt_attn_layout* lo, const void* o_lo, const gpt_attn_layout* llo,
+                         const void* dout, const gpt_attn_layout* ldo, const float* lse,
+                         float* dq, const gpt_attn_layout* ldq, float* dk,
+                         const gpt_attn_layout* ldk, float* dv, const gpt_attn_layout* ldv,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  GA_TRY(check_shape(dtype, B, H, T, D, &s));
+  if (s.rows == 0) return GPT_ATTN_OK;
+  // Validate everything both phases need before enqueuing either.
+  gpt_attn::BwdArgs a;
+  GA_TRY(bwd_args(s, 3, q, lq, k, lk, v, lv, o, lo, o_lo, llo, dout, ldo, lse, dq, ldq, dk, ldk,
+                  dv, ldv, workspace, workspace_bytes, &a));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  GA_TRY(run_prep(s, a, st));
+  return run_main(s, a, st);
 }
 
 int gpt_attn_bwd_prep(int dtype, int B, int H, int T, int D, const void* o, const void* o_lo,
                       const void* dout, float* dq, void* workspace, size_t workspace_bytes,
                       void* stream) {
-  long long rows = 0;
-  const int st = check_shape(dtype, B, H, T, D, &rows);
-  if (st != GPT_ATTN_OK) return st;
-  if (rows == 0) return GPT_ATTN_OK;
-  if (!o || !dout || (dtype == GPT_ATTN_BF16 && !dq)) return GPT_ATTN_E_INVAL;
-  if (o_lo && dtype != GPT_ATTN_BF16) return GPT_ATTN_E_INVAL;
-  if (!aligned16(o) || !aligned16(o_lo) || !aligned16(dout) || !aligned16(dq))
-    return GPT_ATTN_E_ALIGN;
-  if (!workspace || workspace_bytes < (size_t)rows * sizeof(float)) return GPT_ATTN_E_WORKSPACE;
-  if (!aligned16(workspace)) return GPT_ATTN_E_ALIGN;
-  float* delta = static_cast<float*>(workspace);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int heads = B * H;
-  if (dtype == GPT_ATTN_BF16)
-    return launch_status(gpt_attn::launch_bwd_prep_bf16(o, o_lo, dout, dq, delta, heads, T, s));
-  return launch_status(gpt_attn::launch_bwd_prep_f32(static_cast<const float*>(o),
-                                                     static_cast<const float*>(dout), delta,
-                                                     heads, T, s));
+  return gpt_attn_bwd_prep_strided(dtype, B, H, T, D, o, nullptr, o_lo, nullptr, dout, nullptr,
+                                   dq, nullptr, workspace, workspace_bytes, stream);
 }
 
 int gpt_attn_bwd_main(int dtype, int B, int H, int T, int D, const void* q, const void* k,
                       const void* v, const void* dout, const float* lse, float* dq, float* dk,
                       float* dv, const void* workspace, size_t workspace_bytes, void* stream) {
-  long long rows = 0;
-  const int st = check_shape(dtype, B, H, T, D, &rows);
-  if (st != GPT_ATTN_OK) return st;
-  if (rows == 0) return GPT_ATTN_OK;
-  if (!q || !k || !v || !dout || !lse || !dq || !dk || !dv) return GPT_ATTN_E_INVAL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(lse) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
-    return GPT_ATTN_E_ALIGN;
-  if (!workspace || workspace_bytes < (size_t)rows * sizeof(float)) return GPT_ATTN_E_WORKSPACE;
-  if (!aligned16(workspace)) return GPT_ATTN_E_ALIGN;
-  const float* delta = static_cast<const float*>(workspace);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int heads = B * H;
-  if (dtype == GPT_ATTN_BF16)
-    return launch_status(
-        gpt_attn::launch_bwd_main_bf16(q, k, v, dout, lse, delta, dq, dk, dv, heads, T, s));
-  return launch_status(gpt_attn::launch_bwd_main_f32(
-      static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-      static_cast<const float*>(dout), lse, delta, dq, dk, dv, heads, T, s));
+  return gpt_attn_bwd_main_strided(dtype, B, H, T, D, q, nullptr, k, nullptr, v, nullptr, dout,
+                                   nullptr, lse, dq, nullptr, dk, nullptr, dv, nullptr, workspace,
+                                   workspace_bytes, stream);
 }
 
 int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const void* k,
                  const void* v, const void* o, const void* o_lo, const void* dout,
                  const float* lse, float* dq, float* dk, float* dv, void* workspace,
                  size_t workspace_bytes, void* stream) {
-  long long rows = 0;
-  const int st = check_shape(dtype, B, H, T, D, &rows);
-  if (st != GPT_ATTN_OK) return st;
-  if (rows == 0) return GPT_ATTN_OK;
-  // Validate everything both phases need before enqueuing either.
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return GPT_ATTN_E_INVAL;
-  if (o_lo && dtype != GPT_ATTN_BF16) return GPT_ATTN_E_INVAL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
-      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(o_lo))
-    return GPT_ATTN_E_ALIGN;
-  if (!workspace || workspace_bytes < (size_t)rows * sizeof(float)) return GPT_ATTN_E_WORKSPACE;
-  if (!aligned16(workspace)) return GPT_ATTN_E_ALIGN;
-  const int r = gpt_attn_bwd_prep(dtype, B, H, T, D, o, o_lo, dout, dq, workspace,
-                                  workspace_bytes, stream);
-  if (r != GPT_ATTN_OK) return r;
-  return gpt_attn_bwd_main(dtype, B, H, T, D, q, k, v, dout, lse, dq, dk, dv, workspace,
-                           workspace_bytes, stream);
+  return gpt_attn_bwd_strided(dtype, B, H, T, D, q, nullptr, k, nullptr, v, nullptr, o, nullptr,
+                              o_lo, nullptr, dout, nullptr, lse, dq, nullptr, dk, nullptr, dv,
+                              nullptr, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -15,8 +15,12 @@
  * Flash Attention").
  *
  * Conventions shared by every entry point
- *   - Layout: every tensor is contiguous row-major [B, H, T, D]; per-row
- *     statistics (lse, and the delta vector in the workspace) are [B, H, T].
+ *   - Layout: q, k, v, o, o_lo, dout, dq, dk, dv are logically [B, H, T, D].
+ *     The plain entry points take them contiguous row-major; the *_strided
+ *     ones take a gpt_attn_layout per operand (below), so that q, k, v can be
+ *     read straight out of a projection's [B, T, 3C] output and o written
+ *     into a [B, T, C] buffer. Per-row statistics (lse, and the delta vector
+ *     in the workspace) are always contiguous [B, H, T] fp32.
  *   - Scale: always 1/sqrt(D). Causal masking is always on: key j is visible
  *     to query i iff j <= i. There is no mask, scale or dropout argument.
  *   - Pointers are DEVICE pointers (hipMalloc or torch CUDA tensors) and must
@@ -45,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GPT_ATTN_ABI_VERSION 1
+#define GPT_ATTN_ABI_VERSION 2
 
 /* Status codes returned by every int-returning entry point. */
 enum gpt_attn_status {
@@ -55,8 +59,42 @@ enum gpt_attn_status {
   GPT_ATTN_E_UNSUPPORTED = 2, /* a head dimension D with no kernel (D != 64) */
   GPT_ATTN_E_ALIGN = 3,       /* a pointer that is not 16-byte aligned */
   GPT_ATTN_E_WORKSPACE = 4,   /* workspace NULL or smaller than gpt_attn_bwd_workspace_bytes */
-  GPT_ATTN_E_HIP = 5          /* the HIP runtime reported an error when launching */
+  GPT_ATTN_E_HIP = 5,         /* the HIP runtime reported an error when launching */
+  GPT_ATTN_E_LAYOUT = 6       /* a gpt_attn_layout breaking the rules below */
 };
+
+/*
+ * Element strides of one logically [B, H, T, D] operand whose D elements are
+ * contiguous: element (b, h, t, d) is at base[b*batch + h*head + t*row + d].
+ * A NULL layout pointer means contiguous [B, H, T, D] (row = D, head = T*D,
+ * batch = H*T*D).
+ *
+ * The causal self-attention layer projects every token to q, k and v with
+ * one linear layer and splits the result into heads (page "nanoGPT: a real
+ * GPT in two 300-line files", section 2 "How the code works"). With that
+ * layer's output qkv of shape [B, T, 3C], C = H*D, the head views are
+ *   q: base = qkv,      batch = 3*T*C, head = D, row = 3*C
+ *   k: base = qkv + C,  same strides;  v: base = qkv + 2*C, same strides
+ * and the merged output y of shape [B, T, C] is batch = T*C, head = D, row = C.
+ *
+ * Rules (GPT_ATTN_E_LAYOUT otherwise):
+ *   - strides are >= 0; those of dimensions with extent > 1 are multiples
+ *     of 16 bytes (8 bf16 or 4 fp32 elements), so every row starts 16-byte
+ *     aligned given an aligned base pointer;
+ *   - (T-1)*row + D fits in a signed 32-bit integer (offsets inside one
+ *     head are 32-bit in the kernels), and the whole operand spans below
+ *     2^48 elements;
+ *   - an output (o, o_lo, dq, dk, dv) does not overlap itself: sorted by
+ *     stride (D counting as stride 1, extent D), every stride exceeds the
+ *     largest offset the smaller ones reach.
+ * Inputs may overlap each other (q, k, v in one buffer). Outputs must not
+ * overlap inputs or each other; this is not checked.
+ */
+typedef struct gpt_attn_layout {
+  long long batch;
+  long long head;
+  long long row;
+} gpt_attn_layout;
 
 /* Element type of q, k, v, o and dout. lse, dq, dk, dv are always fp32. */
 enum gpt_attn_dtype {
@@ -141,6 +179,40 @@ int gpt_attn_bwd_prep(int dtype, int B, int H, int T, int D, const void* o, cons
 int gpt_attn_bwd_main(int dtype, int B, int H, int T, int D, const void* q, const void* k,
                       const void* v, const void* dout, const float* lse, float* dq, float* dk,
                       float* dv, const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Strided forms of the four calls above: each operand pointer is followed by
+ * its layout (NULL = contiguous [B,H,T,D]). Operand meanings, dtypes,
+ * workspace and errors are those of the plain entry points, which are these
+ * calls with every layout NULL. lse and the workspace's delta stay
+ * contiguous [B,H,T]. gpt_attn_bwd_main_strided expects dq in the layout the
+ * preceding gpt_attn_bwd_prep_strided zero-filled.
+ */
+int gpt_attn_fwd_strided(int dtype, int B, int H, int T, int D, const void* q,
+                         const gpt_attn_layout* lq, const void* k, const gpt_attn_layout* lk,
+                         const void* v, const gpt_attn_layout* lv, void* o,
+                         const gpt_attn_layout* lo, void* o_lo, const gpt_attn_layout* llo,
+                         float* lse, void* stream);
+int gpt_attn_bwd_strided(int dtype, int B, int H, int T, int D, const void* q,
+                         const gpt_attn_layout* lq, const void* k, const gpt_attn_layout* lk,
+                         const void* v, const gpt_attn_layout* lv, const void* o,
+                         const gpt_attn_layout* lo, const void* o_lo, const gpt_attn_layout* llo,
+                         const void* dout, const gpt_attn_layout* ldo, const float* lse,
+                         float* dq, const gpt_attn_layout* ldq, float* dk,
+                         const gpt_attn_layout* ldk, float* dv, const gpt_attn_layout* ldv,
+                         void* workspace, size_t workspace_bytes, void* stream);
+int gpt_attn_bwd_prep_strided(int dtype, int B, int H, int T, int D, const void* o,
+                              const gpt_attn_layout* lo, const void* o_lo,
+                              const gpt_attn_layout* llo, const void* dout,
+                              const gpt_attn_layout* ldo, float* dq, const gpt_attn_layout* ldq,
+                              void* workspace, size_t workspace_bytes, void* stream);
+int gpt_attn_bwd_main_strided(int dtype, int B, int H, int T, int D, const void* q,
+                              const gpt_attn_layout* lq, const void* k, const gpt_attn_layout* lk,
+                              const void* v, const gpt_attn_layout* lv, const void* dout,
+                              const gpt_attn_layout* ldo, const float* lse, float* dq,
+                              const gpt_attn_layout* ldq, float* dk, const gpt_attn_layout* ldk,
+                              float* dv, const gpt_attn_layout* ldv, const void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code. Never NULL. */
 const char* gpt_attn_status_string(int status);

@@ -16,7 +16,7 @@ import causal_self_attention_amd as gattn
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gpt_attn.h")
 
-OK, E_INVAL, E_UNSUP, E_ALIGN, E_WS, E_HIP = 0, 1, 2, 3, 4, 5
+OK, E_INVAL, E_UNSUP, E_ALIGN, E_WS, E_HIP, E_LAYOUT = 0, 1, 2, 3, 4, 5, 6
 F32, BF16 = 0, 1
 P = 0x10000  # 16-byte aligned fake device address, never dereferenced
 
@@ -54,7 +54,7 @@ def test_abi_version_matches_header(lib):
 
 
 def test_status_strings(lib):
-    for st in range(6):
+    for st in range(7):
         assert gattn.gpt_attn_status_string(st)
     assert gattn.gpt_attn_status_string(99) == "unknown status"
 
@@ -128,3 +128,104 @@ def test_binding_refuses_host_tensors(lib):
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         gattn.gpt_attn_fwd(q, q, q, q, None, torch.zeros(1, 1, 4))
+
+
+# ---- strided entry points --------------------------------------------------------
+
+L = gattn.GptAttnLayout
+
+
+def lay(batch, head, row):
+    return ctypes.byref(L(batch, head, row))
+
+
+def fused(B, H, T, D=64):
+    """Layouts of q/k/v inside a [B, T, 3C] projection output and of O in [B, T, C]."""
+    C = H * D
+    return L(3 * T * C, D, 3 * C), L(T * C, D, C)
+
+
+def fwd_s(lib, dtype=BF16, B=2, H=3, T=8, D=64, lq=None, lk=None, lv=None, lo=None, llo=None,
+          o_lo=None):
+    r = lambda x: None if x is None else ctypes.byref(x)
+    return lib.gpt_attn_fwd_strided(dtype, B, H, T, D, P, r(lq), P, r(lk), P, r(lv), P, r(lo),
+                                    o_lo, r(llo), P, None)
+
+
+def bwd_s(lib, dtype=BF16, B=2, H=3, T=8, D=64, ws=None, ws_bytes=0, **lays):
+    r = lambda n: None if lays.get(n) is None else ctypes.byref(lays[n])
+    return lib.gpt_attn_bwd_strided(dtype, B, H, T, D, P, r("q"), P, r("k"), P, r("v"), P,
+                                    r("o"), None, None, P, r("do"), P, P, r("dq"), P, r("dk"),
+                                    P, r("dv"), ws, ws_bytes, None)
+
+
+def test_strided_layout_rules_forward(lib):
+    B, H, T = 2, 3, 8
+    qkv, out = fused(B, H, T)
+    # Negative and misaligned strides, for inputs and outputs alike.
+    for name in ("lq", "lk", "lv", "lo"):
+        assert fwd_s(lib, **{name: L(-8, 64, 64 * H)}) == E_LAYOUT, name
+        assert fwd_s(lib, **{name: L(qkv.batch, qkv.head, qkv.row + 1)}) == E_LAYOUT, name
+        assert fwd_s(lib, **{name: L(qkv.batch, 60, qkv.row)}) == E_LAYOUT, name
+    # fp32 rows are 16-byte aligned at multiples of 4 elements, bf16 at 8.
+    assert fwd_s(lib, lq=L(qkv.batch, qkv.head, qkv.row + 4)) == E_LAYOUT
+    assert bwd_s(lib, dtype=F32, q=L(4 * 1000, 4 * 100, 68)) == E_WS  # accepted
+    assert bwd_s(lib, dtype=F32, q=L(4 * 1000, 4 * 100, 66)) == E_LAYOUT
+    assert bwd_s(lib, q=L(4 * 1000, 4 * 100, 68)) == E_LAYOUT  # bf16 needs 8
+    # Strides of extent-1 dimensions need no alignment.
+    assert bwd_s(lib, B=1, q=L(3, 64, 64 * 3)) == E_WS
+    # An output overlapping itself: rows closer than D, heads sharing rows,
+    # batches sharing heads.
+    assert fwd_s(lib, lo=L(out.batch, out.head, 32)) == E_LAYOUT
+    assert fwd_s(lib, lo=L(out.batch, 0, out.row)) == E_LAYOUT
+    assert fwd_s(lib, lo=L(0, out.head, out.row)) == E_LAYOUT
+    assert fwd_s(lib, o_lo=P, llo=L(out.batch, out.head, 8)) == E_LAYOUT
+    assert fwd_s(lib, dtype=F32, lo=L(out.batch, out.head, 60)) == E_LAYOUT
+    # Offsets inside one head must fit 32 bits.
+    assert fwd_s(lib, T=1 << 16, lq=L(0, 64, 1 << 16)) == E_LAYOUT
+
+
+def test_strided_backward_accepts_the_fused_layout(lib):
+    """Every layout check passes for the projection layout (the call then
+    stops at the missing workspace, before any launch)."""
+    B, H, T = 2, 3, 8
+    qkv, out = fused(B, H, T)
+    g = L(3 * T * H * 64, 64, 3 * H * 64)  # fp32 gradients in a [B, T, 3C] buffer
+    kw = dict(q=qkv, k=qkv, v=qkv, o=out, do=out, dq=g, dk=g, dv=g)
+    assert bwd_s(lib, **kw) == E_WS
+    assert bwd_s(lib, dtype=F32, **kw) == E_WS
+    # Inputs may overlap (a broadcast head), outputs may not.
+    assert bwd_s(lib, **{**kw, "k": L(3 * T * H * 64, 0, 3 * H * 64)}) == E_WS
+    assert bwd_s(lib, **{**kw, "dk": L(3 * T * H * 64, 0, 3 * H * 64)}) == E_LAYOUT
+    assert bwd_s(lib, **{**kw, "dq": L(-4, 64, 64)}) == E_LAYOUT
+    assert bwd_s(lib, **{**kw, "do": L(8, 64, 3)}) == E_LAYOUT
+
+
+def test_plain_calls_equal_strided_calls_with_null_layouts(lib):
+    # Same validation outcome either way.
+    assert fwd_s(lib, D=32) == fwd(lib, D=32) == E_UNSUP
+    assert bwd_s(lib) == E_WS
+    assert lib.gpt_attn_bwd_prep_strided(BF16, 1, 1, 8, 64, P, None, None, None, P, None, P,
+                                         ctypes.byref(L(0, 0, 32)), P, 1 << 20, None) == E_LAYOUT
+    assert lib.gpt_attn_bwd_main_strided(BF16, 1, 1, 8, 64, P, None, P, None, P, None, P, None,
+                                         P, P, None, P, None, P, ctypes.byref(L(0, 0, 32)), None,
+                                         0, None) == E_LAYOUT
+
+
+def test_view_helpers_match_the_fused_layout():
+    import torch
+    B, T, H, D = 2, 5, 3, 64
+    qkv = torch.arange(B * T * 3 * H * D, dtype=torch.float32).view(B, T, 3 * H * D)
+    q, k, v = gattn.split_qkv_heads(qkv, H)
+    qkv_l, out_l = fused(B, H, T)
+    for i, t in enumerate((q, k, v)):
+        assert tuple(t.shape) == (B, H, T, D)
+        assert t.stride() == (qkv_l.batch, qkv_l.head, qkv_l.row, 1)
+        assert t.storage_offset() == i * H * D
+        # element (b, h, t, d) is the projection's column (i*C + h*D + d) of token t
+        assert t[1, 2, 3, 4].item() == qkv[1, 3, i * H * D + 2 * D + 4].item()
+    y = torch.zeros(B, T, H * D)
+    o = gattn.merged_heads_view(y, H)
+    assert o.stride() == (out_l.batch, out_l.head, out_l.row, 1)
+    o[1, 2, 3, 4] = 7.0
+    assert y[1, 3, 2 * D + 4].item() == 7.0
