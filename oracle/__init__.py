@@ -56,6 +56,22 @@ def _load():
     lib.oracle_attn_head_intermediates.argtypes = [L, L, _DP, _DP, _DP, _DP, _DP, _DP,
                                                    _DP, _DP]
     lib.oracle_attn_head_intermediates.restype = I
+    U32P = ctypes.POINTER(ctypes.c_uint32)
+    U8P = ctypes.POINTER(ctypes.c_uint8)
+    LP = ctypes.POINTER(ctypes.c_long)
+    lib.oracle_philox4x32_10.argtypes = [U32P, U32P, U32P]
+    lib.oracle_philox4x32_10.restype = None
+    lib.oracle_dropout_threshold.argtypes = [ctypes.c_double]
+    lib.oracle_dropout_threshold.restype = L
+    lib.oracle_dropout_keep.argtypes = [L, LP, L, ctypes.c_double, ctypes.c_uint64,
+                                        ctypes.c_uint32, U8P]
+    lib.oracle_dropout_keep.restype = I
+    lib.oracle_attn_fwd_dropout.argtypes = [L, L, L, _DP, _DP, _DP, U8P, ctypes.c_double, _DP,
+                                            _DP, I]
+    lib.oracle_attn_fwd_dropout.restype = I
+    lib.oracle_attn_bwd_dropout.argtypes = [L, L, L, _DP, _DP, _DP, _DP, U8P, ctypes.c_double,
+                                            _DP, _DP, _DP, I]
+    lib.oracle_attn_bwd_dropout.restype = I
     _lib = lib
     return lib
 
@@ -128,3 +144,93 @@ def head_intermediates(q, k, v, dout) -> dict:
     if st != 0:
         raise RuntimeError(f"oracle_attn_head_intermediates failed with status {st}")
     return {"P": P, "dP": dP, "dS": dS, "delta": delta}
+
+
+# ---- attention dropout ------------------------------------------------------------
+# Definitions in attn_oracle.c: keep mask M from Philox4x32-10 keyed by the
+# seed, counter (j div 8, i, b*H + h, offset); Pd = z M P with
+# z = 65536 / (65536 - thr), thr = round(p * 65536).
+
+def philox4x32_10(counter, key) -> tuple:
+    """One Philox4x32-10 block: four 32-bit outputs for a 4-word counter and a
+    2-word key."""
+    lib = _load()
+    c = (ctypes.c_uint32 * 4)(*[int(x) & 0xFFFFFFFF for x in counter])
+    k = (ctypes.c_uint32 * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+    out = (ctypes.c_uint32 * 4)()
+    lib.oracle_philox4x32_10(c, k, out)
+    return tuple(int(x) for x in out)
+
+
+def dropout_threshold(p: float) -> int:
+    """thr = round(p * 65536); raises for p outside [0, 1) or thr = 65536."""
+    thr = int(_load().oracle_dropout_threshold(float(p)))
+    if thr < 0:
+        raise ValueError(f"dropout probability {p} not in [0, 1) at 16-bit resolution")
+    return thr
+
+
+def dropout_scale(p: float) -> float:
+    """z = 1 / (1 - thr/65536)."""
+    thr = dropout_threshold(p)
+    return 65536.0 / (65536.0 - thr)
+
+
+def dropout_keep(heads, T: int, p: float, seed: int, offset: int) -> np.ndarray:
+    """Keep mask (uint8, 1 = kept, zero above the diagonal) of shape
+    [len(heads), T, T] for the flat head indices b*H + h in ``heads``."""
+    bh = np.ascontiguousarray(np.asarray(list(heads), dtype=np.int64))
+    n = int(bh.size)
+    keep = np.zeros((n, T, T), dtype=np.uint8)
+    st = _load().oracle_dropout_keep(n, bh.ctypes.data_as(ctypes.POINTER(ctypes.c_long)), T,
+                                     float(p), int(seed) & (2**64 - 1),
+                                     int(offset) & 0xFFFFFFFF,
+                                     keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+    if st != 0:
+        raise RuntimeError(f"oracle_dropout_keep failed with status {st}")
+    return keep
+
+
+def _keep_arg(keep, heads: int, T: int) -> np.ndarray:
+    keep = np.ascontiguousarray(np.asarray(keep, dtype=np.uint8))
+    if keep.size != heads * T * T:
+        raise ValueError(f"keep mask must hold {heads} x {T} x {T} entries")
+    return keep
+
+
+def attn_fwd_dropout(q, k, v, keep, z: float, nthreads: int | None = None):
+    """(O, LSE) in fp64 with attention dropout given by the explicit keep mask
+    [heads, T, T] and survivor scale z."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v shapes differ")
+    heads, T, D = _heads_shape(q)
+    keep = _keep_arg(keep, heads, T)
+    o = np.zeros(q.shape, dtype=np.float64)
+    lse = np.zeros(q.shape[:-1], dtype=np.float64)
+    st = _load().oracle_attn_fwd_dropout(
+        heads, T, D, _ptr(q), _ptr(k), _ptr(v),
+        keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), float(z), _ptr(o), _ptr(lse),
+        nthreads or _default_threads())
+    if st != 0:
+        raise RuntimeError(f"oracle_attn_fwd_dropout failed with status {st}")
+    return o, lse
+
+
+def attn_bwd_dropout(q, k, v, dout, keep, z: float, nthreads: int | None = None):
+    """(dQ, dK, dV) in fp64: the gradient of sum(dout * O) for attn_fwd_dropout."""
+    q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    if not (q.shape == k.shape == v.shape == dout.shape):
+        raise ValueError("q, k, v, dout shapes differ")
+    heads, T, D = _heads_shape(q)
+    keep = _keep_arg(keep, heads, T)
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(q.shape, dtype=np.float64)
+    dv = np.zeros(q.shape, dtype=np.float64)
+    st = _load().oracle_attn_bwd_dropout(
+        heads, T, D, _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+        keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), float(z), _ptr(dq), _ptr(dk),
+        _ptr(dv), nthreads or _default_threads())
+    if st != 0:
+        raise RuntimeError(f"oracle_attn_bwd_dropout failed with status {st}")
+    return dq, dk, dv

@@ -44,9 +44,15 @@
  * differences, the library routine scaled_dot_product_attention in fp64,
  * closed forms (row 0, all keys equal, T = 1), zero row sums of dS, column
  * sums of dK and dV, and equivariances.
+ *
+ * Attention dropout (the dropout_p argument of the fused call, same page,
+ * section 2) is the second half of this file: a keep mask M drawn from the
+ * counter-based generator Philox4x32-10, and forward / backward that take M
+ * explicitly (see the block comment there).
  */
 #include <math.h>
 #include <pthread.h>
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -282,4 +288,263 @@ int oracle_attn_head_intermediates(long T, long D, const double* q, const double
   free(o);
   free(p);
   return ORACLE_OK;
+}
+
+/* ==== attention dropout ===================================================
+ *
+ * nanoGPT passes dropout_p = its dropout rate to the fused attention call in
+ * training (page "nanoGPT: a real GPT in two 300-line files", section 2 "How
+ * the code works"): every attention weight P_ij is zeroed with probability
+ * p and the survivors are scaled by 1/(1-p), after the softmax and before
+ * the product with V.
+ *
+ * With a keep mask M (M_ij in {0, 1}) and z = 1/(1-p):
+ *   Pd_ij  = z M_ij P_ij,            O_i = sum_j Pd_ij V_j
+ *   LSE_i  as without dropout (the softmax is unchanged)
+ * Backward, the chain rule through the same three steps:
+ *   dPd_ij = sum_d dO_id V_jd,       dV_j = sum_i Pd_ij dO_i
+ *   dP_ij  = z M_ij dPd_ij
+ *   dS_ij  = P_ij (dP_ij - sum_k P_ik dP_ik)   (softmax Jacobian)
+ *   dQ_i   = s sum_j dS_ij K_j,      dK_j = s sum_i dS_ij Q_i
+ *
+ * The mask. The pages fix no generator; the one used here is
+ * Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+ * easy as 1, 2, 3", SC'11, section 4), a keyed bijection on 128-bit counters.
+ * For head bh (= b*H + h), query i, key j, with a 64-bit seed and a 32-bit
+ * offset (a caller-chosen stream number):
+ *   key     = (seed mod 2^32, seed div 2^32)
+ *   counter = (j div 8, i, bh, offset)
+ *   u_ij    = 16-bit field (j mod 2) of output word (j mod 8) div 2
+ *   thr     = round(p * 65536),  M_ij = [u_ij >= thr]
+ * so a dropped weight has probability thr/65536 (p rounded to a multiple of
+ * 2^-16), and z = 65536 / (65536 - thr) keeps E[z M] = 1 exactly.
+ */
+
+/* Philox4x32 with 10 rounds. One round: two 32x32 -> 64-bit products of
+ * counter words 0 and 2 with the round multipliers; the new words are
+ * (hi(M1*x2) ^ x1 ^ k0, lo(M1*x2), hi(M0*x0) ^ x3 ^ k1, lo(M0*x0)). Between
+ * rounds the key words are bumped by the Weyl constants (the golden ratio
+ * and sqrt(3) - 1 in 32-bit fixed point). */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+  uint32_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)M0 * x0;
+    const uint64_t p1 = (uint64_t)M1 * x2;
+    const uint32_t y0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0;
+    const uint32_t y1 = (uint32_t)p1;
+    const uint32_t y2 = (uint32_t)(p0 >> 32) ^ x3 ^ k1;
+    const uint32_t y3 = (uint32_t)p0;
+    x0 = y0;
+    x1 = y1;
+    x2 = y2;
+    x3 = y3;
+    k0 += W0;
+    k1 += W1;
+  }
+  out[0] = x0;
+  out[1] = x1;
+  out[2] = x2;
+  out[3] = x3;
+}
+
+/* thr = round(p * 65536) for 0 <= p < 1, or -1 when p is outside [0, 1) or
+ * rounds to 65536 (everything dropped). */
+long oracle_dropout_threshold(double p) {
+  if (!(p >= 0.0 && p < 1.0)) return -1;
+  const double t = floor(p * 65536.0 + 0.5);
+  return t >= 65536.0 ? -1 : (long)t;
+}
+
+/* Keep mask [n, T, T] (uint8, 1 = kept; zero above the diagonal) of the heads
+ * listed in bh[0..n-1] (flat b*H + h indices). */
+int oracle_dropout_keep(long n, const long* bh, long T, double p, uint64_t seed,
+                        uint32_t offset, uint8_t* keep) {
+  const long thr = oracle_dropout_threshold(p);
+  if (n < 0 || T < 0 || thr < 0 || (n > 0 && (!bh || !keep))) return ORACLE_EINVAL;
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  for (long h = 0; h < n; ++h) {
+    uint8_t* mh = keep + h * T * T;
+    memset(mh, 0, (size_t)(T * T));
+    for (long i = 0; i < T; ++i)
+      for (long j = 0; j <= i; ++j) {
+        const uint32_t ctr[4] = {(uint32_t)(j / 8), (uint32_t)i, (uint32_t)bh[h], offset};
+        uint32_t out[4];
+        oracle_philox4x32_10(ctr, key, out);
+        const uint32_t word = out[(j % 8) / 2];
+        const uint32_t u = (word >> (16 * (j % 2))) & 0xFFFFu;
+        mh[i * T + j] = u >= (uint32_t)thr ? 1 : 0;
+      }
+  }
+  return ORACLE_OK;
+}
+
+/* One head, forward with dropout. p is T doubles of scratch. */
+static void head_forward_dropout(long T, long D, const double* q, const double* k,
+                                 const double* v, const uint8_t* M, double z, double* o,
+                                 double* lse, double* p) {
+  const double s = 1.0 / sqrt((double)D);
+  for (long i = 0; i < T; ++i) {
+    const double li = softmax_row(i, D, s, q, k, p);
+    if (lse) lse[i] = li;
+    double* oi = o + i * D;
+    for (long d = 0; d < D; ++d) oi[d] = 0.0;
+    for (long j = 0; j <= i; ++j) {
+      const double pd = M[i * T + j] ? z * p[j] : 0.0;
+      const double* vj = v + j * D;
+      for (long d = 0; d < D; ++d) oi[d] += pd * vj[d];
+    }
+  }
+}
+
+/* One head, backward with dropout. p and dp are T doubles of scratch. */
+static void head_backward_dropout(long T, long D, const double* q, const double* k,
+                                  const double* v, const double* dout, const uint8_t* M,
+                                  double z, double* dq, double* dk, double* dv, double* p,
+                                  double* dp) {
+  const double s = 1.0 / sqrt((double)D);
+  memset(dq, 0, sizeof(double) * T * D);
+  memset(dk, 0, sizeof(double) * T * D);
+  memset(dv, 0, sizeof(double) * T * D);
+  for (long i = 0; i < T; ++i) {
+    softmax_row(i, D, s, q, k, p);
+    const double* qi = q + i * D;
+    const double* doi = dout + i * D;
+    double* dqi = dq + i * D;
+    double rowdot = 0.0; /* sum_k P_ik dP_ik */
+    for (long j = 0; j <= i; ++j) {
+      const double* vj = v + j * D;
+      double dpd = 0.0;
+      for (long d = 0; d < D; ++d) dpd += doi[d] * vj[d];
+      dp[j] = M[i * T + j] ? z * dpd : 0.0;
+      rowdot += p[j] * dp[j];
+      const double pd = M[i * T + j] ? z * p[j] : 0.0;
+      double* dvj = dv + j * D;
+      for (long d = 0; d < D; ++d) dvj[d] += pd * doi[d];
+    }
+    for (long j = 0; j <= i; ++j) {
+      const double ds = p[j] * (dp[j] - rowdot);
+      const double* kj = k + j * D;
+      double* dkj = dk + j * D;
+      for (long d = 0; d < D; ++d) {
+        dqi[d] += s * ds * kj[d];
+        dkj[d] += s * ds * qi[d];
+      }
+    }
+  }
+}
+
+typedef struct {
+  int backward;
+  long heads, T, D;
+  const double *q, *k, *v, *dout;
+  const uint8_t* keep;
+  double z;
+  double *o, *lse, *dq, *dk, *dv;
+  int tid, nthreads, status;
+} djob_t;
+
+static void* run_djob(void* arg) {
+  djob_t* jb = (djob_t*)arg;
+  const long T = jb->T, D = jb->D, E = T * D;
+  double* p = (double*)malloc(sizeof(double) * (size_t)T);
+  double* dp = (double*)malloc(sizeof(double) * (size_t)T);
+  if (!p || !dp) {
+    jb->status = ORACLE_ENOMEM;
+  } else {
+    for (long h = jb->tid; h < jb->heads; h += jb->nthreads) {
+      const uint8_t* M = jb->keep + h * T * T;
+      if (jb->backward)
+        head_backward_dropout(T, D, jb->q + h * E, jb->k + h * E, jb->v + h * E,
+                              jb->dout + h * E, M, jb->z, jb->dq + h * E, jb->dk + h * E,
+                              jb->dv + h * E, p, dp);
+      else
+        head_forward_dropout(T, D, jb->q + h * E, jb->k + h * E, jb->v + h * E, M, jb->z,
+                             jb->o + h * E, jb->lse ? jb->lse + h * T : NULL, p);
+    }
+    jb->status = ORACLE_OK;
+  }
+  free(p);
+  free(dp);
+  return NULL;
+}
+
+static int run_djobs(djob_t proto, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 1024) nthreads = 1024;
+  if ((long)nthreads > proto.heads) nthreads = (int)(proto.heads > 0 ? proto.heads : 1);
+  djob_t* jobs = (djob_t*)calloc((size_t)nthreads, sizeof(djob_t));
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  if (!jobs || !th) {
+    free(jobs);
+    free(th);
+    return ORACLE_ENOMEM;
+  }
+  for (int t = 0; t < nthreads; ++t) {
+    jobs[t] = proto;
+    jobs[t].tid = t;
+    jobs[t].nthreads = nthreads;
+  }
+  int started = 0;
+  for (int t = 1; t < nthreads; ++t) {
+    if (pthread_create(&th[t], NULL, run_djob, &jobs[t]) != 0) break;
+    started = t;
+  }
+  run_djob(&jobs[0]);
+  for (int t = 1; t <= started; ++t) pthread_join(th[t], NULL);
+  for (int t = started + 1; t < nthreads; ++t) run_djob(&jobs[t]);
+  int status = ORACLE_OK;
+  for (int t = 0; t < nthreads; ++t)
+    if (jobs[t].status != ORACLE_OK) status = jobs[t].status;
+  free(jobs);
+  free(th);
+  return status;
+}
+
+/* Forward with dropout: keep [heads, T, T] (uint8) and z = 1/(1-p). */
+int oracle_attn_fwd_dropout(long heads, long T, long D, const double* q, const double* k,
+                            const double* v, const uint8_t* keep, double z, double* o,
+                            double* lse, int nthreads) {
+  if (heads < 0 || T < 0 || D < 1 || !q || !k || !v || !keep || !o) return ORACLE_EINVAL;
+  if (heads == 0 || T == 0) return ORACLE_OK;
+  djob_t jb;
+  memset(&jb, 0, sizeof jb);
+  jb.heads = heads;
+  jb.T = T;
+  jb.D = D;
+  jb.q = q;
+  jb.k = k;
+  jb.v = v;
+  jb.keep = keep;
+  jb.z = z;
+  jb.o = o;
+  jb.lse = lse;
+  return run_djobs(jb, nthreads);
+}
+
+/* Backward with dropout: gradients of sum(dout * O) for the forward above. */
+int oracle_attn_bwd_dropout(long heads, long T, long D, const double* q, const double* k,
+                            const double* v, const double* dout, const uint8_t* keep,
+                            double z, double* dq, double* dk, double* dv, int nthreads) {
+  if (heads < 0 || T < 0 || D < 1 || !q || !k || !v || !dout || !keep || !dq || !dk || !dv)
+    return ORACLE_EINVAL;
+  if (heads == 0 || T == 0) return ORACLE_OK;
+  djob_t jb;
+  memset(&jb, 0, sizeof jb);
+  jb.backward = 1;
+  jb.heads = heads;
+  jb.T = T;
+  jb.D = D;
+  jb.q = q;
+  jb.k = k;
+  jb.v = v;
+  jb.dout = dout;
+  jb.keep = keep;
+  jb.z = z;
+  jb.dq = dq;
+  jb.dk = dk;
+  jb.dv = dv;
+  return run_djobs(jb, nthreads);
 }

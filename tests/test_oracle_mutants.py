@@ -37,6 +37,45 @@ MUTANTS = [
 ]
 
 
+# Planted mistakes in the dropout half of the oracle (generator, mask mapping,
+# threshold, forward and backward with a mask).
+DROPOUT_MUTANTS = [
+    ("philox_lo_words_swapped", "const uint32_t y1 = (uint32_t)p1;", "const uint32_t y1 = (uint32_t)p0;"),
+    ("philox_no_key_bump", "    k0 += W0;\n    k1 += W1;\n  }", "    k1 += W1;\n  }"),
+    ("philox_nine_rounds", "for (int r = 0; r < 10; ++r) {\n    const uint64_t p0",
+     "for (int r = 0; r < 9; ++r) {\n    const uint64_t p0"),
+    ("mask_counter_words_swapped", "{(uint32_t)(j / 8), (uint32_t)i, (uint32_t)bh[h], offset}",
+     "{(uint32_t)i, (uint32_t)(j / 8), (uint32_t)bh[h], offset}"),
+    ("mask_word_index", "out[(j % 8) / 2]", "out[(j % 4)]"),
+    ("mask_field", "(16 * (j % 2))", "(16 * ((j / 2) % 2))"),
+    ("threshold_truncated", "floor(p * 65536.0 + 0.5)", "floor(p * 65536.0)"),
+    ("keep_compare_strict", "u >= (uint32_t)thr ? 1 : 0", "u > (uint32_t)thr ? 1 : 0"),
+    ("fwd_scale_missing", "const double pd = M[i * T + j] ? z * p[j] : 0.0;\n      const double* vj",
+     "const double pd = M[i * T + j] ? p[j] : 0.0;\n      const double* vj"),
+    ("bwd_mask_ignored_in_dp", "dp[j] = M[i * T + j] ? z * dpd : 0.0;", "dp[j] = z * dpd;"),
+    ("bwd_dv_undropped", "const double pd = M[i * T + j] ? z * p[j] : 0.0;\n      double* dvj",
+     "const double pd = p[j];\n      double* dvj"),
+    ("bwd_rowdot_undropped", "rowdot += p[j] * dp[j];", "rowdot += p[j] * dpd;"),
+]
+
+
+def _dropout_pin_suite(rocrand_ref):
+    from tests import test_oracle_dropout as dp
+    suite = [
+        ("thresholds", dp.test_threshold_values),
+        ("statistics", dp.test_mask_statistics),
+        ("keep_all", dp.test_keep_all_equals_plain_oracle),
+        ("closed_forms", dp.test_closed_forms_all_dropped_and_diagonal_only),
+        ("fd", lambda: dp.test_finite_differences_with_mask((1, 1, 6, 3))),
+        ("brute", lambda: dp.test_brute_force_decimal_with_mask((1, 2, 5, 3))),
+    ]
+    if rocrand_ref is not None:
+        suite += [("rocrand_blocks", lambda: dp.test_philox_matches_rocrand(rocrand_ref)),
+                  ("rocrand_mask", lambda: dp.test_keep_mask_recomputed_from_rocrand(rocrand_ref)),
+                  ("boundary", lambda: dp.test_threshold_compare_boundary(rocrand_ref))]
+    return suite
+
+
 def _pin_suite():
     """(name, callable) for every pin in test_oracle_pins."""
     suite = []
@@ -74,7 +113,7 @@ def _swapped_oracle(lib_path):
 def _build_mutant(tmp_path, name, old, new):
     src = open(SRC).read()
     assert src.count(old) >= 1, f"mutation site for {name} not found"
-    mutated = src.replace(old, new)
+    mutated = src.replace(old, new, 1)  # the first site: the plain half precedes dropout
     c_path = tmp_path / f"{name}.c"
     c_path.write_text(mutated)
     so_path = tmp_path / f"lib{name}.so"
@@ -83,18 +122,37 @@ def _build_mutant(tmp_path, name, old, new):
     return str(so_path)
 
 
-def _failing_pins():
+def _failing_pins(suite=None):
     failed = []
-    for pin_name, fn in _pin_suite():
+    for pin_name, fn in (suite if suite is not None else _pin_suite()):
         try:
             fn()
-        except AssertionError:
+        except (AssertionError, ValueError):
             failed.append(pin_name)
     return failed
 
 
 def test_real_oracle_passes_every_pin():
     assert _failing_pins() == []
+
+
+@pytest.fixture(scope="module")
+def rocrand_ref(tmp_path_factory):
+    from tests import test_oracle_dropout as dp
+    return dp.build_rocrand_ref(tmp_path_factory.mktemp("rocrand_mut"))
+
+
+def test_real_oracle_passes_every_dropout_pin(rocrand_ref):
+    assert rocrand_ref is not None, "hipcc / rocRAND headers missing"
+    assert _failing_pins(_dropout_pin_suite(rocrand_ref)) == []
+
+
+@pytest.mark.parametrize("name,old,new", DROPOUT_MUTANTS, ids=[m[0] for m in DROPOUT_MUTANTS])
+def test_dropout_mutant_is_caught(tmp_path, rocrand_ref, name, old, new):
+    lib = _build_mutant(tmp_path, name, old, new)
+    with _swapped_oracle(lib):
+        failed = _failing_pins(_dropout_pin_suite(rocrand_ref))
+    assert failed, f"no pin caught the planted mistake {name}"
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
