@@ -7,6 +7,8 @@ two phases gpt_attn_bwd_prep (delta, dQ zero-fill) and gpt_attn_bwd_main
 ``--layout fused`` the same step runs through the strided entry points on the
 attention layer's own buffers: q, k, v read from one [B, T, 3C] projection
 output, dO from and O into [B, T, C], fp32 dQ, dK, dV into one [B, T, 3C].
+``--dropout P`` applies attention dropout at rate P in the forward and the
+backward (the keep mask regenerated in both); the FLOP count is unchanged.
 
 FLOPs are the causal algorithmic count: only the T(T+1)/2 unmasked (query,
 key) pairs per head, 4*D per pair forward (QK^T and PV) and 10*D per pair
@@ -102,6 +104,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-heads", type=int, default=64,
                     help="heads of the workload the oracle baseline runs")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="attention dropout rate (Philox keep mask, seed 1234, offset 0)")
     ap.add_argument("--layout", choices=("bhtd", "fused"), default="bhtd",
                     help="bhtd: contiguous [B, H, T, D] operands; fused: views of the "
                          "projection's [B, T, 3C] output and of [B, T, C] buffers")
@@ -164,6 +168,12 @@ def main(argv=None) -> int:
         dv = torch.empty_like(dq)
         fwd_call, prep_call, main_call = (gattn.gpt_attn_fwd, gattn.gpt_attn_bwd_prep,
                                           gattn.gpt_attn_bwd_main)
+    if args.dropout > 0.0:
+        import functools
+        drop = (args.dropout, 1234, 0)
+        fwd_call = functools.partial(gattn.gpt_attn_fwd_strided, dropout=drop)
+        prep_call = gattn.gpt_attn_bwd_prep_strided
+        main_call = functools.partial(gattn.gpt_attn_bwd_main_strided, dropout=drop)
     o_lo = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
     ws = torch.empty(gattn.gpt_attn_bwd_workspace_bytes("bf16", w.B, w.H, w.T, w.D) // 4,
@@ -219,7 +229,7 @@ def main(argv=None) -> int:
         return 1
 
     main_tflops = bwd_flop / (avg["main"] * 1e-3) / 1e12
-    traffic = None if fused else load_traffic(bwd_flop)
+    traffic = None if (fused or args.dropout > 0.0) else load_traffic(bwd_flop)
     out = {
         "metric": "causal attn fwd+bwd TFLOP/s and % bf16 MFMA peak, GPT-2 124M shape",
         "value": round(value, 2),
@@ -235,7 +245,8 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "D": w.D,
                    "causal": True, "scale": 1.0 / w.D ** 0.5, "seed": args.seed,
-                   "layout": "B,T,3C views" if fused else "BHTD", "pct_of_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2)},
+                   "layout": "B,T,3C views" if fused else "BHTD", "dropout": args.dropout,
+                   "pct_of_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2)},
         "fwd": {"ms": round(avg["fwd"], 5),
                 "tflops": round(fwd_flop / (avg["fwd"] * 1e-3) / 1e12, 2),
                 "pct_peak": round(100 * fwd_flop / (avg["fwd"] * 1e-3) / 1e12 /

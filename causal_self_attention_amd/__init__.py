@@ -19,7 +19,9 @@ The names mirror the C entry points:
 
 and the strided forms gpt_attn_fwd_strided, gpt_attn_bwd_strided,
 gpt_attn_bwd_prep_strided, gpt_attn_bwd_main_strided (same arguments; each
-tensor's own strides become its gpt_attn_layout), plus two allocating
+tensor's own strides become its gpt_attn_layout; the forward and backward
+ones take an optional ``dropout=(p, seed, offset)``), gpt_attn_dropout_mask
+(the keep mask the kernels derive, written out), plus two allocating
 conveniences, ``attention_forward`` and ``attention_backward``, and the view
 helpers ``split_qkv_heads`` / ``merged_heads_view`` for the fused [B, T, 3C]
 projection layout. Tensors are logically [B, H, T, D]: contiguous for the
@@ -40,7 +42,7 @@ __all__ = [
     "gpt_attn_status_string", "gpt_attn_abi_version", "gpt_attn_fwd_strided",
     "gpt_attn_bwd_strided", "gpt_attn_bwd_prep_strided", "gpt_attn_bwd_main_strided",
     "attention_forward", "attention_backward", "split_qkv_heads", "merged_heads_view",
-    "DTYPE_CODES", "GptAttnLayout",
+    "DTYPE_CODES", "GptAttnLayout", "GptAttnDropout", "gpt_attn_dropout_mask",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -54,10 +56,11 @@ DTYPE_CODES = {"f32": GPT_ATTN_F32, "bf16": GPT_ATTN_BF16}
 #: every symbol include/gpt_attn.h declares
 EXPORTED_SYMBOLS = ("gpt_attn_fwd", "gpt_attn_bwd", "gpt_attn_bwd_prep", "gpt_attn_bwd_main",
                     "gpt_attn_fwd_strided", "gpt_attn_bwd_strided", "gpt_attn_bwd_prep_strided",
-                    "gpt_attn_bwd_main_strided", "gpt_attn_bwd_workspace_bytes",
-                    "gpt_attn_status_string", "gpt_attn_abi_version")
+                    "gpt_attn_bwd_main_strided", "gpt_attn_dropout_mask",
+                    "gpt_attn_bwd_workspace_bytes", "gpt_attn_status_string",
+                    "gpt_attn_abi_version")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class GptAttnLayout(ctypes.Structure):
@@ -65,6 +68,24 @@ class GptAttnLayout(ctypes.Structure):
     logically [B, H, T, D] operand whose D elements are contiguous."""
     _fields_ = [("batch", ctypes.c_longlong), ("head", ctypes.c_longlong),
                 ("row", ctypes.c_longlong)]
+
+
+class GptAttnDropout(ctypes.Structure):
+    """struct gpt_attn_dropout: drop probability p (0 <= p < 1, rounded to a
+    multiple of 2^-16), 64-bit Philox seed and 32-bit stream offset."""
+    _fields_ = [("p", ctypes.c_double), ("seed", ctypes.c_ulonglong),
+                ("offset", ctypes.c_uint)]
+
+
+def _dropout_arg(dropout):
+    """None, a GptAttnDropout, or (p, seed[, offset]) -> pointer or None."""
+    if dropout is None:
+        return None
+    if not isinstance(dropout, GptAttnDropout):
+        p, seed, *rest = dropout
+        dropout = GptAttnDropout(float(p), int(seed) & (2**64 - 1),
+                                 int(rest[0] if rest else 0) & 0xFFFFFFFF)
+    return ctypes.byref(dropout)
 
 
 class GptAttnError(RuntimeError):
@@ -97,18 +118,21 @@ def load_library():
     lib.gpt_attn_bwd_main.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gpt_attn_bwd_main.restype = i
     lp = ctypes.POINTER(GptAttnLayout)
+    dp_ = ctypes.POINTER(GptAttnDropout)
     lib.gpt_attn_fwd_strided.argtypes = [i, i, i, i, i, vp, lp, vp, lp, vp, lp, vp, lp, vp, lp,
-                                         vp, vp]
+                                         vp, dp_, vp]
     lib.gpt_attn_fwd_strided.restype = i
     lib.gpt_attn_bwd_strided.argtypes = [i, i, i, i, i, vp, lp, vp, lp, vp, lp, vp, lp, vp, lp,
-                                         vp, lp, vp, vp, lp, vp, lp, vp, lp, vp, sz, vp]
+                                         vp, lp, vp, vp, lp, vp, lp, vp, lp, vp, sz, dp_, vp]
     lib.gpt_attn_bwd_strided.restype = i
     lib.gpt_attn_bwd_prep_strided.argtypes = [i, i, i, i, i, vp, lp, vp, lp, vp, lp, vp, lp, vp,
                                               sz, vp]
     lib.gpt_attn_bwd_prep_strided.restype = i
     lib.gpt_attn_bwd_main_strided.argtypes = [i, i, i, i, i, vp, lp, vp, lp, vp, lp, vp, lp, vp,
-                                              vp, lp, vp, lp, vp, lp, vp, sz, vp]
+                                              vp, lp, vp, lp, vp, lp, vp, sz, dp_, vp]
     lib.gpt_attn_bwd_main_strided.restype = i
+    lib.gpt_attn_dropout_mask.argtypes = [i, i, i, dp_, vp, vp]
+    lib.gpt_attn_dropout_mask.restype = i
     lib.gpt_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.gpt_attn_bwd_workspace_bytes.restype = sz
     lib.gpt_attn_status_string.argtypes = [i]
@@ -237,22 +261,24 @@ def gpt_attn_bwd_main(q, k, v, dout, lse, dq, dk, dv, workspace, stream=None) ->
 
 # ---- strided forms ------------------------------------------------------------
 
-def gpt_attn_fwd_strided(q, k, v, o, o_lo, lse, stream=None) -> None:
-    """gpt_attn_fwd on [B, H, T, D] views of any layout with unit D stride."""
+def gpt_attn_fwd_strided(q, k, v, o, o_lo, lse, stream=None, dropout=None) -> None:
+    """gpt_attn_fwd on [B, H, T, D] views of any layout with unit D stride;
+    ``dropout`` = None or (p, seed, offset)."""
     B, H, T, D = _bhtd(q)
     _same_shape(q, k, v, o, o_lo)
     args = []
     for t in (q, k, v, o, o_lo):
         args.extend(_sptr(t))
     st = load_library().gpt_attn_fwd_strided(_dtype_code(q), B, H, T, D, *args, _ptr(lse),
-                                             _stream(q.device, stream))
+                                             _dropout_arg(dropout), _stream(q.device, stream))
     if st != 0:
         raise GptAttnError("gpt_attn_fwd_strided", st)
 
 
 def gpt_attn_bwd_strided(q, k, v, o, o_lo, dout, lse, dq, dk, dv, workspace,
-                         stream=None) -> None:
-    """gpt_attn_bwd on [B, H, T, D] views of any layout with unit D stride."""
+                         stream=None, dropout=None) -> None:
+    """gpt_attn_bwd on [B, H, T, D] views of any layout with unit D stride;
+    ``dropout`` must be the forward's."""
     B, H, T, D = _bhtd(q)
     _same_shape(q, k, v, o, o_lo, dout, dq, dk, dv)
     args = []
@@ -262,7 +288,8 @@ def gpt_attn_bwd_strided(q, k, v, o, o_lo, dout, lse, dq, dk, dv, workspace,
     for t in (dq, dk, dv):
         args.extend(_sptr(t))
     st = load_library().gpt_attn_bwd_strided(_dtype_code(q), B, H, T, D, *args, _ptr(workspace),
-                                             _ws_bytes(workspace), _stream(q.device, stream))
+                                             _ws_bytes(workspace), _dropout_arg(dropout),
+                                             _stream(q.device, stream))
     if st != 0:
         raise GptAttnError("gpt_attn_bwd_strided", st)
 
@@ -281,7 +308,8 @@ def gpt_attn_bwd_prep_strided(o, o_lo, dout, dq, workspace, stream=None) -> None
         raise GptAttnError("gpt_attn_bwd_prep_strided", st)
 
 
-def gpt_attn_bwd_main_strided(q, k, v, dout, lse, dq, dk, dv, workspace, stream=None) -> None:
+def gpt_attn_bwd_main_strided(q, k, v, dout, lse, dq, dk, dv, workspace, stream=None,
+                              dropout=None) -> None:
     """gpt_attn_bwd_main on [B, H, T, D] views (unit D stride)."""
     B, H, T, D = _bhtd(q)
     _same_shape(q, k, v, dout, dq, dk, dv)
@@ -293,9 +321,22 @@ def gpt_attn_bwd_main_strided(q, k, v, dout, lse, dq, dk, dv, workspace, stream=
         args.extend(_sptr(t))
     st = load_library().gpt_attn_bwd_main_strided(_dtype_code(q), B, H, T, D, *args,
                                                   _ptr(workspace), _ws_bytes(workspace),
+                                                  _dropout_arg(dropout),
                                                   _stream(q.device, stream))
     if st != 0:
         raise GptAttnError("gpt_attn_bwd_main_strided", st)
+
+
+def gpt_attn_dropout_mask(B: int, H: int, T: int, dropout, mask, stream=None) -> None:
+    """Write the keep mask (uint8 [B, H, T, T], contiguous, 1 = visible and
+    kept) the attention kernels derive for ``dropout`` = (p, seed, offset)."""
+    import torch
+    if mask.dtype != torch.uint8 or tuple(mask.shape) != (B, H, T, T):
+        raise ValueError("mask must be uint8 of shape [B, H, T, T]")
+    st = load_library().gpt_attn_dropout_mask(B, H, T, _dropout_arg(dropout), _ptr(mask),
+                                              _stream(mask.device, stream))
+    if st != 0:
+        raise GptAttnError("gpt_attn_dropout_mask", st)
 
 
 # ---- views of the fused projection layout ---------------------------------------
@@ -320,11 +361,12 @@ def merged_heads_view(y, n_head: int):
     return y.view(B, T, n_head, C // n_head).transpose(1, 2)
 
 
-def attention_forward(q, k, v, stream=None, keep_o_lo: bool = True, out=None):
+def attention_forward(q, k, v, stream=None, keep_o_lo: bool = True, out=None, dropout=None):
     """Run the forward on [B, H, T, D] views (any layout with unit D stride).
     O goes to ``out`` (a view of that shape, e.g. merged_heads_view of a
     [B, T, C] buffer) or a new contiguous tensor; LSE (fp32) and, for bf16
-    with keep_o_lo, the low part o_lo are allocated. Returns (o, lse, o_lo)."""
+    with keep_o_lo, the low part o_lo are allocated. ``dropout`` = None or
+    (p, seed, offset) applies attention dropout. Returns (o, lse, o_lo)."""
     import torch
     for t in (k, v):
         if t.shape != q.shape or t.dtype != q.dtype:
@@ -334,16 +376,17 @@ def attention_forward(q, k, v, stream=None, keep_o_lo: bool = True, out=None):
     o_lo = (torch.empty(shape, dtype=q.dtype, device=q.device)
             if (keep_o_lo and q.dtype == torch.bfloat16) else None)
     lse = torch.empty(shape[:-1], dtype=torch.float32, device=q.device)
-    gpt_attn_fwd_strided(q, k, v, o, o_lo, lse, stream)
+    gpt_attn_fwd_strided(q, k, v, o, o_lo, lse, stream, dropout)
     return o, lse, o_lo
 
 
 def attention_backward(q, k, v, o, dout, lse, o_lo=None, stream=None, workspace=None,
-                       grads=None):
+                       grads=None, dropout=None):
     """Run the backward on [B, H, T, D] views (any layout with unit D stride).
     dQ, dK, dV (fp32) go to ``grads`` = (dq, dk, dv) views when given (e.g.
     split_qkv_heads of an fp32 [B, T, 3C] buffer), else to new tensors; the
-    workspace is allocated unless given. Returns (dq, dk, dv)."""
+    workspace is allocated unless given; ``dropout`` must be the forward's.
+    Returns (dq, dk, dv)."""
     import torch
     B, H, T, D = _bhtd(q)
     if grads is None:
@@ -355,5 +398,5 @@ def attention_backward(q, k, v, o, dout, lse, o_lo=None, stream=None, workspace=
     if workspace is None:
         nbytes = gpt_attn_bwd_workspace_bytes(_dtype_code(q), B, H, T, D)
         workspace = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device=q.device)
-    gpt_attn_bwd_strided(q, k, v, o, o_lo, dout, lse, dq, dk, dv, workspace, stream)
+    gpt_attn_bwd_strided(q, k, v, o, o_lo, dout, lse, dq, dk, dv, workspace, stream, dropout)
     return dq, dk, dv

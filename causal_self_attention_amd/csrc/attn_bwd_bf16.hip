@@ -31,6 +31,14 @@
 // three products with a rounded operand (dV += P^T dO, dK += dS^T Q,
 // dQ += dS K) use fp16 MFMA: P and dS are rounded to fp16 (11 significant
 // bits) and the bf16 Q, K, dO tiles convert to fp16 exactly.
+//
+// Attention dropout (a separate instantiation) regenerates the forward's
+// keep mask M: per 32x32 block each lane draws the Philox blocks of one query
+// and 16 keys, writes the 0 / 0xFFFF masks to a per-wave LDS tile, and reads
+// them back transposed (ds_read_b64_tr_b16) into its own register order (its
+// key, 8 consecutive queries). With z the survivor scale: dV accumulates
+// (M P)^T dO and is scaled by z at the end, and dS = P (z M dP - delta);
+// delta = rowsum(dO * O) holds with dropout too (O is the dropped output).
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -42,6 +50,7 @@ constexpr int kBQ = 64;       // queries per step
 constexpr int kThreads = 512;
 constexpr int kLoaders = 256; // threads of waves 4..7: they alone load Q/dO tiles
 constexpr int kRowQ = 72;     // padded row of a 64-wide 16-bit LDS tile (144 bytes)
+constexpr int kRowM = 40;     // row of a wave's 32 x 32 keep-mask tile (80 bytes)
 
 // Eight threads per (head, row): row r of the flattened [B*H, T] index space
 // is head r / T, position r % T.
@@ -128,11 +137,11 @@ __device__ __forceinline__ void bwd_store_tile(f16* sQ, f16* sdO, float* sL, flo
 // P = exp2(S log2(e)/8 - LSE log2(e)) and dS = P (dP - delta) for the 16
 // (query, key) pairs of one lane in one 32x32 block, as fp16. Register
 // 8c + t of half hf is query q0 + 16c + 8hf + t; the lane's key is key0 + l32.
-template <int KIND>
+template <int KIND, bool DROP>
 __device__ __forceinline__ void bwd_p_ds(const f32x16& s, const f32x16& dp, const float* cL,
                                          const float* cD, int qoff0, int q0, int key0, int T,
-                                         int l32, int hf, float scale_log2, f16x8 (&pf)[2],
-                                         f16x8 (&dsf)[2]) {
+                                         int l32, int hf, float scale_log2, const f16x8 (&mk)[2],
+                                         float zscale, f16x8 (&pf)[2], f16x8 (&dsf)[2]) {
   const int key = key0 + l32;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
@@ -155,15 +164,29 @@ __device__ __forceinline__ void bwd_p_ds(const f32x16& s, const f32x16& dp, cons
         pv = (key > qi || key >= T || qi >= T) ? 0.f : pv;
       }
       p[t] = pv;
-      ds[t] = pv * (dp[8 * c + t] - del);
+      if (DROP) {
+        const uint32_t w = (uint32_t)__builtin_bit_cast(i32x4, mk[c])[t >> 1];
+        const bool kept = (w >> (16 * (t & 1))) & 1u;
+        ds[t] = pv * ((kept ? dp[8 * c + t] * zscale : 0.f) - del);
+      } else {
+        ds[t] = pv * (dp[8 * c + t] - del);
+      }
     }
     pf[c] = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+    if (DROP) {  // dV takes the dropped weights M P
+      i32x4 bits = __builtin_bit_cast(i32x4, pf[c]);
+      const i32x4 mbits = __builtin_bit_cast(i32x4, mk[c]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) bits[w] &= mbits[w];
+      pf[c] = __builtin_bit_cast(f16x8, bits);
+    }
     dsf[c] = pack_f16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
   }
 }
 
 // Row strides inside one head are 32-bit (the host checks T * stride < 2^31);
 // head offsets are 64-bit.
+template <bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(const BwdArgs a,
                                                                          int n_ktiles, float scale,
                                                                          float scale_log2) {
@@ -175,6 +198,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(const B
   __shared__ __attribute__((aligned(16))) float sPart[4][16][64];       // dQ half sums
   __shared__ __attribute__((aligned(16))) float sL[2][kBQ];             // LSE * log2(e)
   __shared__ __attribute__((aligned(16))) float sD[2][kBQ];             // delta
+  __shared__ __attribute__((aligned(16))) uint16_t sMask[DROP ? 8 : 1][DROP ? 32 * kRowM : 8];
 
   const int T = a.T;
   const TileMap tm = map_tile_xcd(blockIdx.x, a.n_heads, n_ktiles, false);
@@ -256,6 +280,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(const B
       if (kind == kEmpty) {
         pf[0] = pf[1] = dsf[0] = dsf[1] = zero_f16x8();
       } else {
+        f16x8 mk[2];
+        if (DROP) {
+          // Lane L draws query qb0 + L/2, keys kw0 + 16 (L%2) .. +15 (two
+          // Philox blocks) into row L/2 of the wave's tile [query][key].
+          uint16_t* tile = sMask[wave];
+          uint32_t m0[4], m1[4];
+          const uint32_t grp = (uint32_t)(kw0 >> 3) + 2u * (uint32_t)(lane & 1);
+          keep_mask8(a.drop, (uint32_t)tm.head, (uint32_t)(qb0 + (lane >> 1)), grp, m0);
+          keep_mask8(a.drop, (uint32_t)tm.head, (uint32_t)(qb0 + (lane >> 1)), grp + 1, m1);
+          i32x4* dst = reinterpret_cast<i32x4*>(tile + (lane >> 1) * kRowM + 16 * (lane & 1));
+          dst[0] = i32x4{(int)m0[0], (int)m0[1], (int)m0[2], (int)m0[3]};
+          dst[1] = i32x4{(int)m1[0], (int)m1[1], (int)m1[2], (int)m1[3]};
+          __builtin_amdgcn_wave_barrier();
+        }
         f32x16 s, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -269,12 +307,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(const B
           dp = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cdO[arow + kk * 16]), vf[kk],
                                 dp);
         }
+        if (DROP) {
+          // Lane (key l32, half hf): queries 16c + 8hf .. +7 of its key.
+          const f16* tile = reinterpret_cast<const f16*>(sMask[wave]);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) mk[c] = lds_operand_tr(tile, kRowM, 16 * c, 0, lane);
+          __builtin_amdgcn_wave_barrier();
+        } else {
+          mk[0] = mk[1] = zero_f16x8();
+        }
+        const float zs = DROP ? a.drop.scale : 1.f;
         if (kind == kFull)
-          bwd_p_ds<kFull>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, scale_log2, pf, dsf);
+          bwd_p_ds<kFull, DROP>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, scale_log2, mk, zs,
+                                pf, dsf);
         else if (kind == kDiag)
-          bwd_p_ds<kDiag>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, scale_log2, pf, dsf);
+          bwd_p_ds<kDiag, DROP>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, scale_log2, mk, zs,
+                                pf, dsf);
         else
-          bwd_p_ds<kGeneral>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, scale_log2, pf, dsf);
+          bwd_p_ds<kGeneral, DROP>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, scale_log2, mk,
+                                   zs, pf, dsf);
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -352,8 +403,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(const B
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = db2 * 32 + 8 * g + 4 * hf;
-        f32x4 x = {dvacc[db2][4 * g], dvacc[db2][4 * g + 1], dvacc[db2][4 * g + 2],
-                   dvacc[db2][4 * g + 3]};
+        const float zs = DROP ? a.drop.scale : 1.f;
+        f32x4 x = {dvacc[db2][4 * g] * zs, dvacc[db2][4 * g + 1] * zs, dvacc[db2][4 * g + 2] * zs,
+                   dvacc[db2][4 * g + 3] * zs};
         f32x4 y = {dkacc[db2][4 * g] * scale, dkacc[db2][4 * g + 1] * scale,
                    dkacc[db2][4 * g + 2] * scale, dkacc[db2][4 * g + 3] * scale};
         *reinterpret_cast<f32x4*>(dvr + d) = x;
@@ -374,8 +426,13 @@ hipError_t launch_bwd_prep_bf16(const BwdArgs& a, hipStream_t stream) {
 hipError_t launch_bwd_main_bf16(const BwdArgs& a, hipStream_t stream) {
   const int n_ktiles = (a.T + kBK - 1) / kBK;
   const float scale = 0.125f;  // 1/sqrt(64)
-  hipLaunchKernelGGL(attn_bwd_main_bf16_kernel, dim3(tiled_grid(a.n_heads, n_ktiles)),
-                     dim3(kThreads), 0, stream, a, n_ktiles, scale, scale * kLog2e);
+  const dim3 grid(tiled_grid(a.n_heads, n_ktiles));
+  if (a.drop.thr != 0)
+    hipLaunchKernelGGL(attn_bwd_main_bf16_kernel<true>, grid, dim3(kThreads), 0, stream, a,
+                       n_ktiles, scale, scale * kLog2e);
+  else
+    hipLaunchKernelGGL(attn_bwd_main_bf16_kernel<false>, grid, dim3(kThreads), 0, stream, a,
+                       n_ktiles, scale, scale * kLog2e);
   return hipGetLastError();
 }
 

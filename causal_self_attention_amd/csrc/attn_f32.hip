@@ -16,6 +16,8 @@
 // looping over the key tiles up to the query. Nothing is accumulated with
 // atomics, so every output is bitwise reproducible. Operands are addressed
 // through per-tensor element strides (D contiguous), like the bf16 path.
+// Attention dropout regenerates the same Philox keep mask as the bf16 path
+// (one block per query and 8 keys) wherever a (query, key) weight is used.
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -23,6 +25,11 @@ namespace gpt_attn {
 namespace {
 
 constexpr int kD = kHeadDim;
+
+// Keep bit of key 8*group + t from keep_mask8's words.
+__device__ __forceinline__ bool kept_bit(const uint32_t (&m)[4], int t) {
+  return (m[t >> 1] >> (16 * (t & 1))) & 1u;
+}
 
 __device__ __forceinline__ const float* fptr(const void* base, const Layout& L, int hd, int H) {
   return static_cast<const float*>(base) + head_base(L, hd, H);
@@ -44,6 +51,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const FwdArgs a, int n
   const float* kh = fptr(a.k, a.lk, head, a.H);
   const float* vh = fptr(a.v, a.lv, head, a.H);
   const long long ldq = a.lq.t, ldk = a.lk.t, ldv = a.lv.t;
+  const bool drop = a.drop.thr != 0;
 
   float qr[kD], acc[kD];
 #pragma unroll
@@ -78,17 +86,20 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const FwdArgs a, int n
     l *= alpha;
 #pragma unroll
     for (int d = 0; d < kD; ++d) acc[d] *= alpha;
+    uint32_t km[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
 #pragma unroll
     for (int j = 0; j < 64; ++j) {
+      if (drop && (j & 7) == 0) keep_mask8(a.drop, head, i, (uint32_t)(k0 + j) >> 3, km);
       const float p = expf(sc[j] - m_new);
       l += p;
+      const float pd = kept_bit(km, j & 7) ? p : 0.f;
 #pragma unroll
-      for (int d = 0; d < kD; ++d) acc[d] = fmaf(p, Vs[j * kD + d], acc[d]);
+      for (int d = 0; d < kD; ++d) acc[d] = fmaf(pd, Vs[j * kD + d], acc[d]);
     }
     m = m_new;
   }
   if (i < T) {
-    const float inv = 1.f / l;
+    const float inv = (drop ? a.drop.scale : 1.f) / l;
     float* orow = fptr_w(a.o, a.lo, head, a.H) + i * a.lo.t;
 #pragma unroll
     for (int d = 0; d < kD; ++d) orow[d] = acc[d] * inv;
@@ -133,6 +144,8 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(const BwdArgs a, 
   const float* vh = fptr(a.v, a.lv, head, a.H);
   const float* doh = fptr(a.dout, a.ldo, head, a.H);
   const size_t roff = (size_t)head * T;
+  const bool drop = a.drop.thr != 0;
+  const float zs = drop ? a.drop.scale : 1.f;
 
   float kr[32], vr[32], dka[32], dva[32];
 #pragma unroll
@@ -167,11 +180,18 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(const BwdArgs a, 
       s += __shfl_xor(s, 1, 64);
       dp += __shfl_xor(dp, 1, 64);
       if (i < T && j < T && j <= i) {
+        bool kept = true;
+        if (drop) {
+          uint32_t km[4];
+          keep_mask8(a.drop, head, i, (uint32_t)j >> 3, km);
+          kept = kept_bit(km, j & 7);
+        }
         const float p = expf(s * scale - lses[ii]);
-        const float ds = p * (dp - dels[ii]);
+        const float ds = p * ((kept ? dp * zs : 0.f) - dels[ii]);
+        const float pd = kept ? p : 0.f;
 #pragma unroll
         for (int d = 0; d < 32; ++d) {
-          dva[d] = fmaf(p, dOs[ii * kD + half * 32 + d], dva[d]);
+          dva[d] = fmaf(pd, dOs[ii * kD + half * 32 + d], dva[d]);
           dka[d] = fmaf(ds, Qs[ii * kD + half * 32 + d], dka[d]);
         }
       }
@@ -183,7 +203,7 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(const BwdArgs a, 
 #pragma unroll
     for (int d = 0; d < 32; ++d) {
       dkr[d] = dka[d] * scale;
-      dvr[d] = dva[d];
+      dvr[d] = dva[d] * zs;
     }
   }
 }
@@ -212,6 +232,8 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(const BwdArgs a, in
     dor[d] = i < T ? doh[i * a.ldo.t + half * 32 + d] : 0.f;
     dqa[d] = 0.f;
   }
+  const bool drop = a.drop.thr != 0;
+  const float zs = drop ? a.drop.scale : 1.f;
   const float lse_i = i < T ? a.lse[roff + i] : 0.f;
   const float del_i = i < T ? a.delta[roff + i] : 0.f;
   const int kv_end = min(T, q0 + 32);
@@ -224,8 +246,10 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(const BwdArgs a, in
       Vs[e] = ok ? vh[(k0 + r) * a.lv.t + d] : 0.f;
     }
     __syncthreads();
+    uint32_t km[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
     for (int jj = 0; jj < 32; ++jj) {
       const int j = k0 + jj;
+      if (drop && (jj & 7) == 0) keep_mask8(a.drop, head, i, (uint32_t)j >> 3, km);
       float s = 0.f, dp = 0.f;
 #pragma unroll
       for (int d = 0; d < 32; ++d) {
@@ -236,7 +260,7 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(const BwdArgs a, in
       dp += __shfl_xor(dp, 1, 64);
       if (i < T && j < T && j <= i) {
         const float p = expf(s * scale - lse_i);
-        const float ds = p * (dp - del_i);
+        const float ds = p * ((kept_bit(km, jj & 7) ? dp * zs : 0.f) - del_i);
 #pragma unroll
         for (int d = 0; d < 32; ++d) dqa[d] = fmaf(ds, Ks[jj * kD + half * 32 + d], dqa[d]);
       }
@@ -249,7 +273,35 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(const BwdArgs a, in
   }
 }
 
+// Keep mask [n_heads, T, T]: one thread per (head, query, 8-key group).
+__global__ __launch_bounds__(256) void dropout_mask_kernel(const Dropout d, int T, int n_groups,
+                                                           long long n_items, uint8_t* mask) {
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= n_items) return;
+  const int g = (int)(gid % n_groups);
+  const long long row = gid / n_groups;  // head * T + query
+  const int i = (int)(row % T);
+  const int head = (int)(row / T);
+  uint32_t km[4];
+  keep_mask8(d, (uint32_t)head, (uint32_t)i, (uint32_t)g, km);
+  uint8_t* out = mask + row * T;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int j = 8 * g + t;
+    if (j < T) out[j] = (j <= i && kept_bit(km, t)) ? 1 : 0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_dropout_mask(const Dropout& d, int n_heads, int T, uint8_t* mask,
+                               hipStream_t stream) {
+  const int n_groups = (T + 7) / 8;
+  const long long n_items = (long long)n_heads * T * n_groups;
+  hipLaunchKernelGGL(dropout_mask_kernel, dim3((unsigned)((n_items + 255) / 256)), dim3(256), 0,
+                     stream, d, T, n_groups, n_items, mask);
+  return hipGetLastError();
+}
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
   const int n_tiles = (a.T + 63) / 64;

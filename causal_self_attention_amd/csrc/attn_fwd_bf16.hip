@@ -26,6 +26,12 @@
 //
 // Outputs: O rounded to bf16, optionally the bf16 rounding of what that
 // dropped (o_lo = bf16(O - o)), and LSE in fp32.
+//
+// Attention dropout (a separate instantiation): the row sum keeps every
+// weight (the softmax comes first), the fp16 weights entering P V are ANDed
+// with the regenerated keep mask (one Philox block per lane per 8 keys, in
+// exactly the lane's register order), and the survivor scale is folded into
+// the final 1/l.
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -82,10 +88,11 @@ struct FwdState {
 // precedes every query of the wave and lies below T (no compares at all).
 // MASKED = true: keys after the lane's query or at/after T get -inf through
 // branch-free selects against one per-lane limit.
-template <bool MASKED>
+template <bool MASKED, bool DROP>
 __device__ __forceinline__ void fwd_tile(const bf16* cK, const f16* cV, const bf16x8 (&qf)[4],
                                          int k0, int my_q, int T, int l32, int hf, int lane,
-                                         float scale_log2, FwdState& st) {
+                                         float scale_log2, const Dropout& drop, int head,
+                                         FwdState& st) {
   // Scores S^T = K Q^T for the two 32-key halves; register v = 8c + t of half
   // hf holds key k0 + 32kb + 16c + 8hf + t (perm32 order) for query my_q.
   f32x16 s[2];
@@ -139,12 +146,23 @@ __device__ __forceinline__ void fwd_tile(const bf16* cK, const f16* cV, const bf
       const f16x8 pb = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
       // The row sum uses the fp16 weights the MFMA multiplies by.
       st.l_run = sum_f16x8(pb, st.l_run);
+      f16x8 pw = pb;
+      if (DROP) {
+        // Keys k0 + 32kb + 16c + 8hf .. +7 of query my_q: one Philox block.
+        uint32_t m[4];
+        keep_mask8(drop, (uint32_t)head, (uint32_t)my_q, (uint32_t)((k0 + 32 * kb + 16 * c) >> 3) + hf,
+                   m);
+        i32x4 bits = __builtin_bit_cast(i32x4, pb);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) bits[w] &= (int)m[w];
+        pw = __builtin_bit_cast(f16x8, bits);
+      }
       const int ks = 2 * kb + c;  // 16-key step inside the tile
       // O^T += V^T P^T: the A operand (lane: dim, 8 consecutive keys) is a
       // transposing read of the row-major V tile.
 #pragma unroll
       for (int db = 0; db < 2; ++db)
-        st.oacc[db] = mfma32x32x16_f16(lds_operand_tr(cV, kRow, ks * 16, db * 32, lane), pb,
+        st.oacc[db] = mfma32x32x16_f16(lds_operand_tr(cV, kRow, ks * 16, db * 32, lane), pw,
                                        st.oacc[db]);
     }
   }
@@ -152,6 +170,7 @@ __device__ __forceinline__ void fwd_tile(const bf16* cK, const f16* cV, const bf
 
 // Row strides inside one head are 32-bit (the host checks T * stride < 2^31);
 // head offsets are 64-bit.
+template <bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdArgs a, int n_qtiles,
                                                                     float scale_log2) {
   // LDS: two K/V tile buffers (K bf16, V fp16, both [key][d]). Buffer 1 also
@@ -230,7 +249,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdArg
     const int k0 = kt * kBN;
     const bool has_next = kt + 1 < n_kt;
     if (has_next) fwd_load_tile(kh, ldk, vh, ldv, k0 + kBN, T, tid, nxt);
-    fwd_tile<false>(Kbuf(buf), Vbuf(buf), qf, k0, my_q, T, l32, hf, lane, scale_log2, st);
+    fwd_tile<false, DROP>(Kbuf(buf), Vbuf(buf), qf, k0, my_q, T, l32, hf, lane, scale_log2,
+                          a.drop, tm.head, st);
     if (has_next) fwd_store_tile(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid);
     __syncthreads();
   }
@@ -238,14 +258,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdArg
     const int k0 = kt * kBN;
     const bool has_next = kt + 1 < n_kt;
     if (has_next) fwd_load_tile(kh, ldk, vh, ldv, k0 + kBN, T, tid, nxt);
-    fwd_tile<true>(Kbuf(buf), Vbuf(buf), qf, k0, my_q, T, l32, hf, lane, scale_log2, st);
+    fwd_tile<true, DROP>(Kbuf(buf), Vbuf(buf), qf, k0, my_q, T, l32, hf, lane, scale_log2,
+                         a.drop, tm.head, st);
     if (has_next) fwd_store_tile(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid);
     __syncthreads();
   }
 
   // Epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2.
   const float l_tot = st.l_run + wave_xor32(st.l_run);
-  const float inv = 1.f / l_tot;
+  const float inv = (DROP ? a.drop.scale : 1.f) / l_tot;
   if (my_q < T) {
     bf16* orow = static_cast<bf16*>(a.o) + head_base(a.lo, tm.head, a.H) + my_q * (int)a.lo.t;
     bf16* lrow = a.o_lo ? static_cast<bf16*>(a.o_lo) + head_base(a.llo, tm.head, a.H) +
@@ -275,8 +296,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(const FwdArg
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.T + kBM - 1) / kBM;
   const float scale_log2 = 0.125f * kLog2e;  // 1/sqrt(64) * log2(e)
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(tiled_grid(a.n_heads, n_qtiles)), dim3(kThreads),
-                     0, stream, a, n_qtiles, scale_log2);
+  const dim3 grid(tiled_grid(a.n_heads, n_qtiles));
+  if (a.drop.thr != 0)
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, grid, dim3(kThreads), 0, stream, a, n_qtiles,
+                       scale_log2);
+  else
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, grid, dim3(kThreads), 0, stream, a, n_qtiles,
+                       scale_log2);
   return hipGetLastError();
 }
 

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "attn_dropout.h"
+
 namespace gpt_attn {
 
 // Work-item placement shared by the tiled kernels. Workgroups are handed to
@@ -64,6 +66,7 @@ struct FwdArgs {
   float* lse;
   Layout lq, lk, lv, lo, llo;
   int n_heads, H, T;
+  Dropout drop;  // drop.thr == 0: no dropout
 };
 
 struct BwdArgs {
@@ -80,7 +83,12 @@ struct BwdArgs {
   float* dv;
   Layout lq, lk, lv, lo, llo, ldo, ldq, ldk, ldv;
   int n_heads, H, T;
+  Dropout drop;  // drop.thr == 0: no dropout
 };
+
+// Keep mask [n_heads, T, T] (uint8, 1 = kept; 0 above the diagonal).
+hipError_t launch_dropout_mask(const Dropout& d, int n_heads, int T, uint8_t* mask,
+                               hipStream_t stream);
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_prep_bf16(const BwdArgs& a, hipStream_t stream);

@@ -1,6 +1,7 @@
 // The C ABI declared in include/gpt_attn.h: argument validation, dispatch
 // by dtype, and launch-error reporting. Validation completes before any HIP
 // call, so a rejected call touches neither the device nor the HIP runtime.
+#include <math.h>
 #include <stdint.h>
 
 #include "attn_launch.h"
@@ -101,6 +102,21 @@ int check_layout(const Layout& L, const Shape& s, long long esize, bool output) 
 
 int launch_status(hipError_t e) { return e == hipSuccess ? GPT_ATTN_OK : GPT_ATTN_E_HIP; }
 
+// Dropout descriptor -> kernel parameters (thr = 0 when d is NULL or p = 0).
+int resolve_dropout(const gpt_attn_dropout* d, gpt_attn::Dropout* out) {
+  *out = gpt_attn::Dropout{0u, 1.f, 0u, 0u, 0u};
+  if (!d) return GPT_ATTN_OK;
+  if (!(d->p >= 0.0 && d->p < 1.0)) return GPT_ATTN_E_INVAL;
+  const double thr = floor(d->p * 65536.0 + 0.5);
+  if (thr >= 65536.0) return GPT_ATTN_E_INVAL;
+  out->thr = (uint32_t)thr;
+  out->scale = (float)(65536.0 / (65536.0 - thr));
+  out->key0 = (uint32_t)(d->seed & 0xFFFFFFFFull);
+  out->key1 = (uint32_t)(d->seed >> 32);
+  out->offset = d->offset;
+  return GPT_ATTN_OK;
+}
+
 #define GA_TRY(expr)                       \
   do {                                     \
     const int st_ = (expr);                \
@@ -121,7 +137,7 @@ int bwd_args(const Shape& s, int which, const void* q, const gpt_attn_layout* lq
              const void* dout, const gpt_attn_layout* ldo, const float* lse, float* dq,
              const gpt_attn_layout* ldq, float* dk, const gpt_attn_layout* ldk, float* dv,
              const gpt_attn_layout* ldv, const void* workspace, size_t workspace_bytes,
-             gpt_attn::BwdArgs* a) {
+             const gpt_attn_dropout* dropout, gpt_attn::BwdArgs* a) {
   const bool prep = which & 1, main = which & 2;
   const bool bf16 = s.dtype == GPT_ATTN_BF16;
   if (!dout) return GPT_ATTN_E_INVAL;
@@ -166,6 +182,7 @@ int bwd_args(const Shape& s, int which, const void* q, const gpt_attn_layout* lq
     GA_TRY(check_layout(a->ldk, s, 4, true));
     GA_TRY(check_layout(a->ldv, s, 4, true));
   }
+  GA_TRY(resolve_dropout(main ? dropout : nullptr, &a->drop));
   GA_TRY(check_workspace(workspace, workspace_bytes, s));
   a->n_heads = s.B * s.H;
   a->H = s.H;
@@ -215,7 +232,7 @@ int gpt_attn_fwd_strided(int dtype, int B, int H, int T, int D, const void* q,
                          const gpt_attn_layout* lq, const void* k, const gpt_attn_layout* lk,
                          const void* v, const gpt_attn_layout* lv, void* o,
                          const gpt_attn_layout* lo, void* o_lo, const gpt_attn_layout* llo,
-                         float* lse, void* stream) {
+                         float* lse, const gpt_attn_dropout* dropout, void* stream) {
   Shape s;
   GA_TRY(check_shape(dtype, B, H, T, D, &s));
   if (s.rows == 0) return GPT_ATTN_OK;
@@ -241,6 +258,7 @@ int gpt_attn_fwd_strided(int dtype, int B, int H, int T, int D, const void* q,
   GA_TRY(check_layout(a.lv, s, s.esize, false));
   GA_TRY(check_layout(a.lo, s, s.esize, true));
   if (o_lo) GA_TRY(check_layout(a.llo, s, 2, true));
+  GA_TRY(resolve_dropout(dropout, &a.drop));
   a.n_heads = B * H;
   a.H = H;
   a.T = T;
@@ -252,7 +270,7 @@ int gpt_attn_fwd_strided(int dtype, int B, int H, int T, int D, const void* q,
 int gpt_attn_fwd(int dtype, int B, int H, int T, int D, const void* q, const void* k,
                  const void* v, void* o, void* o_lo, float* lse, void* stream) {
   return gpt_attn_fwd_strided(dtype, B, H, T, D, q, nullptr, k, nullptr, v, nullptr, o, nullptr,
-                              o_lo, nullptr, lse, stream);
+                              o_lo, nullptr, lse, nullptr, stream);
 }
 
 size_t gpt_attn_bwd_workspace_bytes(int dtype, int B, int H, int T, int D) {
@@ -272,7 +290,7 @@ int gpt_attn_bwd_prep_strided(int dtype, int B, int H, int T, int D, const void*
   gpt_attn::BwdArgs a;
   GA_TRY(bwd_args(s, 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, o, lo, o_lo, llo,
                   dout, ldo, nullptr, dq, ldq, nullptr, nullptr, nullptr, nullptr, workspace,
-                  workspace_bytes, &a));
+                  workspace_bytes, nullptr, &a));
   return run_prep(s, a, static_cast<hipStream_t>(stream));
 }
 
@@ -282,13 +300,14 @@ int gpt_attn_bwd_main_strided(int dtype, int B, int H, int T, int D, const void*
                               const gpt_attn_layout* ldo, const float* lse, float* dq,
                               const gpt_attn_layout* ldq, float* dk, const gpt_attn_layout* ldk,
                               float* dv, const gpt_attn_layout* ldv, const void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              size_t workspace_bytes, const gpt_attn_dropout* dropout,
+                              void* stream) {
   Shape s;
   GA_TRY(check_shape(dtype, B, H, T, D, &s));
   if (s.rows == 0) return GPT_ATTN_OK;
   gpt_attn::BwdArgs a;
   GA_TRY(bwd_args(s, 2, q, lq, k, lk, v, lv, nullptr, nullptr, nullptr, nullptr, dout, ldo, lse,
-                  dq, ldq, dk, ldk, dv, ldv, workspace, workspace_bytes, &a));
+                  dq, ldq, dk, ldk, dv, ldv, workspace, workspace_bytes, dropout, &a));
   return run_main(s, a, static_cast<hipStream_t>(stream));
 }
 
@@ -299,14 +318,15 @@ int gpt_attn_bwd_strided(int dtype, int B, int H, int T, int D, const void* q,
                          const void* dout, const gpt_attn_layout* ldo, const float* lse,
                          float* dq, const gpt_attn_layout* ldq, float* dk,
                          const gpt_attn_layout* ldk, float* dv, const gpt_attn_layout* ldv,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         void* workspace, size_t workspace_bytes,
+                         const gpt_attn_dropout* dropout, void* stream) {
   Shape s;
   GA_TRY(check_shape(dtype, B, H, T, D, &s));
   if (s.rows == 0) return GPT_ATTN_OK;
   // Validate everything both phases need before enqueuing either.
   gpt_attn::BwdArgs a;
   GA_TRY(bwd_args(s, 3, q, lq, k, lk, v, lv, o, lo, o_lo, llo, dout, ldo, lse, dq, ldq, dk, ldk,
-                  dv, ldv, workspace, workspace_bytes, &a));
+                  dv, ldv, workspace, workspace_bytes, dropout, &a));
   hipStream_t st = static_cast<hipStream_t>(stream);
   GA_TRY(run_prep(s, a, st));
   return run_main(s, a, st);
@@ -324,7 +344,7 @@ int gpt_attn_bwd_main(int dtype, int B, int H, int T, int D, const void* q, cons
                       float* dv, const void* workspace, size_t workspace_bytes, void* stream) {
   return gpt_attn_bwd_main_strided(dtype, B, H, T, D, q, nullptr, k, nullptr, v, nullptr, dout,
                                    nullptr, lse, dq, nullptr, dk, nullptr, dv, nullptr, workspace,
-                                   workspace_bytes, stream);
+                                   workspace_bytes, nullptr, stream);
 }
 
 int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const void* k,
@@ -333,7 +353,21 @@ int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const voi
                  size_t workspace_bytes, void* stream) {
   return gpt_attn_bwd_strided(dtype, B, H, T, D, q, nullptr, k, nullptr, v, nullptr, o, nullptr,
                               o_lo, nullptr, dout, nullptr, lse, dq, nullptr, dk, nullptr, dv,
-                              nullptr, workspace, workspace_bytes, stream);
+                              nullptr, workspace, workspace_bytes, nullptr, stream);
+}
+
+int gpt_attn_dropout_mask(int B, int H, int T, const gpt_attn_dropout* dropout,
+                          unsigned char* mask, void* stream) {
+  if (B < 0 || H < 0 || T < 0 || !dropout) return GPT_ATTN_E_INVAL;
+  const long long heads = (long long)B * H;
+  const long long bytes = heads * (long long)T * (long long)T;
+  if (heads * (long long)T >= (1LL << 31) || bytes >= (1LL << 40)) return GPT_ATTN_E_INVAL;
+  gpt_attn::Dropout d;
+  GA_TRY(resolve_dropout(dropout, &d));
+  if (bytes == 0) return GPT_ATTN_OK;
+  if (!mask) return GPT_ATTN_E_INVAL;
+  return launch_status(
+      gpt_attn::launch_dropout_mask(d, (int)heads, T, mask, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -22,7 +22,8 @@
  *     into a [B, T, C] buffer. Per-row statistics (lse, and the delta vector
  *     in the workspace) are always contiguous [B, H, T] fp32.
  *   - Scale: always 1/sqrt(D). Causal masking is always on: key j is visible
- *     to query i iff j <= i. There is no mask, scale or dropout argument.
+ *     to query i iff j <= i. There is no mask or scale argument; attention
+ *     dropout is an optional gpt_attn_dropout on the strided calls.
  *   - Pointers are DEVICE pointers (hipMalloc or torch CUDA tensors) and must
  *     be 16-byte aligned. The caller owns every buffer; the library allocates
  *     nothing and keeps no state between calls. Outputs must not alias
@@ -49,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GPT_ATTN_ABI_VERSION 2
+#define GPT_ATTN_ABI_VERSION 3
 
 /* Status codes returned by every int-returning entry point. */
 enum gpt_attn_status {
@@ -95,6 +96,30 @@ typedef struct gpt_attn_layout {
   long long head;
   long long row;
 } gpt_attn_layout;
+
+/*
+ * Attention dropout. In training nanoGPT passes its dropout rate to the
+ * fused attention call (page "nanoGPT: a real GPT in two 300-line files",
+ * section 2 "How the code works"): each attention weight P_ij is zeroed with
+ * probability p after the softmax and the survivors are scaled by 1/(1-p),
+ * O = (z M o P) V with keep mask M. The mask is never stored: the forward,
+ * the backward and gpt_attn_dropout_mask all derive it from the
+ * counter-based generator Philox4x32-10 (Salmon et al., "Parallel random
+ * numbers: as easy as 1, 2, 3", SC'11) with
+ *   key     = (seed & 0xFFFFFFFF, seed >> 32)
+ *   counter = (j / 8, i, b*H + h, offset)        for query i, key j
+ *   u_ij    = 16-bit field (j % 2) of output word (j % 8) / 2
+ *   M_ij    = [u_ij >= thr],  thr = round(p * 65536),  z = 65536 / (65536 - thr)
+ * so the drop probability is p rounded to a multiple of 2^-16. A backward
+ * must get the same descriptor as its forward. LSE is unaffected by dropout.
+ * p must satisfy 0 <= p < 1 with thr < 65536 (GPT_ATTN_E_INVAL otherwise);
+ * p = 0 (or a NULL descriptor) means no dropout.
+ */
+typedef struct gpt_attn_dropout {
+  double p;
+  unsigned long long seed;
+  unsigned int offset;
+} gpt_attn_dropout;
 
 /* Element type of q, k, v, o and dout. lse, dq, dk, dv are always fp32. */
 enum gpt_attn_dtype {
@@ -184,15 +209,18 @@ int gpt_attn_bwd_main(int dtype, int B, int H, int T, int D, const void* q, cons
  * Strided forms of the four calls above: each operand pointer is followed by
  * its layout (NULL = contiguous [B,H,T,D]). Operand meanings, dtypes,
  * workspace and errors are those of the plain entry points, which are these
- * calls with every layout NULL. lse and the workspace's delta stay
- * contiguous [B,H,T]. gpt_attn_bwd_main_strided expects dq in the layout the
- * preceding gpt_attn_bwd_prep_strided zero-filled.
+ * calls with every layout NULL and no dropout. lse and the workspace's delta
+ * stay contiguous [B,H,T]. gpt_attn_bwd_main_strided expects dq in the
+ * layout the preceding gpt_attn_bwd_prep_strided zero-filled.
+ * dropout: NULL, or the descriptor above; the forward, gpt_attn_bwd_strided
+ * and gpt_attn_bwd_main_strided take it (the prep phase does not depend on
+ * it: delta = rowsum(dout * O) holds for the dropped output O too).
  */
 int gpt_attn_fwd_strided(int dtype, int B, int H, int T, int D, const void* q,
                          const gpt_attn_layout* lq, const void* k, const gpt_attn_layout* lk,
                          const void* v, const gpt_attn_layout* lv, void* o,
                          const gpt_attn_layout* lo, void* o_lo, const gpt_attn_layout* llo,
-                         float* lse, void* stream);
+                         float* lse, const gpt_attn_dropout* dropout, void* stream);
 int gpt_attn_bwd_strided(int dtype, int B, int H, int T, int D, const void* q,
                          const gpt_attn_layout* lq, const void* k, const gpt_attn_layout* lk,
                          const void* v, const gpt_attn_layout* lv, const void* o,
@@ -200,7 +228,8 @@ int gpt_attn_bwd_strided(int dtype, int B, int H, int T, int D, const void* q,
                          const void* dout, const gpt_attn_layout* ldo, const float* lse,
                          float* dq, const gpt_attn_layout* ldq, float* dk,
                          const gpt_attn_layout* ldk, float* dv, const gpt_attn_layout* ldv,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         void* workspace, size_t workspace_bytes,
+                         const gpt_attn_dropout* dropout, void* stream);
 int gpt_attn_bwd_prep_strided(int dtype, int B, int H, int T, int D, const void* o,
                               const gpt_attn_layout* lo, const void* o_lo,
                               const gpt_attn_layout* llo, const void* dout,
@@ -212,7 +241,19 @@ int gpt_attn_bwd_main_strided(int dtype, int B, int H, int T, int D, const void*
                               const gpt_attn_layout* ldo, const float* lse, float* dq,
                               const gpt_attn_layout* ldq, float* dk, const gpt_attn_layout* ldk,
                               float* dv, const gpt_attn_layout* ldv, const void* workspace,
-                              size_t workspace_bytes, void* stream);
+                              size_t workspace_bytes, const gpt_attn_dropout* dropout,
+                              void* stream);
+
+/*
+ * The keep mask the kernels derive for a dropout descriptor, written out:
+ * mask [B,H,T,T] uint8 (device memory, contiguous), 1 where key j is visible
+ * to query i (j <= i) and kept, 0 elsewhere. For inspection and testing; the
+ * attention calls never read or write it. GPT_ATTN_E_INVAL for a NULL
+ * descriptor, a bad p, negative sizes, B*H*T >= 2^31 or B*H*T*T >= 2^40, or
+ * a NULL mask with a non-empty shape.
+ */
+int gpt_attn_dropout_mask(int B, int H, int T, const gpt_attn_dropout* dropout,
+                          unsigned char* mask, void* stream);
 
 /* Static, NUL-terminated description of a status code. Never NULL. */
 const char* gpt_attn_status_string(int status);

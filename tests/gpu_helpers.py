@@ -65,3 +65,31 @@ def assert_parity(errs: dict, dtype: str, label: str) -> None:
         if tol["mean"] is not None and mean > tol["mean"]:
             bad.append(f"{name}: mean-abs {mean:.3e} > {tol['mean']}")
     assert not bad, f"{label}: " + "; ".join(bad)
+
+
+def run_gpu_dropout(inp: dict, dropout, keep_o_lo: bool = True):
+    """run_gpu with attention dropout ``dropout`` = (p, seed, offset)."""
+    dev = torch.device("cuda:0")
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse, o_lo = gattn.attention_forward(q, k, v, keep_o_lo=keep_o_lo, dropout=dropout)
+    dq, dk, dv = gattn.attention_backward(q, k, v, o, do, lse, o_lo, dropout=dropout)
+    torch.cuda.synchronize()
+    return {"o": o.cpu(), "lse": lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
+
+
+def run_oracle_dropout(inp: dict, dropout, heads=None):
+    """fp64 oracle with the keep mask the oracle derives for ``dropout``."""
+    p, seed, offset = dropout
+    arrs = {n: inp[n].double().numpy() for n in ("q", "k", "v", "do")}
+    B, H, T, D = arrs["q"].shape
+    flat = list(range(B * H)) if heads is None else list(heads)
+    arrs = {n: a.reshape(B * H, T, D)[flat] for n, a in arrs.items()}
+    keep = oracle.dropout_keep(flat, T, p, seed, offset)
+    z = oracle.dropout_scale(p)
+    o, lse = oracle.attn_fwd_dropout(arrs["q"], arrs["k"], arrs["v"], keep, z)
+    dq, dk, dv = oracle.attn_bwd_dropout(arrs["q"], arrs["k"], arrs["v"], arrs["do"], keep, z)
+    if heads is None:
+        shape = (B, H, T, D)
+        o, dq, dk, dv = (x.reshape(shape) for x in (o, dq, dk, dv))
+        lse = lse.reshape(B, H, T)
+    return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}

@@ -17,6 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gpt_attn.h")
 
 OK, E_INVAL, E_UNSUP, E_ALIGN, E_WS, E_HIP, E_LAYOUT = 0, 1, 2, 3, 4, 5, 6
+DROP = gattn.GptAttnDropout
 F32, BF16 = 0, 1
 P = 0x10000  # 16-byte aligned fake device address, never dereferenced
 
@@ -146,17 +147,18 @@ def fused(B, H, T, D=64):
 
 
 def fwd_s(lib, dtype=BF16, B=2, H=3, T=8, D=64, lq=None, lk=None, lv=None, lo=None, llo=None,
-          o_lo=None):
+          o_lo=None, drop=None):
     r = lambda x: None if x is None else ctypes.byref(x)
     return lib.gpt_attn_fwd_strided(dtype, B, H, T, D, P, r(lq), P, r(lk), P, r(lv), P, r(lo),
-                                    o_lo, r(llo), P, None)
+                                    o_lo, r(llo), P, r(drop), None)
 
 
-def bwd_s(lib, dtype=BF16, B=2, H=3, T=8, D=64, ws=None, ws_bytes=0, **lays):
+def bwd_s(lib, dtype=BF16, B=2, H=3, T=8, D=64, ws=None, ws_bytes=0, drop=None, **lays):
     r = lambda n: None if lays.get(n) is None else ctypes.byref(lays[n])
     return lib.gpt_attn_bwd_strided(dtype, B, H, T, D, P, r("q"), P, r("k"), P, r("v"), P,
                                     r("o"), None, None, P, r("do"), P, P, r("dq"), P, r("dk"),
-                                    P, r("dv"), ws, ws_bytes, None)
+                                    P, r("dv"), ws, ws_bytes,
+                                    None if drop is None else ctypes.byref(drop), None)
 
 
 def test_strided_layout_rules_forward(lib):
@@ -209,7 +211,7 @@ def test_plain_calls_equal_strided_calls_with_null_layouts(lib):
                                          ctypes.byref(L(0, 0, 32)), P, 1 << 20, None) == E_LAYOUT
     assert lib.gpt_attn_bwd_main_strided(BF16, 1, 1, 8, 64, P, None, P, None, P, None, P, None,
                                          P, P, None, P, None, P, ctypes.byref(L(0, 0, 32)), None,
-                                         0, None) == E_LAYOUT
+                                         0, None, None) == E_LAYOUT
 
 
 def test_view_helpers_match_the_fused_layout():
@@ -229,3 +231,29 @@ def test_view_helpers_match_the_fused_layout():
     assert o.stride() == (out_l.batch, out_l.head, out_l.row, 1)
     o[1, 2, 3, 4] = 7.0
     assert y[1, 3, 2 * D + 4].item() == 7.0
+
+
+# ---- dropout descriptor ------------------------------------------------------------
+
+def test_dropout_descriptor_validation(lib):
+    """Bad probabilities are rejected before any launch; good descriptors pass
+    validation (the backward then stops at the missing workspace)."""
+    for p in (-0.1, 1.0, 1.5, 0.999995, float("nan"), float("inf")):
+        assert fwd_s(lib, drop=DROP(p, 1, 0)) == E_INVAL, p
+        assert bwd_s(lib, drop=DROP(p, 1, 0)) == E_INVAL, p
+        assert bwd_s(lib, dtype=F32, drop=DROP(p, 1, 0)) == E_INVAL, p
+    for p in (0.0, 0.1, 0.2, 0.99999):
+        assert bwd_s(lib, drop=DROP(p, 2**64 - 1, 2**32 - 1)) == E_WS, p
+    # Shape errors still come first.
+    assert fwd_s(lib, D=32, drop=DROP(2.0, 0, 0)) == E_UNSUP
+
+
+def test_dropout_mask_entry_validation(lib):
+    d = ctypes.byref(DROP(0.2, 5, 1))
+    assert lib.gpt_attn_dropout_mask(1, 1, 8, None, P, None) == E_INVAL
+    assert lib.gpt_attn_dropout_mask(-1, 1, 8, d, P, None) == E_INVAL
+    assert lib.gpt_attn_dropout_mask(1, 1, 8, ctypes.byref(DROP(1.0, 5, 1)), P, None) == E_INVAL
+    assert lib.gpt_attn_dropout_mask(1, 1, 8, d, None, None) == E_INVAL
+    assert lib.gpt_attn_dropout_mask(1 << 12, 1 << 10, 1 << 10, d, P, None) == E_INVAL  # 2^42 B
+    assert lib.gpt_attn_dropout_mask(0, 1, 8, d, None, None) == OK   # empty: nothing to do
+    assert lib.gpt_attn_dropout_mask(1, 1, 0, d, None, None) == OK
