@@ -72,6 +72,8 @@ def _load():
     lib.oracle_attn_bwd_dropout.argtypes = [L, L, L, _DP, _DP, _DP, _DP, U8P, ctypes.c_double,
                                             _DP, _DP, _DP, I]
     lib.oracle_attn_bwd_dropout.restype = I
+    lib.oracle_attn_decode.argtypes = [L, L, L, _DP, _DP, _DP, LP, _DP, _DP]
+    lib.oracle_attn_decode.restype = I
     _lib = lib
     return lib
 
@@ -234,3 +236,29 @@ def attn_bwd_dropout(q, k, v, dout, keep, z: float, nthreads: int | None = None)
     if st != 0:
         raise RuntimeError(f"oracle_attn_bwd_dropout failed with status {st}")
     return dq, dk, dv
+
+
+# ---- one query against a key/value cache --------------------------------------------
+
+def attn_decode(q, k, v, lengths):
+    """(O [..., D], LSE [...]) in fp64 for queries q [..., D] against caches
+    k, v [..., L, D] of which the first lengths[...] rows are used (lengths
+    broadcast over the leading dimensions of q, e.g. [B] for q [B, H, D])."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    if k.shape != v.shape or k.shape[:-2] != q.shape[:-1] or k.shape[-1] != q.shape[-1]:
+        raise ValueError("expected q [..., D] and k, v [..., L, D]")
+    lead = q.shape[:-1]
+    L, D = k.shape[-2], k.shape[-1]
+    heads = int(np.prod(lead)) if lead else 1
+    lens = np.asarray(lengths, dtype=np.int64)
+    while lens.ndim < len(lead):
+        lens = lens[..., None]
+    lens = np.ascontiguousarray(np.broadcast_to(lens, lead).reshape(-1))
+    o = np.zeros(q.shape, dtype=np.float64)
+    lse = np.zeros(lead, dtype=np.float64)
+    st = _load().oracle_attn_decode(heads, L, D, _ptr(q), _ptr(k), _ptr(v),
+                                    lens.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
+                                    _ptr(o), _ptr(lse))
+    if st != 0:
+        raise RuntimeError(f"oracle_attn_decode failed with status {st}")
+    return o, lse

@@ -548,3 +548,56 @@ int oracle_attn_bwd_dropout(long heads, long T, long D, const double* q, const d
   jb.dv = dv;
   return run_djobs(jb, nthreads);
 }
+
+/* ==== one query against a key/value cache ================================
+ *
+ * Sampling (generate() on the same page, section 2) feeds the sequence back
+ * one position at a time; the newest position's query attends to every key
+ * up to and including its own. With a cache of n keys and values that is the
+ * last row of the causal forward at T = n:
+ *   S_j = s q.K_j (j < n),  O = sum_j softmax(S)_j V_j,  LSE = ln sum_j e^S_j
+ * heads are independent; each head h has its own length n_h (0 <= n_h <= L,
+ * cache rows beyond n_h are ignored). n_h = 0 gives O = 0 and LSE = -inf.
+ * q is [heads, D], the caches [heads, L, D], o [heads, D], lse [heads].
+ */
+int oracle_attn_decode(long heads, long L, long D, const double* q, const double* k,
+                       const double* v, const long* lengths, double* o, double* lse) {
+  if (heads < 0 || L < 0 || D < 1 || (heads > 0 && (!q || !k || !v || !lengths || !o || !lse)))
+    return ORACLE_EINVAL;
+  const double s = 1.0 / sqrt((double)D);
+  double* p = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+  if (!p) return ORACLE_ENOMEM;
+  for (long h = 0; h < heads; ++h) {
+    const long n = lengths[h];
+    if (n < 0 || n > L) {
+      free(p);
+      return ORACLE_EINVAL;
+    }
+    const double* qh = q + h * D;
+    const double* kh = k + h * L * D;
+    const double* vh = v + h * L * D;
+    double* oh = o + h * D;
+    for (long d = 0; d < D; ++d) oh[d] = 0.0;
+    if (n == 0) {
+      lse[h] = -INFINITY;
+      continue;
+    }
+    double m = -INFINITY;
+    for (long j = 0; j < n; ++j) {
+      double dot = 0.0;
+      for (long d = 0; d < D; ++d) dot += qh[d] * kh[j * D + d];
+      p[j] = s * dot;
+      if (p[j] > m) m = p[j];
+    }
+    double l = 0.0;
+    for (long j = 0; j < n; ++j) {
+      p[j] = exp(p[j] - m);
+      l += p[j];
+    }
+    for (long j = 0; j < n; ++j)
+      for (long d = 0; d < D; ++d) oh[d] += (p[j] / l) * vh[j * D + d];
+    lse[h] = m + log(l);
+  }
+  free(p);
+  return ORACLE_OK;
+}

@@ -59,6 +59,26 @@ DROPOUT_MUTANTS = [
 ]
 
 
+# Planted mistakes in the one-query decode function.
+DECODE_MUTANTS = [
+    ("decode_length_off_by_one", "for (long j = 0; j < n; ++j) {\n      double dot",
+     "for (long j = 0; j + 1 < n; ++j) {\n      double dot"),
+    ("decode_unnormalized", "oh[d] += (p[j] / l) * vh[j * D + d];", "oh[d] += p[j] * vh[j * D + d];"),
+    ("decode_lse_without_max", "lse[h] = m + log(l);\n  }\n  free(p);", "lse[h] = log(l);\n  }\n  free(p);"),
+    ("decode_cache_stride", "const double* kh = k + h * L * D;", "const double* kh = k + h * D;"),
+]
+
+
+def _decode_pin_suite():
+    from tests import test_oracle_decode as dc
+    return [
+        ("last_row", lambda: dc.test_equals_last_row_of_causal_forward(17, 8)),
+        ("brute", lambda: dc.test_brute_force_last_row(6, 5)),
+        ("closed", dc.test_closed_forms),
+        ("lengths", dc.test_rows_past_length_are_ignored_and_lengths_per_head),
+    ]
+
+
 def _dropout_pin_suite(rocrand_ref):
     from tests import test_oracle_dropout as dp
     suite = [
@@ -160,4 +180,16 @@ def test_mutant_is_caught(tmp_path, name, old, new):
     lib = _build_mutant(tmp_path, name, old, new)
     with _swapped_oracle(lib):
         failed = _failing_pins()
+    assert failed, f"no pin caught the planted mistake {name}"
+
+
+def test_real_oracle_passes_every_decode_pin():
+    assert _failing_pins(_decode_pin_suite()) == []
+
+
+@pytest.mark.parametrize("name,old,new", DECODE_MUTANTS, ids=[m[0] for m in DECODE_MUTANTS])
+def test_decode_mutant_is_caught(tmp_path, name, old, new):
+    lib = _build_mutant(tmp_path, name, old, new)
+    with _swapped_oracle(lib):
+        failed = _failing_pins(_decode_pin_suite())
     assert failed, f"no pin caught the planted mistake {name}"
