@@ -14,6 +14,11 @@ FLOPs are the causal algorithmic count: only the T(T+1)/2 unmasked (query,
 key) pairs per head, 4*D per pair forward (QK^T and PV) and 10*D per pair
 backward (QK^T recompute, dP, dV, dK, dQ).
 
+``--mode decode`` measures the inference path instead: one step = one
+gpt_attn_decode call (one new query per sequence and head against a
+key/value cache) on a decode workload; the metric is cache bytes read per
+second against the HBM roofline.
+
 Prints one JSON line. ``roofline`` describes the dominant kernel (the
 backward main kernel): its algorithmic FLOPs per launch over its average
 launch duration, timed with HIP events on the launch stream inside the timed
@@ -36,6 +41,7 @@ if ROOT not in sys.path:
 PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "gpt2_124m_bf16_b12_h12_t1024"
+DEFAULT_DECODE_WORKLOAD = "gpt2_124m_decode_bf16_b64_h12_l1024"
 DOMINANT_KERNEL = "attn_bwd_main_bf16_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bwd_main_bf16_gpt2_124m_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "causal_self_attention_amd", "csrc", f)
@@ -90,6 +96,86 @@ def cpu_baseline(w, inp, max_heads: int, threads: int):
                       f"fp64, {dt:.2f} s wall"}
 
 
+def decode_bytes(w, lengths) -> int:
+    """Algorithmic bytes of one decode call: every cached K and V row up to
+    each sequence's length, q, O (input dtype) and LSE (fp32)."""
+    esize = 2 if w.dtype == "bf16" else 4
+    rows = int(sum(int(n) for n in lengths)) * w.H
+    return rows * w.D * 2 * esize + 2 * w.B * w.H * w.D * esize + 4 * w.B * w.H
+
+
+def run_decode(args) -> int:
+    import torch
+    import causal_self_attention_amd as gattn
+    from causal_self_attention_amd.inputs import DECODE_WORKLOADS, decode_inputs
+
+    if not os.path.exists(gattn.library_path()):
+        from causal_self_attention_amd import build
+        build.build()
+    name = args.workload if args.workload in DECODE_WORKLOADS else DEFAULT_DECODE_WORKLOAD
+    w = DECODE_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    inp = decode_inputs(w, seed=args.seed)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    lengths = inp["lengths"].to(dev) if w.ragged else None
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, gattn.gpt_attn_decode_workspace_bytes(w.dtype, w.B, w.H, w.L, w.D)
+                         // 4), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        gattn.gpt_attn_decode(q, k, v, lengths, o, lse, ws, stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        gattn.gpt_attn_decode(q, k, v, lengths, o, lse, ws, stream)
+        b.record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    avg = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    nbytes = decode_bytes(w, inp["lengths"].tolist())
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (avg * 1e-3) / 1e9
+    if not (torch.isfinite(o.float()).all() and torch.isfinite(lse).all()):
+        print("non-finite outputs", file=sys.stderr)
+        return 1
+    out = {
+        "metric": "causal attn decode step GB/s (KV cache read), GPT-2 124M layer",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "D": w.D,
+                   "ragged": w.ragged, "seed": args.seed, "bytes_per_step": nbytes},
+        "roofline": {"kernel": "attn_decode_split_kernel + attn_decode_merge_kernel",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "avg_launch_ms": round(avg, 5), "bytes_per_launch": nbytes,
+                     "traffic": None},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle._load()
+        t = time.perf_counter()
+        oracle.attn_decode(inp["q"], inp["k"], inp["v"], inp["lengths"].numpy())
+        dt = time.perf_counter() - t
+        out["cpu_baseline"] = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"all {w.B * w.H} heads, one fp64 thread, "
+                                         f"{dt:.2f} s wall"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +192,9 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="attention dropout rate (Philox keep mask, seed 1234, offset 0)")
+    ap.add_argument("--mode", choices=("train", "decode"), default="train",
+                    help="train: forward + backward (the headline); decode: one query per "
+                         "sequence against a key/value cache")
     ap.add_argument("--layout", choices=("bhtd", "fused"), default="bhtd",
                     help="bhtd: contiguous [B, H, T, D] operands; fused: views of the "
                          "projection's [B, T, 3C] output and of [B, T, C] buffers")
@@ -130,6 +219,9 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
         return 0
+
+    if args.mode == "decode":
+        return run_decode(args)
 
     import causal_self_attention_amd as gattn
     from causal_self_attention_amd.inputs import WORKLOADS, workload_inputs

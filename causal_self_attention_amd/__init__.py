@@ -21,8 +21,11 @@ and the strided forms gpt_attn_fwd_strided, gpt_attn_bwd_strided,
 gpt_attn_bwd_prep_strided, gpt_attn_bwd_main_strided (same arguments; each
 tensor's own strides become its gpt_attn_layout; the forward and backward
 ones take an optional ``dropout=(p, seed, offset)``), gpt_attn_dropout_mask
-(the keep mask the kernels derive, written out), plus two allocating
-conveniences, ``attention_forward`` and ``attention_backward``, and the view
+(the keep mask the kernels derive, written out), gpt_attn_decode (one query
+per head against a key/value cache) with gpt_attn_decode_workspace_bytes,
+plus three allocating
+conveniences, ``attention_forward``, ``attention_backward`` and
+``attention_decode``, and the view
 helpers ``split_qkv_heads`` / ``merged_heads_view`` for the fused [B, T, 3C]
 projection layout. Tensors are logically [B, H, T, D]: contiguous for the
 plain calls, any layout with unit stride along D for the strided ones; q, k,
@@ -43,6 +46,7 @@ __all__ = [
     "gpt_attn_bwd_strided", "gpt_attn_bwd_prep_strided", "gpt_attn_bwd_main_strided",
     "attention_forward", "attention_backward", "split_qkv_heads", "merged_heads_view",
     "DTYPE_CODES", "GptAttnLayout", "GptAttnDropout", "gpt_attn_dropout_mask",
+    "gpt_attn_decode", "gpt_attn_decode_workspace_bytes", "attention_decode",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,11 +60,11 @@ DTYPE_CODES = {"f32": GPT_ATTN_F32, "bf16": GPT_ATTN_BF16}
 #: every symbol include/gpt_attn.h declares
 EXPORTED_SYMBOLS = ("gpt_attn_fwd", "gpt_attn_bwd", "gpt_attn_bwd_prep", "gpt_attn_bwd_main",
                     "gpt_attn_fwd_strided", "gpt_attn_bwd_strided", "gpt_attn_bwd_prep_strided",
-                    "gpt_attn_bwd_main_strided", "gpt_attn_dropout_mask",
-                    "gpt_attn_bwd_workspace_bytes", "gpt_attn_status_string",
-                    "gpt_attn_abi_version")
+                    "gpt_attn_bwd_main_strided", "gpt_attn_dropout_mask", "gpt_attn_decode",
+                    "gpt_attn_decode_workspace_bytes", "gpt_attn_bwd_workspace_bytes",
+                    "gpt_attn_status_string", "gpt_attn_abi_version")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class GptAttnLayout(ctypes.Structure):
@@ -133,6 +137,11 @@ def load_library():
     lib.gpt_attn_bwd_main_strided.restype = i
     lib.gpt_attn_dropout_mask.argtypes = [i, i, i, dp_, vp, vp]
     lib.gpt_attn_dropout_mask.restype = i
+    lib.gpt_attn_decode.argtypes = [i, i, i, i, i, vp, lp, vp, lp, vp, lp, vp, vp, lp, vp, vp,
+                                    sz, vp]
+    lib.gpt_attn_decode.restype = i
+    lib.gpt_attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.gpt_attn_decode_workspace_bytes.restype = sz
     lib.gpt_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.gpt_attn_bwd_workspace_bytes.restype = sz
     lib.gpt_attn_status_string.argtypes = [i]
@@ -337,6 +346,54 @@ def gpt_attn_dropout_mask(B: int, H: int, T: int, dropout, mask, stream=None) ->
                                               _stream(mask.device, stream))
     if st != 0:
         raise GptAttnError("gpt_attn_dropout_mask", st)
+
+
+# ---- one query against a key/value cache -------------------------------------------
+
+def gpt_attn_decode_workspace_bytes(dtype: int | str, B: int, H: int, L: int, D: int) -> int:
+    code = DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
+    return int(load_library().gpt_attn_decode_workspace_bytes(code, B, H, L, D))
+
+
+def gpt_attn_decode(q, k_cache, v_cache, lengths, o, lse, workspace, stream=None) -> None:
+    """q, o [B, H, D] and caches [B, H, L, D] (any layout with unit D
+    stride); lengths: int32 [B] device tensor or None (L everywhere); lse
+    [B, H] fp32 contiguous."""
+    if q.dim() != 3 or o.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("expected q, o [B, H, D] and caches [B, H, L, D]")
+    B, H, L, D = (int(x) for x in k_cache.shape)
+    if tuple(q.shape) != (B, H, D) or tuple(o.shape) != (B, H, D):
+        raise ValueError("q and o must be [B, H, D] matching the caches")
+    _same_shape(k_cache, v_cache)
+    if lengths is not None:
+        import torch
+        if lengths.dtype != torch.int32 or tuple(lengths.shape) != (B,):
+            raise ValueError("lengths must be int32 of shape [B]")
+    args = []
+    for t in (q.unsqueeze(2), k_cache, v_cache):
+        args.extend(_sptr(t))
+    args.append(_ptr(lengths))
+    args.extend(_sptr(o.unsqueeze(2)))
+    st = load_library().gpt_attn_decode(_dtype_code(q), B, H, L, D, *args, _ptr(lse),
+                                        _ptr(workspace), _ws_bytes(workspace),
+                                        _stream(q.device, stream))
+    if st != 0:
+        raise GptAttnError("gpt_attn_decode", st)
+
+
+def attention_decode(q, k_cache, v_cache, lengths=None, stream=None, out=None, workspace=None):
+    """One new query per (sequence, head) against the first lengths[b] rows
+    of the caches. Allocates O (unless ``out``), LSE and the workspace;
+    returns (o, lse)."""
+    import torch
+    B, H, L, D = (int(x) for x in k_cache.shape)
+    o = torch.empty((B, H, D), dtype=q.dtype, device=q.device) if out is None else out
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = gpt_attn_decode_workspace_bytes(_dtype_code(q), B, H, L, D)
+        workspace = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device=q.device)
+    gpt_attn_decode(q, k_cache, v_cache, lengths, o, lse, workspace, stream)
+    return o, lse
 
 
 # ---- views of the fused projection layout ---------------------------------------

@@ -86,6 +86,35 @@ struct BwdArgs {
   Dropout drop;  // drop.thr == 0: no dropout
 };
 
+// One query per head against a key/value cache. q and o are [B, H, D]
+// (lq.t, lo.t unused), k and v [B, H, L, D]; lengths [B] (device, int32) or
+// null for L everywhere, clamped to [0, L]. part is the workspace:
+// [n_heads, ceil(L / decode_chunk), kDecPart] fp32 partial (O, max, sum).
+struct DecArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int* lengths;
+  void* o;
+  float* lse;
+  float* part;
+  Layout lq, lk, lv, lo;
+  int n_heads, H, L;
+};
+
+constexpr int kDecPart = 68;  // 64 partial outputs, max, sum, 2 floats of padding
+
+// Cache rows per split workgroup: about 2048 workgroups in total, a multiple
+// of 128 keys (one step of the split kernel), between 128 and 1024.
+__host__ __device__ inline int decode_chunk(int n_heads, int L) {
+  const long long per = ((long long)n_heads * L + 2047) / 2048;
+  const long long c = (per + 127) / 128 * 128;
+  return (int)(c < 128 ? 128 : (c > 1024 ? 1024 : c));
+}
+
+hipError_t launch_decode_bf16(const DecArgs& a, hipStream_t stream);
+hipError_t launch_decode_f32(const DecArgs& a, hipStream_t stream);
+
 // Keep mask [n_heads, T, T] (uint8, 1 = kept; 0 above the diagonal).
 hipError_t launch_dropout_mask(const Dropout& d, int n_heads, int T, uint8_t* mask,
                                hipStream_t stream);

@@ -356,6 +356,59 @@ int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const voi
                               nullptr, workspace, workspace_bytes, nullptr, stream);
 }
 
+size_t gpt_attn_decode_workspace_bytes(int dtype, int B, int H, int L, int D) {
+  Shape s;
+  if (check_shape(dtype, B, H, L, D, &s) != GPT_ATTN_OK) return 0;
+  const long long heads = (long long)B * H;
+  if (heads == 0 || L == 0) return 0;
+  const long long chunks = ((long long)L + 127) / 128;  // the smallest chunk is 128 keys
+  return (size_t)(heads * chunks * gpt_attn::kDecPart * (long long)sizeof(float));
+}
+
+int gpt_attn_decode(int dtype, int B, int H, int L, int D, const void* q,
+                    const gpt_attn_layout* lq, const void* k_cache, const gpt_attn_layout* lk,
+                    const void* v_cache, const gpt_attn_layout* lv, const int* lengths, void* o,
+                    const gpt_attn_layout* lo, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  Shape s;  // the caches: [B, H, L, D]
+  GA_TRY(check_shape(dtype, B, H, L, D, &s));
+  Shape s1;  // one query per head: [B, H, 1, D]
+  GA_TRY(check_shape(dtype, B, H, 1, D, &s1));
+  const long long heads = (long long)B * H;
+  if (heads == 0) return GPT_ATTN_OK;
+  if (!q || !o || !lse || (L > 0 && (!k_cache || !v_cache))) return GPT_ATTN_E_INVAL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      !aligned16(lse) || !aligned16(lengths))
+    return GPT_ATTN_E_ALIGN;
+  gpt_attn::DecArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.lengths = lengths;
+  a.o = o;
+  a.lse = lse;
+  a.part = static_cast<float*>(workspace);
+  a.lq = resolve(lq, s1);
+  a.lo = resolve(lo, s1);
+  a.lk = resolve(lk, s);
+  a.lv = resolve(lv, s);
+  GA_TRY(check_layout(a.lq, s1, s1.esize, false));
+  GA_TRY(check_layout(a.lo, s1, s1.esize, true));
+  if (L > 0) {
+    GA_TRY(check_layout(a.lk, s, s.esize, false));
+    GA_TRY(check_layout(a.lv, s, s.esize, false));
+  }
+  const size_t need = gpt_attn_decode_workspace_bytes(dtype, B, H, L, D);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GPT_ATTN_E_WORKSPACE;
+  if (!aligned16(workspace)) return GPT_ATTN_E_ALIGN;
+  a.n_heads = (int)heads;
+  a.H = H;
+  a.L = L;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launch_status(dtype == GPT_ATTN_BF16 ? gpt_attn::launch_decode_bf16(a, st)
+                                              : gpt_attn::launch_decode_f32(a, st));
+}
+
 int gpt_attn_dropout_mask(int B, int H, int T, const gpt_attn_dropout* dropout,
                           unsigned char* mask, void* stream) {
   if (B < 0 || H < 0 || T < 0 || !dropout) return GPT_ATTN_E_INVAL;

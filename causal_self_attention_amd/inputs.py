@@ -16,6 +16,13 @@ the "baby GPT" Shakespeare-char model (6 heads of 64 channels, block size
 256) and GPT-2 124M / 774M / 1558M (12 / 20 / 25 heads of 64, block size
 1024). The pages give no activation statistics, so i.i.d. N(0, 1) draws stand
 in for real activations.
+
+Decode inputs (one new query per sequence against a key/value cache, as
+sampling with generate() does one position at a time): q [B, H, D] and
+caches k, v [B, H, L, D] drawn in that order with ``torch.randn`` in fp32,
+then cast; with ``ragged`` the per-sequence lengths [B] are drawn uniformly
+from 1 .. L with ``torch.randint`` from the same generator afterwards,
+otherwise every length is L.
 """
 from __future__ import annotations
 
@@ -23,7 +30,8 @@ import dataclasses
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "workload_inputs", "torch_dtype"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "workload_inputs", "torch_dtype",
+           "DecodeWorkload", "DECODE_WORKLOADS", "make_decode_inputs", "decode_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -84,3 +92,51 @@ def make_inputs(B: int, H: int, T: int, D: int, dtype: str = "bf16", seed: int =
 
 def workload_inputs(w: Workload, seed: int = 0) -> dict[str, torch.Tensor]:
     return make_inputs(w.B, w.H, w.T, w.D, w.dtype, seed, w.qk_scale)
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """One decode step of an attention layer: B sequences, cache length L."""
+
+    name: str
+    dtype: str
+    B: int
+    H: int
+    L: int
+    D: int
+    ragged: bool = False
+
+
+DECODE_WORKLOADS: dict[str, DecodeWorkload] = {
+    w.name: w
+    for w in (
+        # GPT-2 124M layer sampling 64 sequences at a full 1024-token context.
+        DecodeWorkload("gpt2_124m_decode_bf16_b64_h12_l1024", "bf16", 64, 12, 1024, 64),
+        # The same with every sequence at its own length in 1 .. 1024.
+        DecodeWorkload("gpt2_124m_decode_ragged_bf16_b64_h12_l1024", "bf16", 64, 12, 1024, 64,
+                       True),
+        # Shakespeare-char layer sampling one sequence (block size 256), fp32.
+        DecodeWorkload("shakespeare_char_decode_f32_b1_h6_l256", "f32", 1, 6, 256, 64),
+    )
+}
+
+
+def make_decode_inputs(B: int, H: int, L: int, D: int, dtype: str = "bf16", seed: int = 0,
+                       ragged: bool = False) -> dict[str, torch.Tensor]:
+    """CPU tensors q [B, H, D], k, v [B, H, L, D] in ``dtype`` and lengths
+    [B] (int32)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn((B, H, D), dtype=torch.float32, generator=gen)
+    k = torch.randn((B, H, L, D), dtype=torch.float32, generator=gen)
+    v = torch.randn((B, H, L, D), dtype=torch.float32, generator=gen)
+    if ragged and L > 0:
+        lengths = torch.randint(1, L + 1, (B,), generator=gen, dtype=torch.int64)
+    else:
+        lengths = torch.full((B,), L, dtype=torch.int64)
+    td = torch_dtype(dtype)
+    return {"q": q.to(td).contiguous(), "k": k.to(td).contiguous(),
+            "v": v.to(td).contiguous(), "lengths": lengths.to(torch.int32)}
+
+
+def decode_inputs(w: DecodeWorkload, seed: int = 0) -> dict[str, torch.Tensor]:
+    return make_decode_inputs(w.B, w.H, w.L, w.D, w.dtype, seed, w.ragged)

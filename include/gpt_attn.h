@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GPT_ATTN_ABI_VERSION 3
+#define GPT_ATTN_ABI_VERSION 4
 
 /* Status codes returned by every int-returning entry point. */
 enum gpt_attn_status {
@@ -254,6 +254,38 @@ int gpt_attn_bwd_main_strided(int dtype, int B, int H, int T, int D, const void*
  */
 int gpt_attn_dropout_mask(int B, int H, int T, const gpt_attn_dropout* dropout,
                           unsigned char* mask, void* stream);
+
+/*
+ * One query per (sequence, head) against a key/value cache: what sampling
+ * needs, since generate() feeds the sequence back one position at a time
+ * (page "nanoGPT: a real GPT in two 300-line files", section 2 "How the code
+ * works") and the newest query sees every earlier position and its own. With
+ * n = lengths[b] cached rows for sequence b this is the last row of the
+ * causal forward at T = n:
+ *   O   = softmax(q K[0:n]^T / sqrt(D)) V[0:n],   LSE = ln sum_j exp(q.K_j / sqrt(D))
+ *
+ *   q          in   [B,H,D] of dtype (lq: batch and head strides; row unused)
+ *   k_cache,
+ *   v_cache    in   [B,H,L,D] of dtype (lk, lv: any gpt_attn_layout); rows at
+ *                   and beyond lengths[b] are never read
+ *   lengths    in   OPTIONAL device int32 [B]: cached rows per sequence,
+ *                   clamped to [0, L]; NULL means L for every sequence. A
+ *                   length of 0 gives O = 0 and LSE = -inf.
+ *   o          out  [B,H,D] of dtype (lo: batch and head strides)
+ *   lse        out  [B,H] fp32, contiguous
+ *   workspace  scratch of gpt_attn_decode_workspace_bytes(...) bytes (the
+ *              per-chunk partial results), owned by the caller
+ *
+ * Layout rules, alignment, errors and streams as for the other calls; the
+ * shape rules apply to [B,H,L,D] (L may be 0). Arithmetic in fp32 for both
+ * dtypes (bf16 inputs are widened exactly).
+ */
+size_t gpt_attn_decode_workspace_bytes(int dtype, int B, int H, int L, int D);
+int gpt_attn_decode(int dtype, int B, int H, int L, int D, const void* q,
+                    const gpt_attn_layout* lq, const void* k_cache, const gpt_attn_layout* lk,
+                    const void* v_cache, const gpt_attn_layout* lv, const int* lengths, void* o,
+                    const gpt_attn_layout* lo, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code. Never NULL. */
 const char* gpt_attn_status_string(int status);

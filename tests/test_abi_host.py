@@ -257,3 +257,33 @@ def test_dropout_mask_entry_validation(lib):
     assert lib.gpt_attn_dropout_mask(1 << 12, 1 << 10, 1 << 10, d, P, None) == E_INVAL  # 2^42 B
     assert lib.gpt_attn_dropout_mask(0, 1, 8, d, None, None) == OK   # empty: nothing to do
     assert lib.gpt_attn_dropout_mask(1, 1, 0, d, None, None) == OK
+
+
+# ---- decode ----------------------------------------------------------------------------
+
+def dec(lib, dtype=BF16, B=2, H=3, L=100, D=64, q=P, k=P, v=P, lengths=None, o=P, lse=P,
+        ws=None, ws_bytes=0, lk=None, lo=None):
+    r = lambda x: None if x is None else ctypes.byref(x)
+    return lib.gpt_attn_decode(dtype, B, H, L, D, q, None, k, r(lk), v, None, lengths, o, r(lo),
+                               lse, ws, ws_bytes, None)
+
+
+def test_decode_validation(lib):
+    need = lib.gpt_attn_decode_workspace_bytes(BF16, 2, 3, 100, 64)
+    assert need == 2 * 3 * 1 * 68 * 4       # one 128-key chunk per head at most
+    assert lib.gpt_attn_decode_workspace_bytes(BF16, 64, 12, 1024, 64) == 768 * 8 * 68 * 4
+    assert lib.gpt_attn_decode_workspace_bytes(BF16, 2, 3, 0, 64) == 0
+    assert lib.gpt_attn_decode_workspace_bytes(BF16, 2, 3, 100, 32) == 0
+    assert dec(lib, D=128) == E_UNSUP
+    assert dec(lib, dtype=5) == E_INVAL
+    assert dec(lib, L=-1) == E_INVAL
+    for name in ("q", "k", "v", "o", "lse"):
+        assert dec(lib, **{name: None}) == E_INVAL, name
+        assert dec(lib, **{name: P + 4}) == E_ALIGN, name
+    assert dec(lib, lengths=P + 4) == E_ALIGN
+    assert dec(lib) == E_WS                             # every check passed but the workspace
+    assert dec(lib, ws=P, ws_bytes=need - 1) == E_WS
+    assert dec(lib, ws=P + 4, ws_bytes=need) == E_ALIGN
+    assert dec(lib, lk=L(-8, 64, 64)) == E_LAYOUT
+    assert dec(lib, lo=L(64, 0, 64)) == E_LAYOUT       # heads of O overlap
+    assert dec(lib, B=0, q=None, k=None, v=None, o=None, lse=None) == OK
