@@ -42,10 +42,10 @@ PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "gpt2_124m_bf16_b12_h12_t1024"
 DEFAULT_DECODE_WORKLOAD = "gpt2_124m_decode_bf16_b64_h12_l1024"
-DOMINANT_KERNEL = "attn_bwd_main_bf16_kernel"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bwd_main_bf16_gpt2_124m_traffic.json")
+DOMINANT_KERNEL = "attn_bwd_main_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bwd_main_gpt2_124m_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "causal_self_attention_amd", "csrc", f)
-                  for f in ("attn_bwd_bf16.hip", "attn_common.h", "attn_launch.h")]
+                  for f in ("attn_bwd.hip", "attn_common.h", "attn_launch.h", "attn_dropout.h")]
 
 
 def flops(w):
@@ -99,7 +99,7 @@ def cpu_baseline(w, inp, max_heads: int, threads: int):
 def decode_bytes(w, lengths) -> int:
     """Algorithmic bytes of one decode call: every cached K and V row up to
     each sequence's length, q, O (input dtype) and LSE (fp32)."""
-    esize = 2 if w.dtype == "bf16" else 4
+    esize = 4 if w.dtype == "f32" else 2
     rows = int(sum(int(n) for n in lengths)) * w.H
     return rows * w.D * 2 * esize + 2 * w.B * w.H * w.D * esize + 4 * w.B * w.H
 
@@ -230,23 +230,24 @@ def main(argv=None) -> int:
         from causal_self_attention_amd import build
         build.build()
     w = WORKLOADS[args.workload]
-    if w.dtype != "bf16":
-        print("bench.py times the bf16 path; pick a bf16 workload", file=sys.stderr)
+    if w.dtype == "f32":
+        print("bench.py times the matrix-core path; pick a bf16 or f16 workload",
+              file=sys.stderr)
         return 2
+    from causal_self_attention_amd.inputs import torch_dtype
+    td = torch_dtype(w.dtype)
     dev = torch.device("cuda:0")
     inp = workload_inputs(w, seed=args.seed)
     fused = args.layout == "fused"
     if fused:
         C = w.H * w.D
-        qkv = torch.empty(w.B, w.T, 3 * C, dtype=torch.bfloat16, device=dev)
+        qkv = torch.empty(w.B, w.T, 3 * C, dtype=td, device=dev)
         q, k, v = gattn.split_qkv_heads(qkv, w.H)
         for view, name in ((q, "q"), (k, "k"), (v, "v")):
             view.copy_(inp[name].to(dev))
-        do = gattn.merged_heads_view(torch.empty(w.B, w.T, C, dtype=torch.bfloat16,
-                                                 device=dev), w.H)
+        do = gattn.merged_heads_view(torch.empty(w.B, w.T, C, dtype=td, device=dev), w.H)
         do.copy_(inp["do"].to(dev))
-        o = gattn.merged_heads_view(torch.empty(w.B, w.T, C, dtype=torch.bfloat16,
-                                                device=dev), w.H)
+        o = gattn.merged_heads_view(torch.empty(w.B, w.T, C, dtype=td, device=dev), w.H)
         dq, dk, dv = gattn.split_qkv_heads(
             torch.empty(w.B, w.T, 3 * C, dtype=torch.float32, device=dev), w.H)
         fwd_call = gattn.gpt_attn_fwd_strided
@@ -266,9 +267,9 @@ def main(argv=None) -> int:
         fwd_call = functools.partial(gattn.gpt_attn_fwd_strided, dropout=drop)
         prep_call = gattn.gpt_attn_bwd_prep_strided
         main_call = functools.partial(gattn.gpt_attn_bwd_main_strided, dropout=drop)
-    o_lo = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    o_lo = torch.empty(q.shape, dtype=td, device=dev)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
-    ws = torch.empty(gattn.gpt_attn_bwd_workspace_bytes("bf16", w.B, w.H, w.T, w.D) // 4,
+    ws = torch.empty(gattn.gpt_attn_bwd_workspace_bytes(w.dtype, w.B, w.H, w.T, w.D) // 4,
                      dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -321,7 +322,8 @@ def main(argv=None) -> int:
         return 1
 
     main_tflops = bwd_flop / (avg["main"] * 1e-3) / 1e12
-    traffic = None if (fused or args.dropout > 0.0) else load_traffic(bwd_flop)
+    traffic = (None if (fused or args.dropout > 0.0 or w.name != DEFAULT_WORKLOAD)
+               else load_traffic(bwd_flop))
     out = {
         "metric": "causal attn fwd+bwd TFLOP/s and % bf16 MFMA peak, GPT-2 124M shape",
         "value": round(value, 2),
@@ -333,7 +335,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "D": w.D,
                    "causal": True, "scale": 1.0 / w.D ** 0.5, "seed": args.seed,

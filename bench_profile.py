@@ -12,7 +12,7 @@ program directly after ``--``):
   4./5. the same two counters over a plain device copy of known size (the
      scale that turns the counters' KiB into bytes)
      -> profiles/hbm_traffic_<workload>.md and, for the dominant kernel,
-        profiles/attn_bwd_main_bf16_gpt2_124m_traffic.json (read by bench.py,
+        profiles/attn_bwd_main_gpt2_124m_traffic.json (read by bench.py,
         keyed by a hash of the kernel source so a stale figure is dropped).
 """
 from __future__ import annotations
@@ -96,7 +96,8 @@ def col(row, *names):
     raise KeyError(f"none of {names} in {list(row)}")
 
 
-KERNELS = ("attn_fwd_bf16_kernel", "attn_bwd_prep_bf16_kernel", "attn_bwd_main_bf16_kernel",
+KERNELS = ("attn_fwd_kernel", "attn_bwd_prep_kernel", "attn_bwd_main_kernel",
+           "attn_decode_split_kernel", "attn_decode_merge_kernel", "dropout_mask_kernel",
            "attn_fwd_f32_kernel", "attn_bwd_prep_f32_kernel", "attn_bwd_dkdv_f32_kernel",
            "attn_bwd_dq_f32_kernel")
 
@@ -217,9 +218,9 @@ def main():
     E = w.B * w.H * w.T * w.D
     R = w.B * w.H * w.T
     algo = {  # compulsory bytes per launch, bf16 inputs, fp32 gradients
-        "attn_fwd_bf16_kernel": 3 * 2 * E + 2 * 2 * E + 4 * R,            # q,k,v in; o, o_lo, lse out
-        "attn_bwd_prep_bf16_kernel": 3 * 2 * E + 4 * R + 4 * E,           # o, o_lo, dout in; delta, dq=0
-        "attn_bwd_main_bf16_kernel": 4 * 2 * E + 8 * R + 3 * 4 * E,       # q,k,v,dout,lse,delta; dq,dk,dv
+        "attn_fwd_kernel": 3 * 2 * E + 2 * 2 * E + 4 * R,            # q,k,v in; o, o_lo, lse out
+        "attn_bwd_prep_kernel": 3 * 2 * E + 4 * R + 4 * E,           # o, o_lo, dout in; delta, dq=0
+        "attn_bwd_main_kernel": 4 * 2 * E + 8 * R + 3 * 4 * E,       # q,k,v,dout,lse,delta; dq,dk,dv
     }
     lines = [f"# HBM traffic per dispatch: {args.workload}", "",
              f"Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one rocprofv3 --pmc run "

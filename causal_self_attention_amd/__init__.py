@@ -29,10 +29,10 @@ conveniences, ``attention_forward``, ``attention_backward`` and
 helpers ``split_qkv_heads`` / ``merged_heads_view`` for the fused [B, T, 3C]
 projection layout. Tensors are logically [B, H, T, D]: contiguous for the
 plain calls, any layout with unit stride along D for the strided ones; q, k,
-v, o, dout are float32 or bfloat16; lse [B, H, T] (contiguous) and dq, dk,
-dv are float32. o_lo (bf16 only, may be None) is the bf16 low part of the
-forward's fp32 O, which the backward uses for an accurate
-delta = rowsum(dO * O).
+v, o, dout are float32, bfloat16 or float16 with D in {32, 64}; lse
+[B, H, T] (contiguous) and dq, dk, dv are float32. o_lo (16-bit dtypes only,
+may be None) is the low part of the forward's fp32 O in the same dtype,
+which the backward uses for an accurate delta = rowsum(dO * O).
 """
 from __future__ import annotations
 
@@ -55,7 +55,8 @@ _lib = None
 
 GPT_ATTN_F32 = 0
 GPT_ATTN_BF16 = 1
-DTYPE_CODES = {"f32": GPT_ATTN_F32, "bf16": GPT_ATTN_BF16}
+GPT_ATTN_F16 = 2
+DTYPE_CODES = {"f32": GPT_ATTN_F32, "bf16": GPT_ATTN_BF16, "f16": GPT_ATTN_F16}
 
 #: every symbol include/gpt_attn.h declares
 EXPORTED_SYMBOLS = ("gpt_attn_fwd", "gpt_attn_bwd", "gpt_attn_bwd_prep", "gpt_attn_bwd_main",
@@ -64,7 +65,7 @@ EXPORTED_SYMBOLS = ("gpt_attn_fwd", "gpt_attn_bwd", "gpt_attn_bwd_prep", "gpt_at
                     "gpt_attn_decode_workspace_bytes", "gpt_attn_bwd_workspace_bytes",
                     "gpt_attn_status_string", "gpt_attn_abi_version")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class GptAttnLayout(ctypes.Structure):
@@ -173,7 +174,9 @@ def _dtype_code(t) -> int:
         return GPT_ATTN_F32
     if t.dtype == torch.bfloat16:
         return GPT_ATTN_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+    if t.dtype == torch.float16:
+        return GPT_ATTN_F16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float32, bfloat16 or float16")
 
 
 def _ptr(t):
@@ -431,7 +434,7 @@ def attention_forward(q, k, v, stream=None, keep_o_lo: bool = True, out=None, dr
     shape = tuple(q.shape)
     o = torch.empty(shape, dtype=q.dtype, device=q.device) if out is None else out
     o_lo = (torch.empty(shape, dtype=q.dtype, device=q.device)
-            if (keep_o_lo and q.dtype == torch.bfloat16) else None)
+            if (keep_o_lo and q.dtype != torch.float32) else None)
     lse = torch.empty(shape[:-1], dtype=torch.float32, device=q.device)
     gpt_attn_fwd_strided(q, k, v, o, o_lo, lse, stream, dropout)
     return o, lse, o_lo

@@ -1,10 +1,10 @@
-// Causal attention backward, bf16 inputs, fp32 accumulation and fp32
-// gradients, head dim 64, for gfx950 (CDNA4).
+// Causal attention backward, bf16 or fp16 inputs, fp32 accumulation and fp32
+// gradients, head dim D in {32, 64}, for gfx950 (CDNA4).
 //
 // The gradient of sum(dO * O) for O = softmax(Q K^T / sqrt(64), causal) V:
 // what autograd forms for nanoGPT's loss.backward() through the fused
 // attention call (page "nanoGPT: a real GPT in two 300-line files", sections
-// 1 "Summary" and 2 "How the code works"). With s = 1/sqrt(64):
+// 1 "Summary" and 2 "How the code works"). With s = 1/sqrt(D):
 //   delta_i = sum_d dO_id O_id
 //   P_ij    = exp(s Q_i.K_j - LSE_i)        (recomputed; j <= i)
 //   dV_j    = sum_i P_ij dO_i
@@ -22,15 +22,17 @@
 // the transposed operands (Q^T, dO^T for dK^T += Q^T dS and dV^T += dO^T P)
 // come from transposing LDS reads. Per tile each wave recomputes P from the
 // saved LSE, forms dS and writes its dS^T rows to LDS; then dQ = dS K over
-// the 256 keys is formed as four 32x32 blocks, each split into two key
-// halves whose sums meet in LDS, and waves 0..3 add the result into the fp32
-// dQ with atomic adds (which the memory side performs; 256 keys per
-// workgroup keep their number at T/256 per dQ element).
+// the 256 keys is formed as 2 * D/32 blocks of 32x32, each split into
+// 8 / (2 * D/32) key parts whose sums meet in LDS, and the waves of part 0
+// add the result into the fp32 dQ with atomic adds (which the memory side
+// performs; 256 keys per workgroup keep their number at T/256 per dQ
+// element).
 //
-// Precision: S = Q K^T and dP = dO V^T multiply bf16 inputs exactly. The
-// three products with a rounded operand (dV += P^T dO, dK += dS^T Q,
-// dQ += dS K) use fp16 MFMA: P and dS are rounded to fp16 (11 significant
-// bits) and the bf16 Q, K, dO tiles convert to fp16 exactly.
+// Precision: every product runs on fp16 MFMA with fp32 accumulation. Q, K,
+// V and dO are converted to fp16 when staged (exact for bf16 in fp16's
+// normal range; nothing to do for fp16 inputs), so S = Q K^T and dP = dO V^T
+// multiply the inputs exactly; P and dS are rounded to fp16 (11 significant
+// bits) for dV += P^T dO, dK += dS^T Q and dQ += dS K.
 //
 // Attention dropout (a separate instantiation) regenerates the forward's
 // keep mask M: per 32x32 block each lane draws the Philox blocks of one query
@@ -49,26 +51,35 @@ constexpr int kBK = 256;      // keys per workgroup (8 waves x 32)
 constexpr int kBQ = 64;       // queries per step
 constexpr int kThreads = 512;
 constexpr int kLoaders = 256; // threads of waves 4..7: they alone load Q/dO tiles
-constexpr int kRowQ = 72;     // padded row of a 64-wide 16-bit LDS tile (144 bytes)
+constexpr int kRowS = 72;     // row of the dS^T tile: 64 queries + 8 (144 bytes)
 constexpr int kRowM = 40;     // row of a wave's 32 x 32 keep-mask tile (80 bytes)
 
-// Eight threads per (head, row): row r of the flattened [B*H, T] index space
-// is head r / T, position r % T.
-__global__ __launch_bounds__(256) void attn_bwd_prep_bf16_kernel(const BwdArgs a, int rows) {
+// Padded LDS row of a D-wide 16-bit tile (D + 8 elements).
+template <int D>
+constexpr int row_of() {
+  return D + 8;
+}
+
+// D/8 threads per (head, row), 8 elements each: row r of the flattened
+// [B*H, T] index space is head r / T, position r % T.
+template <typename TIn, int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const BwdArgs a, int rows) {
+  typedef typename In16<TIn>::vec vec;
+  constexpr int kTPR = D / 8;
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  const int row = (int)(gid >> 3);  // rows < 2^31
-  const int part = (int)(gid & 7);
+  const int row = (int)(gid / kTPR);  // rows < 2^31
+  const int part = (int)(gid % kTPR);
   float acc = 0.f;
   if (row < rows) {
     const int hd = row / a.T, t = row - hd * a.T;
-    const bf16* o = static_cast<const bf16*>(a.o) + head_base(a.lo, hd, a.H) + t * a.lo.t;
-    const bf16* dout = static_cast<const bf16*>(a.dout) + head_base(a.ldo, hd, a.H) + t * a.ldo.t;
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + part * 8);
-    const bf16x8 y = *reinterpret_cast<const bf16x8*>(dout + part * 8);
+    const TIn* o = static_cast<const TIn*>(a.o) + head_base(a.lo, hd, a.H) + t * a.lo.t;
+    const TIn* dout = static_cast<const TIn*>(a.dout) + head_base(a.ldo, hd, a.H) + t * a.ldo.t;
+    const vec x = *reinterpret_cast<const vec*>(o + part * 8);
+    const vec y = *reinterpret_cast<const vec*>(dout + part * 8);
     if (a.o_lo) {
-      const bf16* o_lo =
-          static_cast<const bf16*>(a.o_lo) + head_base(a.llo, hd, a.H) + t * a.llo.t;
-      const bf16x8 c = *reinterpret_cast<const bf16x8*>(o_lo + part * 8);
+      const TIn* o_lo =
+          static_cast<const TIn*>(a.o_lo) + head_base(a.llo, hd, a.H) + t * a.llo.t;
+      const vec c = *reinterpret_cast<const vec*>(o_lo + part * 8);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc = fmaf((float)x[i] + (float)c[i], (float)y[i], acc);
     } else {
@@ -81,9 +92,8 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_bf16_kernel(const BwdArgs a
     dst[0] = z;
     dst[1] = z;
   }
-  acc += __shfl_xor(acc, 1, 64);
-  acc += __shfl_xor(acc, 2, 64);
-  acc += __shfl_xor(acc, 4, 64);
+#pragma unroll
+  for (int m = 1; m < kTPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
   if (row < rows && part == 0) a.delta[row] = acc;
 }
 
@@ -92,40 +102,48 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_bf16_kernel(const BwdArgs a
 // T-1, so every address is valid, and nothing is computed from the results);
 // bwd_store_tile, a step later, zeroes rows past T, converts to fp16 and
 // writes the LDS buffers. Only the 256 threads of waves 4..7 take part (tid
-// below is their index 0..255): each moves two 16-byte chunks of Q and of dO
-// (row c/8, dims (c%8)*8 for c = tid, tid+256), and those with tid < 64 also
-// move the LSE and delta of row tid.
+// below is their index 0..255): each moves D/32 16-byte chunks of Q and of
+// dO (row c/(D/8), dims (c%(D/8))*8 for c = tid, tid+256, ...), and those
+// with tid < 64 also move the LSE and delta of row tid.
+template <typename TIn, int D>
 struct TileRegs {
-  bf16x8 q[2], d[2];
+  static constexpr int kN = kBQ * D / 8 / kLoaders;
+  typename In16<TIn>::vec q[kN], d[kN];
   float lse, del;
 };
 
-__device__ __forceinline__ void bwd_load_tile(const bf16* qh, int ldq, const bf16* doh, int lddo,
+template <typename TIn, int D>
+__device__ __forceinline__ void bwd_load_tile(const TIn* qh, int ldq, const TIn* doh, int lddo,
                                               const float* lse, const float* delta, int qs, int T,
-                                              int tid, TileRegs& r) {
+                                              int tid, TileRegs<TIn, D>& r) {
+  typedef typename In16<TIn>::vec vec;
+  constexpr int kC = D / 8;
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
+  for (int p = 0; p < TileRegs<TIn, D>::kN; ++p) {
     const int c = tid + kLoaders * p;
-    const int row = min(qs + (c >> 3), T - 1), col = (c & 7) * 8;
-    r.q[p] = *reinterpret_cast<const bf16x8*>(qh + row * ldq + col);
-    r.d[p] = *reinterpret_cast<const bf16x8*>(doh + row * lddo + col);
+    const int row = min(qs + c / kC, T - 1), col = (c % kC) * 8;
+    r.q[p] = *reinterpret_cast<const vec*>(qh + row * ldq + col);
+    r.d[p] = *reinterpret_cast<const vec*>(doh + row * lddo + col);
   }
   const int row = min(qs + (tid & (kBQ - 1)), T - 1);
   r.lse = lse[row];
   r.del = delta[row];
 }
 
+template <typename TIn, int D>
 __device__ __forceinline__ void bwd_store_tile(f16* sQ, f16* sdO, float* sL, float* sD,
-                                               const TileRegs& r, int qs, int T, int tid) {
+                                               const TileRegs<TIn, D>& r, int qs, int T,
+                                               int tid) {
+  constexpr int kC = D / 8, kRowQ = row_of<D>();
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
+  for (int p = 0; p < TileRegs<TIn, D>::kN; ++p) {
     const int c = tid + kLoaders * p;
-    const int row = c >> 3, col = (c & 7) * 8;
+    const int row = c / kC, col = (c % kC) * 8;
     const bool ok = qs + row < T;
     *reinterpret_cast<f16x8*>(&sQ[row * kRowQ + col]) =
-        ok ? bf16x8_to_f16x8(r.q[p]) : zero_f16x8();
+        ok ? In16<TIn>::to_f16(r.q[p]) : zero_f16x8();
     *reinterpret_cast<f16x8*>(&sdO[row * kRowQ + col]) =
-        ok ? bf16x8_to_f16x8(r.d[p]) : zero_f16x8();
+        ok ? In16<TIn>::to_f16(r.d[p]) : zero_f16x8();
   }
   if (tid < kBQ) {
     const bool ok = qs + tid < T;
@@ -134,7 +152,7 @@ __device__ __forceinline__ void bwd_store_tile(f16* sQ, f16* sdO, float* sL, flo
   }
 }
 
-// P = exp2(S log2(e)/8 - LSE log2(e)) and dS = P (dP - delta) for the 16
+// P = exp2(S s log2(e) - LSE log2(e)) and dS = P (dP - delta) for the 16
 // (query, key) pairs of one lane in one 32x32 block, as fp16. Register
 // 8c + t of half hf is query q0 + 16c + 8hf + t; the lane's key is key0 + l32.
 template <int KIND, bool DROP>
@@ -186,16 +204,22 @@ __device__ __forceinline__ void bwd_p_ds(const f32x16& s, const f32x16& dp, cons
 
 // Row strides inside one head are 32-bit (the host checks T * stride < 2^31);
 // head offsets are 64-bit.
-template <bool DROP>
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(const BwdArgs a,
-                                                                         int n_ktiles, float scale,
-                                                                         float scale_log2) {
+template <typename TIn, int D, bool DROP>
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArgs a, int n_ktiles,
+                                                                    float scale,
+                                                                    float scale_log2) {
+  typedef typename In16<TIn>::vec vec;
+  constexpr int kRowQ = row_of<D>();
+  constexpr int kDB = D / 32;          // 32-wide dimension blocks
+  constexpr int kBlk = 2 * kDB;        // 32x32 blocks of a tile's dQ
+  constexpr int kParts = 8 / kBlk;     // key parts per block (one wave each)
+  constexpr int kSteps = kBK / 16 / kParts;  // 16-key MFMA steps per part
   // All tiles fp16, row-major; transposed operands come from lds_operand_tr.
   __shared__ __attribute__((aligned(16))) f16 sK[kBK * kRowQ];          // [key][d]
   __shared__ __attribute__((aligned(16))) f16 sQ[2][kBQ * kRowQ];       // [q][d]
   __shared__ __attribute__((aligned(16))) f16 sdO[2][kBQ * kRowQ];      // [q][d]
-  __shared__ __attribute__((aligned(16))) f16 sdS[kBK * kRowQ];         // [key][q]
-  __shared__ __attribute__((aligned(16))) float sPart[4][16][64];       // dQ half sums
+  __shared__ __attribute__((aligned(16))) f16 sdS[kBK * kRowS];         // [key][q]
+  __shared__ __attribute__((aligned(16))) float sPart[(kParts - 1) * kBlk][16][64];  // partial dQ
   __shared__ __attribute__((aligned(16))) float sL[2][kBQ];             // LSE * log2(e)
   __shared__ __attribute__((aligned(16))) float sD[2][kBQ];             // delta
   __shared__ __attribute__((aligned(16))) uint16_t sMask[DROP ? 8 : 1][DROP ? 32 * kRowM : 8];
@@ -208,17 +232,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(const B
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
-  // Waves 4..7 load the query tiles; waves 0..3 issue the dQ atomics. No wave
-  // does both, so a wait for a prefetched tile never waits on atomics too.
+  // Waves 4..7 load the query tiles; the waves of key part 0 (0 .. kBlk-1)
+  // issue the dQ atomics. No wave does both, so a wait for a prefetched tile
+  // never waits on atomics too.
   const bool loader = wave >= 4;
   const int ltid = tid - kLoaders;
 
   const size_t roff = (size_t)tm.head * (size_t)T;
-  const bf16* __restrict__ qh = static_cast<const bf16*>(a.q) + head_base(a.lq, tm.head, a.H);
-  const bf16* __restrict__ kh = static_cast<const bf16*>(a.k) + head_base(a.lk, tm.head, a.H);
-  const bf16* __restrict__ vh = static_cast<const bf16*>(a.v) + head_base(a.lv, tm.head, a.H);
-  const bf16* __restrict__ doh =
-      static_cast<const bf16*>(a.dout) + head_base(a.ldo, tm.head, a.H);
+  const TIn* __restrict__ qh = static_cast<const TIn*>(a.q) + head_base(a.lq, tm.head, a.H);
+  const TIn* __restrict__ kh = static_cast<const TIn*>(a.k) + head_base(a.lk, tm.head, a.H);
+  const TIn* __restrict__ vh = static_cast<const TIn*>(a.v) + head_base(a.lv, tm.head, a.H);
+  const TIn* __restrict__ doh = static_cast<const TIn*>(a.dout) + head_base(a.ldo, tm.head, a.H);
   const int ldq = (int)a.lq.t, ldk = (int)a.lk.t, ldv = (int)a.lv.t, lddo = (int)a.ldo.t;
   const float* lseh = a.lse + roff;
   const float* delh = a.delta + roff;
@@ -228,36 +252,42 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(const B
   const int my_key = kw0 + l32;  // the key column this lane owns
 
   // K and V of this wave's 32 keys as fp16 B operands (lane: its key, 8 dims).
-  f16x8 kf[4], vf[4];
+  f16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    kf[kk] = bf16x8_to_f16x8(
-        load_bf16x8(kh + my_key * ldk + kk * 16 + 8 * hf, my_key < T));
-    vf[kk] = bf16x8_to_f16x8(
-        load_bf16x8(vh + my_key * ldv + kk * 16 + 8 * hf, my_key < T));
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const bool ok = my_key < T;
+    kf[kk] = ok ? In16<TIn>::to_f16(*reinterpret_cast<const vec*>(kh + my_key * ldk + kk * 16 +
+                                                                  8 * hf))
+                : zero_f16x8();
+    vf[kk] = ok ? In16<TIn>::to_f16(*reinterpret_cast<const vec*>(vh + my_key * ldv + kk * 16 +
+                                                                  8 * hf))
+                : zero_f16x8();
   }
   // All 256 keys of K, row-major fp16, for the dQ product.
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int c = tid + kThreads * p;  // 0..2047: key c/8, 8 dims at (c%8)*8
-    const int row = c >> 3, col = (c & 7) * 8;
-    *reinterpret_cast<f16x8*>(&sK[row * kRowQ + col]) = bf16x8_to_f16x8(
-        load_bf16x8(kh + (k0 + row) * ldk + col, k0 + row < T));
+  for (int p = 0; p < kBK * D / 8 / kThreads; ++p) {
+    constexpr int kC = D / 8;
+    const int c = tid + kThreads * p;  // key c/kC, 8 dims at (c%kC)*8
+    const int row = c / kC, col = (c % kC) * 8;
+    *reinterpret_cast<f16x8*>(&sK[row * kRowQ + col]) =
+        k0 + row < T ? In16<TIn>::to_f16(*reinterpret_cast<const vec*>(kh + (k0 + row) * ldk +
+                                                                        col))
+                     : zero_f16x8();
   }
 
-  f32x16 dvacc[2], dkacc[2];
+  f32x16 dvacc[kDB], dkacc[kDB];
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
+  for (int db = 0; db < kDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       dvacc[db][r] = 0.f;
       dkacc[db][r] = 0.f;
     }
 
-  TileRegs nxt;
+  TileRegs<TIn, D> nxt;
   if (loader) {
-    bwd_load_tile(qh, ldq, doh, lddo, lseh, delh, k0, T, ltid, nxt);
-    bwd_store_tile(sQ[0], sdO[0], sL[0], sD[0], nxt, k0, T, ltid);
+    bwd_load_tile<TIn, D>(qh, ldq, doh, lddo, lseh, delh, k0, T, ltid, nxt);
+    bwd_store_tile<TIn, D>(sQ[0], sdO[0], sL[0], sD[0], nxt, k0, T, ltid);
   }
   __syncthreads();
 
@@ -265,7 +295,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(const B
   for (int qs = k0; qs < T; qs += kBQ, buf ^= 1) {
     // Prefetch the next tile into registers while this one is computed.
     const bool has_next = qs + kBQ < T;
-    if (loader && has_next) bwd_load_tile(qh, ldq, doh, lddo, lseh, delh, qs + kBQ, T, ltid, nxt);
+    if (loader && has_next)
+      bwd_load_tile<TIn, D>(qh, ldq, doh, lddo, lseh, delh, qs + kBQ, T, ltid, nxt);
 
     const f16* cQ = sQ[buf];
     const f16* cdO = sdO[buf];
@@ -302,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(const B
         }
         const int arow = (mb * 32 + perm32(l32)) * kRowQ + 8 * hf;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < D / 16; ++kk) {
           s = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cQ[arow + kk * 16]), kf[kk], s);
           dp = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cdO[arow + kk * 16]), vf[kk],
                                 dp);
@@ -330,12 +361,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(const B
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         // dS^T row of this lane's key: 8 consecutive queries, one 16-byte write.
-        *reinterpret_cast<f16x8*>(&sdS[(wave * 32 + l32) * kRowQ + mb * 32 + 16 * c + 8 * hf]) =
+        *reinterpret_cast<f16x8*>(&sdS[(wave * 32 + l32) * kRowS + mb * 32 + 16 * c + 8 * hf]) =
             dsf[c];
         // dV^T += dO^T P and dK^T += Q^T dS over these 16 queries.
         const int ks = 2 * mb + c;
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
+        for (int db = 0; db < kDB; ++db) {
           dvacc[db] = mfma32x32x16_f16(lds_operand_tr(cdO, kRowQ, ks * 16, db * 32, lane), pf[c],
                                        dvacc[db]);
           dkacc[db] = mfma32x32x16_f16(lds_operand_tr(cQ, kRowQ, ks * 16, db * 32, lane), dsf[c],
@@ -346,36 +377,39 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(const B
     // Stage the prefetched tile into the other buffer, last read in the
     // previous step before its first barrier.
     if (loader && has_next)
-      bwd_store_tile(sQ[buf ^ 1], sdO[buf ^ 1], sL[buf ^ 1], sD[buf ^ 1], nxt, qs + kBQ, T, ltid);
+      bwd_store_tile<TIn, D>(sQ[buf ^ 1], sdO[buf ^ 1], sL[buf ^ 1], sD[buf ^ 1], nxt, qs + kBQ,
+                             T, ltid);
     __syncthreads();
 
-    // dQ of the 64-query tile = dS K over the 256 keys, as four 32x32 blocks
-    // (queries 32qb.., dims 32db..). Wave w takes block w % 4 over key half
-    // w / 4 (8 steps of 16 keys); waves 4..7 pass their half sums to waves
-    // 0..3 through LDS, which add them into dQ with atomics. Every wave wrote
-    // its dS rows (zeros where nothing is visible).
-    const int blk = wave & 3, khalf = wave >> 2;
-    const int qb = blk >> 1, db = blk & 1;
+    // dQ of the 64-query tile = dS K over the 256 keys, as kBlk 32x32 blocks
+    // (queries 32qb.., dims 32db..). Wave w takes block w % kBlk over key
+    // part w / kBlk (kSteps steps of 16 keys); the other parts pass their sums
+    // to part 0 through LDS, whose waves add the total into dQ with atomics.
+    // Every wave wrote its dS rows (zeros where nothing is visible).
+    const int blk = wave % kBlk, kpart = wave / kBlk;
+    const int qb = blk / kDB, db = blk % kDB;
     const int qb0 = qs + qb * 32;
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
     if (qb0 < T) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int ks = 8 * khalf + j;
-        acc = mfma32x32x16_f16(lds_operand_tr(sdS, kRowQ, ks * 16, qb * 32, lane),
+      for (int j = 0; j < kSteps; ++j) {
+        const int ks = kSteps * kpart + j;
+        acc = mfma32x32x16_f16(lds_operand_tr(sdS, kRowS, ks * 16, qb * 32, lane),
                                lds_operand_tr(sK, kRowQ, ks * 16, db * 32, lane), acc);
       }
-      if (khalf == 1) {
+      if (kpart > 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sPart[blk][r][lane] = acc[r];
+        for (int r = 0; r < 16; ++r) sPart[(kpart - 1) * kBlk + blk][r][lane] = acc[r];
       }
     }
     __syncthreads();
-    if (khalf == 0 && qb0 < T) {
+    if (kpart == 0 && qb0 < T) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] += sPart[blk][r][lane];
+      for (int p = 0; p < kParts - 1; ++p)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] += sPart[p * kBlk + blk][r][lane];
       const int lddq = (int)a.ldq.t;
       float* dqh = a.dq + head_base(a.ldq, tm.head, a.H) + qb0 * lddq + db * 32 + l32;
       if (qb0 + 32 <= T) {
@@ -399,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(const B
     float* dvr = a.dv + head_base(a.ldv, tm.head, a.H) + my_key * a.ldv.t;
     float* dkr = a.dk + head_base(a.ldk, tm.head, a.H) + my_key * a.ldk.t;
 #pragma unroll
-    for (int db2 = 0; db2 < 2; ++db2)
+    for (int db2 = 0; db2 < kDB; ++db2)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = db2 * 32 + 8 * g + 4 * hf;
@@ -414,26 +448,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_bf16_kernel(const B
   }
 }
 
-}  // namespace
-
-hipError_t launch_bwd_prep_bf16(const BwdArgs& a, hipStream_t stream) {
+template <typename TIn, int D>
+hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
   const int rows = a.n_heads * a.T;
-  const unsigned prep_blocks = (unsigned)(((long long)rows * 8 + 255) / 256);
-  hipLaunchKernelGGL(attn_bwd_prep_bf16_kernel, dim3(prep_blocks), dim3(256), 0, stream, a, rows);
+  const unsigned blocks = (unsigned)(((long long)rows * (D / 8) + 255) / 256);
+  hipLaunchKernelGGL((attn_bwd_prep_kernel<TIn, D>), dim3(blocks), dim3(256), 0, stream, a, rows);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_main_bf16(const BwdArgs& a, hipStream_t stream) {
+template <typename TIn, int D>
+hipError_t launch_main(const BwdArgs& a, hipStream_t stream) {
   const int n_ktiles = (a.T + kBK - 1) / kBK;
-  const float scale = 0.125f;  // 1/sqrt(64)
+  const float scale = 1.f / __builtin_sqrtf((float)D);
   const dim3 grid(tiled_grid(a.n_heads, n_ktiles));
   if (a.drop.thr != 0)
-    hipLaunchKernelGGL(attn_bwd_main_bf16_kernel<true>, grid, dim3(kThreads), 0, stream, a,
+    hipLaunchKernelGGL((attn_bwd_main_kernel<TIn, D, true>), grid, dim3(kThreads), 0, stream, a,
                        n_ktiles, scale, scale * kLog2e);
   else
-    hipLaunchKernelGGL(attn_bwd_main_bf16_kernel<false>, grid, dim3(kThreads), 0, stream, a,
+    hipLaunchKernelGGL((attn_bwd_main_kernel<TIn, D, false>), grid, dim3(kThreads), 0, stream, a,
                        n_ktiles, scale, scale * kLog2e);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_prep_16(const BwdArgs& a, bool fp16, int D, hipStream_t stream) {
+  if (fp16) return D == 32 ? launch_prep<f16, 32>(a, stream) : launch_prep<f16, 64>(a, stream);
+  return D == 32 ? launch_prep<bf16, 32>(a, stream) : launch_prep<bf16, 64>(a, stream);
+}
+
+hipError_t launch_bwd_main_16(const BwdArgs& a, bool fp16, int D, hipStream_t stream) {
+  if (fp16) return D == 32 ? launch_main<f16, 32>(a, stream) : launch_main<f16, 64>(a, stream);
+  return D == 32 ? launch_main<bf16, 32>(a, stream) : launch_main<bf16, 64>(a, stream);
 }
 
 }  // namespace gpt_attn

@@ -135,6 +135,38 @@ __device__ __forceinline__ f16x8 zero_f16x8() {
   return __builtin_bit_cast(f16x8, z);
 }
 
+// The two 16-bit input types of the MFMA kernels. vec is eight elements (one
+// 16-byte load); mfma is the 32x32x16 product of two such operands with fp32
+// accumulation; to_f16 converts for the products that run in fp16 (exact for
+// bf16 in fp16's normal range, the identity for fp16); round rounds an fp32
+// value to the type (nearest even).
+template <typename T>
+struct In16;
+
+template <>
+struct In16<bf16> {
+  typedef bf16x8 vec;
+  typedef bf16x4 vec4;
+  __device__ static __forceinline__ f32x16 mfma(vec a, vec b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f16x8 to_f16(vec x) { return bf16x8_to_f16x8(x); }
+  __device__ static __forceinline__ vec zero() { return zero_bf16x8(); }
+  __device__ static __forceinline__ bf16 round(float x) { return (bf16)x; }
+};
+
+template <>
+struct In16<f16> {
+  typedef f16x8 vec;
+  typedef f16x4 vec4;
+  __device__ static __forceinline__ f32x16 mfma(vec a, vec b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f16x8 to_f16(vec x) { return x; }
+  __device__ static __forceinline__ vec zero() { return zero_f16x8(); }
+  __device__ static __forceinline__ f16 round(float x) { return (f16)x; }
+};
+
 // ds_read_b64_tr_b16 (CDNA4): each lane supplies the LDS address of four
 // consecutive 16-bit elements; inside every group of 16 lanes the 16 x 4
 // block is transposed, so that lane i of the group receives element i of the

@@ -1,22 +1,24 @@
-// One query per (sequence, head) against a key/value cache, for gfx950.
+// One query per (sequence, head) against a key/value cache, for gfx950:
+// bf16, fp16 or fp32 inputs, head dim D in {32, 64}.
 //
 // Sampling feeds the sequence back one position at a time (generate(), page
 // "nanoGPT: a real GPT in two 300-line files", section 2 "How the code
 // works"); the newest query attends to every cached key up to and including
 // its own position, which is the last row of the causal forward:
-//   O = softmax(q K^T / sqrt(64)) V over the first n cache rows, LSE = ln sum.
+//   O = softmax(q K^T / sqrt(D)) V over the first n cache rows, LSE = ln sum.
 // With one query there is no matrix product to feed the matrix cores: the
 // work is two passes over the cache (K, V: 256 bytes per key in bf16) at four
 // FLOPs per byte, so it is bound by HBM bandwidth, and the kernels are shaped
 // for coalesced streaming and enough bytes in flight, not for MFMA.
 //
 // Split kernel: the cache rows of a head are cut into chunks; a workgroup
-// of 256 threads owns one (head, chunk). Eight lanes share a key: each loads
-// 16 bytes of the key's K and V rows (one 128-byte row per 8 lanes, so a
-// wave reads 8 whole rows per load), forms its partial dot product with its
-// 8 elements of q and completes it with three lane exchanges. The 32 key
+// of 256 threads owns one (head, chunk). D/8 lanes share a key: each loads
+// 8 elements of the key's K and V rows (a whole row per D/8 lanes, so every
+// load of a wave covers whole rows), forms its partial dot product with its
+// 8 elements of q and completes it with lane exchanges. The 256/(D/8) key
 // groups of the workgroup each run an online softmax (base 2, fp32) over
-// every 32nd key of the chunk, 4 keys per step with all loads issued first;
+// every group-count-th key of the chunk, 4 keys per step with all loads
+// issued first;
 // the group states meet in LDS and the chunk's unnormalized O with its
 // running max and sum goes to the workspace. Merge kernel: one wave per head
 // combines the chunks with the log-sum-exp rule and writes O and LSE.
@@ -27,7 +29,6 @@ namespace gpt_attn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kGroups = kThreads / 8;  // keys in flight per step per workgroup
 constexpr int kUnroll = 4;             // keys per group per step
 
 // Raw 8-element row pieces: loaded first, converted when used.
@@ -37,6 +38,12 @@ template <>
 struct Raw8<bf16> {
   bf16x8 x;
   __device__ __forceinline__ void load(const bf16* p) { x = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ float operator[](int t) const { return (float)x[t]; }
+};
+template <>
+struct Raw8<f16> {
+  f16x8 x;
+  __device__ __forceinline__ void load(const f16* p) { x = *reinterpret_cast<const f16x8*>(p); }
   __device__ __forceinline__ float operator[](int t) const { return (float)x[t]; }
 };
 template <>
@@ -54,12 +61,14 @@ __device__ __forceinline__ int cache_length(const DecArgs& a, int head) {
   return min(max(n, 0), a.L);
 }
 
-template <typename TIn>
+template <typename TIn, int D>
 __global__ __launch_bounds__(kThreads) void attn_decode_split_kernel(const DecArgs a, int chunk,
                                                                      int n_chunks,
                                                                      float scale_log2) {
+  constexpr int kLanes = D / 8;                 // lanes per key
+  constexpr int kGroups = kThreads / kLanes;    // keys in flight per step per workgroup
   __shared__ float s_m[kGroups], s_l[kGroups];
-  __shared__ __attribute__((aligned(16))) float s_acc[kGroups][kHeadDim + 4];
+  __shared__ __attribute__((aligned(16))) float s_acc[kGroups][D + 4];
 
   const int head = blockIdx.x / n_chunks;  // flat b*H + h
   const int c = blockIdx.x - head * n_chunks;
@@ -68,12 +77,12 @@ __global__ __launch_bounds__(kThreads) void attn_decode_split_kernel(const DecAr
   float* part = a.part + ((size_t)head * n_chunks + c) * kDecPart;
   const int tid = threadIdx.x;
   if (kb >= ke) {  // nothing cached here: an empty partial (workgroup-uniform)
-    if (tid < kHeadDim) part[tid] = 0.f;
-    if (tid == kHeadDim) part[kHeadDim] = -INFINITY;
-    if (tid == kHeadDim + 1) part[kHeadDim + 1] = 0.f;
+    if (tid < D) part[tid] = 0.f;
+    if (tid == kDecMax) part[kDecMax] = -INFINITY;
+    if (tid == kDecSum) part[kDecSum] = 0.f;
     return;
   }
-  const int sub = tid & 7, grp = tid >> 3;
+  const int sub = tid % kLanes, grp = tid / kLanes;
   const TIn* qh = static_cast<const TIn*>(a.q) + head_base(a.lq, head, a.H);
   const TIn* kh = static_cast<const TIn*>(a.k) + head_base(a.lk, head, a.H) + sub * 8;
   const TIn* vh = static_cast<const TIn*>(a.v) + head_base(a.lv, head, a.H) + sub * 8;
@@ -106,9 +115,8 @@ __global__ __launch_bounds__(kThreads) void attn_decode_split_kernel(const DecAr
       float d = 0.f;
 #pragma unroll
       for (int t = 0; t < 8; ++t) d = fmaf(qv[t], kr[u][t], d);
-      d += __shfl_xor(d, 1, 64);
-      d += __shfl_xor(d, 2, 64);
-      d += __shfl_xor(d, 4, 64);
+#pragma unroll
+      for (int msk = 1; msk < kLanes; msk <<= 1) d += __shfl_xor(d, msk, 64);
       s[u] = key0 + u * kGroups < ke ? d : -INFINITY;
       mx = fmaxf(mx, s[u]);
     }
@@ -134,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void attn_decode_split_kernel(const DecAr
 #pragma unroll
   for (int t = 0; t < 8; ++t) s_acc[grp][sub * 8 + t] = acc[t];
   __syncthreads();
-  if (tid < kHeadDim) {
+  if (tid < D) {
     // Groups that saw no key hold m = -inf and contribute exp2(-inf) = 0.
     float M = s_m[0];
     for (int g = 1; g < kGroups; ++g) M = fmaxf(M, s_m[g]);
@@ -146,8 +154,8 @@ __global__ __launch_bounds__(kThreads) void attn_decode_split_kernel(const DecAr
     }
     part[tid] = O;
     if (tid == 0) {
-      part[kHeadDim] = M;
-      part[kHeadDim + 1] = L;
+      part[kDecMax] = M;
+      part[kDecSum] = L;
     }
   }
 }
@@ -159,13 +167,17 @@ __device__ __forceinline__ void store_out<bf16>(bf16* p, float x) {
   *p = (bf16)x;
 }
 template <>
+__device__ __forceinline__ void store_out<f16>(f16* p, float x) {
+  *p = (f16)x;
+}
+template <>
 __device__ __forceinline__ void store_out<float>(float* p, float x) {
   *p = x;
 }
 
-template <typename TOut>
-__global__ __launch_bounds__(64) void attn_decode_merge_kernel(const DecArgs a, int chunk,
-                                                               int n_chunks) {
+template <typename TOut, int D>
+__global__ __launch_bounds__(D) void attn_decode_merge_kernel(const DecArgs a, int chunk,
+                                                              int n_chunks) {
   const int head = blockIdx.x;
   const int d = threadIdx.x;
   const int n = cache_length(a, head);
@@ -178,41 +190,44 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(const DecArgs a, 
   const int nc = (n + chunk - 1) / chunk;
   const float* part = a.part + (size_t)head * n_chunks * kDecPart;
   float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, part[c * kDecPart + kHeadDim]);
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, part[c * kDecPart + kDecMax]);
   float L = 0.f, O = 0.f;
   for (int c = 0; c < nc; ++c) {
-    const float w = fast_exp2(part[c * kDecPart + kHeadDim] - M);
-    L = fmaf(part[c * kDecPart + kHeadDim + 1], w, L);
+    const float w = fast_exp2(part[c * kDecPart + kDecMax] - M);
+    L = fmaf(part[c * kDecPart + kDecSum], w, L);
     O = fmaf(part[c * kDecPart + d], w, O);
   }
   store_out<TOut>(oh + d, O / L);
   if (d == 0) a.lse[head] = (M + fast_log2(L)) * kLn2;
 }
 
-template <typename T>
+template <typename T, int D>
 hipError_t launch_decode(const DecArgs& a, hipStream_t stream) {
   const int chunk = decode_chunk(a.n_heads, a.L);
   const int n_chunks = (a.L + chunk - 1) / chunk;
-  const float scale_log2 = 0.125f * kLog2e;  // 1/sqrt(64) * log2(e)
+  const float scale_log2 = kLog2e / __builtin_sqrtf((float)D);  // 1/sqrt(D) * log2(e)
   if (n_chunks > 0) {  // L = 0: every length is 0 and the merge writes O = 0
-    hipLaunchKernelGGL(attn_decode_split_kernel<T>, dim3((unsigned)(a.n_heads * n_chunks)),
+    hipLaunchKernelGGL((attn_decode_split_kernel<T, D>), dim3((unsigned)(a.n_heads * n_chunks)),
                        dim3(kThreads), 0, stream, a, chunk, n_chunks, scale_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(attn_decode_merge_kernel<T>, dim3((unsigned)a.n_heads), dim3(64), 0, stream,
-                     a, chunk, n_chunks);
+  hipLaunchKernelGGL((attn_decode_merge_kernel<T, D>), dim3((unsigned)a.n_heads), dim3(D), 0,
+                     stream, a, chunk, n_chunks);
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_decode_d(const DecArgs& a, int D, hipStream_t stream) {
+  return D == 32 ? launch_decode<T, 32>(a, stream) : launch_decode<T, 64>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecArgs& a, hipStream_t stream) {
-  return launch_decode<bf16>(a, stream);
-}
-
-hipError_t launch_decode_f32(const DecArgs& a, hipStream_t stream) {
-  return launch_decode<float>(a, stream);
+hipError_t launch_decode(const DecArgs& a, int dtype_code, int D, hipStream_t stream) {
+  if (dtype_code == 1) return launch_decode_d<bf16>(a, D, stream);
+  if (dtype_code == 2) return launch_decode_d<f16>(a, D, stream);
+  return launch_decode_d<float>(a, D, stream);
 }
 
 }  // namespace gpt_attn

@@ -1,4 +1,5 @@
-// Causal attention forward and backward in fp32, head dim 64, for gfx950.
+// Causal attention forward and backward in fp32, head dim D in {32, 64}, for
+// gfx950.
 //
 // The fp32 path serves the small fp32 workload (the Shakespeare-char "baby
 // GPT" layer: 6 heads, block size 256) where the tolerance is 1e-5 max-abs,
@@ -24,8 +25,6 @@
 namespace gpt_attn {
 namespace {
 
-constexpr int kD = kHeadDim;
-
 // Keep bit of key 8*group + t from keep_mask8's words.
 __device__ __forceinline__ bool kept_bit(const uint32_t (&m)[4], int t) {
   return (m[t >> 1] >> (16 * (t & 1))) & 1u;
@@ -38,6 +37,7 @@ __device__ __forceinline__ float* fptr_w(void* base, const Layout& L, int hd, in
   return static_cast<float*>(base) + head_base(L, hd, H);
 }
 
+template <int kD>
 __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const FwdArgs a, int n_tiles,
                                                           float scale) {
   __shared__ float Ks[64 * kD];
@@ -108,10 +108,12 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const FwdArgs a, int n
 }
 
 // Eight threads per (head, row); row r of [B*H, T] is head r / T, position r % T.
+template <int kD>
 __global__ __launch_bounds__(256) void attn_bwd_prep_f32_kernel(const BwdArgs a, int rows) {
+  constexpr int kTPR = kD / 8;  // threads per row, 8 elements each
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  const int row = (int)(gid >> 3);
-  const int part = (int)(gid & 7);
+  const int row = (int)(gid / kTPR);
+  const int part = (int)(gid % kTPR);
   float acc = 0.f;
   if (row < rows) {
     const int hd = row / a.T, t = row - hd * a.T;
@@ -120,15 +122,16 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_f32_kernel(const BwdArgs a,
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf(o[e], dout[e], acc);
   }
-  acc += __shfl_xor(acc, 1, 64);
-  acc += __shfl_xor(acc, 2, 64);
-  acc += __shfl_xor(acc, 4, 64);
+#pragma unroll
+  for (int m = 1; m < kTPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
   if (row < rows && part == 0) a.delta[row] = acc;
 }
 
-// dK, dV: thread pair (key j, half) holds 32 dims of K_j, V_j, dK_j, dV_j.
+// dK, dV: thread pair (key j, half) holds D/2 dims of K_j, V_j, dK_j, dV_j.
+template <int kD>
 __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(const BwdArgs a, int n_tiles,
                                                                float scale) {
+  constexpr int kH = kD / 2;
   __shared__ float Qs[32 * kD];
   __shared__ float dOs[32 * kD];
   __shared__ float lses[32];
@@ -147,11 +150,11 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(const BwdArgs a, 
   const bool drop = a.drop.thr != 0;
   const float zs = drop ? a.drop.scale : 1.f;
 
-  float kr[32], vr[32], dka[32], dva[32];
+  float kr[kH], vr[kH], dka[kH], dva[kH];
 #pragma unroll
-  for (int d = 0; d < 32; ++d) {
-    kr[d] = j < T ? kh[j * a.lk.t + half * 32 + d] : 0.f;
-    vr[d] = j < T ? vh[j * a.lv.t + half * 32 + d] : 0.f;
+  for (int d = 0; d < kH; ++d) {
+    kr[d] = j < T ? kh[j * a.lk.t + half * kH + d] : 0.f;
+    vr[d] = j < T ? vh[j * a.lv.t + half * kH + d] : 0.f;
     dka[d] = 0.f;
     dva[d] = 0.f;
   }
@@ -173,9 +176,9 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(const BwdArgs a, 
       const int i = qs + ii;
       float s = 0.f, dp = 0.f;
 #pragma unroll
-      for (int d = 0; d < 32; ++d) {
-        s = fmaf(Qs[ii * kD + half * 32 + d], kr[d], s);
-        dp = fmaf(dOs[ii * kD + half * 32 + d], vr[d], dp);
+      for (int d = 0; d < kH; ++d) {
+        s = fmaf(Qs[ii * kD + half * kH + d], kr[d], s);
+        dp = fmaf(dOs[ii * kD + half * kH + d], vr[d], dp);
       }
       s += __shfl_xor(s, 1, 64);
       dp += __shfl_xor(dp, 1, 64);
@@ -190,27 +193,29 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(const BwdArgs a, 
         const float ds = p * ((kept ? dp * zs : 0.f) - dels[ii]);
         const float pd = kept ? p : 0.f;
 #pragma unroll
-        for (int d = 0; d < 32; ++d) {
-          dva[d] = fmaf(pd, dOs[ii * kD + half * 32 + d], dva[d]);
-          dka[d] = fmaf(ds, Qs[ii * kD + half * 32 + d], dka[d]);
+        for (int d = 0; d < kH; ++d) {
+          dva[d] = fmaf(pd, dOs[ii * kD + half * kH + d], dva[d]);
+          dka[d] = fmaf(ds, Qs[ii * kD + half * kH + d], dka[d]);
         }
       }
     }
   }
   if (j < T) {
-    float* dkr = fptr_w(a.dk, a.ldk, head, a.H) + j * a.ldk.t + half * 32;
-    float* dvr = fptr_w(a.dv, a.ldv, head, a.H) + j * a.ldv.t + half * 32;
+    float* dkr = fptr_w(a.dk, a.ldk, head, a.H) + j * a.ldk.t + half * kH;
+    float* dvr = fptr_w(a.dv, a.ldv, head, a.H) + j * a.ldv.t + half * kH;
 #pragma unroll
-    for (int d = 0; d < 32; ++d) {
+    for (int d = 0; d < kH; ++d) {
       dkr[d] = dka[d] * scale;
       dvr[d] = dva[d] * zs;
     }
   }
 }
 
-// dQ: thread pair (query i, half) holds 32 dims of Q_i, dO_i, dQ_i.
+// dQ: thread pair (query i, half) holds D/2 dims of Q_i, dO_i, dQ_i.
+template <int kD>
 __global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(const BwdArgs a, int n_tiles,
                                                              float scale) {
+  constexpr int kH = kD / 2;
   __shared__ float Ks[32 * kD];
   __shared__ float Vs[32 * kD];
   const int T = a.T;
@@ -225,11 +230,11 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(const BwdArgs a, in
   const float* doh = fptr(a.dout, a.ldo, head, a.H);
   const size_t roff = (size_t)head * T;
 
-  float qr[32], dor[32], dqa[32];
+  float qr[kH], dor[kH], dqa[kH];
 #pragma unroll
-  for (int d = 0; d < 32; ++d) {
-    qr[d] = i < T ? qh[i * a.lq.t + half * 32 + d] : 0.f;
-    dor[d] = i < T ? doh[i * a.ldo.t + half * 32 + d] : 0.f;
+  for (int d = 0; d < kH; ++d) {
+    qr[d] = i < T ? qh[i * a.lq.t + half * kH + d] : 0.f;
+    dor[d] = i < T ? doh[i * a.ldo.t + half * kH + d] : 0.f;
     dqa[d] = 0.f;
   }
   const bool drop = a.drop.thr != 0;
@@ -252,9 +257,9 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(const BwdArgs a, in
       if (drop && (jj & 7) == 0) keep_mask8(a.drop, head, i, (uint32_t)j >> 3, km);
       float s = 0.f, dp = 0.f;
 #pragma unroll
-      for (int d = 0; d < 32; ++d) {
-        s = fmaf(qr[d], Ks[jj * kD + half * 32 + d], s);
-        dp = fmaf(dor[d], Vs[jj * kD + half * 32 + d], dp);
+      for (int d = 0; d < kH; ++d) {
+        s = fmaf(qr[d], Ks[jj * kD + half * kH + d], s);
+        dp = fmaf(dor[d], Vs[jj * kD + half * kH + d], dp);
       }
       s += __shfl_xor(s, 1, 64);
       dp += __shfl_xor(dp, 1, 64);
@@ -262,14 +267,14 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(const BwdArgs a, in
         const float p = expf(s * scale - lse_i);
         const float ds = p * ((kept_bit(km, jj & 7) ? dp * zs : 0.f) - del_i);
 #pragma unroll
-        for (int d = 0; d < 32; ++d) dqa[d] = fmaf(ds, Ks[jj * kD + half * 32 + d], dqa[d]);
+        for (int d = 0; d < kH; ++d) dqa[d] = fmaf(ds, Ks[jj * kD + half * kH + d], dqa[d]);
       }
     }
   }
   if (i < T) {
-    float* dqr = fptr_w(a.dq, a.ldq, head, a.H) + i * a.ldq.t + half * 32;
+    float* dqr = fptr_w(a.dq, a.ldq, head, a.H) + i * a.ldq.t + half * kH;
 #pragma unroll
-    for (int d = 0; d < 32; ++d) dqr[d] = dqa[d] * scale;
+    for (int d = 0; d < kH; ++d) dqr[d] = dqa[d] * scale;
   }
 }
 
@@ -303,28 +308,49 @@ hipError_t launch_dropout_mask(const Dropout& d, int n_heads, int T, uint8_t* ma
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
+namespace {
+
+template <int D>
+hipError_t fwd_f32(const FwdArgs& a, hipStream_t stream) {
   const int n_tiles = (a.T + 63) / 64;
-  hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3((unsigned)a.n_heads * n_tiles), dim3(64), 0,
-                     stream, a, n_tiles, 0.125f);
+  hipLaunchKernelGGL(attn_fwd_f32_kernel<D>, dim3((unsigned)a.n_heads * n_tiles), dim3(64), 0,
+                     stream, a, n_tiles, 1.f / __builtin_sqrtf((float)D));
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_prep_f32(const BwdArgs& a, hipStream_t stream) {
+template <int D>
+hipError_t prep_f32(const BwdArgs& a, hipStream_t stream) {
   const int rows = a.n_heads * a.T;
-  hipLaunchKernelGGL(attn_bwd_prep_f32_kernel, dim3((unsigned)(((long long)rows * 8 + 255) / 256)),
-                     dim3(256), 0, stream, a, rows);
+  hipLaunchKernelGGL(attn_bwd_prep_f32_kernel<D>,
+                     dim3((unsigned)(((long long)rows * (D / 8) + 255) / 256)), dim3(256), 0,
+                     stream, a, rows);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_main_f32(const BwdArgs& a, hipStream_t stream) {
+template <int D>
+hipError_t main_f32(const BwdArgs& a, hipStream_t stream) {
   const int n_tiles = (a.T + 31) / 32;
   const dim3 grid((unsigned)a.n_heads * n_tiles);
-  hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel, grid, dim3(64), 0, stream, a, n_tiles, 0.125f);
+  const float scale = 1.f / __builtin_sqrtf((float)D);
+  hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<D>, grid, dim3(64), 0, stream, a, n_tiles, scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dq_f32_kernel, grid, dim3(64), 0, stream, a, n_tiles, 0.125f);
+  hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<D>, grid, dim3(64), 0, stream, a, n_tiles, scale);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(const FwdArgs& a, int D, hipStream_t stream) {
+  return D == 32 ? fwd_f32<32>(a, stream) : fwd_f32<64>(a, stream);
+}
+
+hipError_t launch_bwd_prep_f32(const BwdArgs& a, int D, hipStream_t stream) {
+  return D == 32 ? prep_f32<32>(a, stream) : prep_f32<64>(a, stream);
+}
+
+hipError_t launch_bwd_main_f32(const BwdArgs& a, int D, hipStream_t stream) {
+  return D == 32 ? main_f32<32>(a, stream) : main_f32<64>(a, stream);
 }
 
 }  // namespace gpt_attn

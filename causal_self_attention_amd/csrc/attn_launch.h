@@ -102,7 +102,9 @@ struct DecArgs {
   int n_heads, H, L;
 };
 
-constexpr int kDecPart = 68;  // 64 partial outputs, max, sum, 2 floats of padding
+// One chunk's partial: D (<= 64) unnormalized outputs, then max and sum.
+constexpr int kDecPart = 68;
+constexpr int kDecMax = 64, kDecSum = 65;
 
 // Cache rows per split workgroup: about 2048 workgroups in total, a multiple
 // of 128 keys (one step of the split kernel), between 128 and 1024.
@@ -112,18 +114,20 @@ __host__ __device__ inline int decode_chunk(int n_heads, int L) {
   return (int)(c < 128 ? 128 : (c > 1024 ? 1024 : c));
 }
 
-hipError_t launch_decode_bf16(const DecArgs& a, hipStream_t stream);
-hipError_t launch_decode_f32(const DecArgs& a, hipStream_t stream);
+// dtype_code: 0 fp32, 1 bf16, 2 fp16 (the C ABI's codes); D is 32 or 64.
+hipError_t launch_decode(const DecArgs& a, int dtype_code, int D, hipStream_t stream);
 
 // Keep mask [n_heads, T, T] (uint8, 1 = kept; 0 above the diagonal).
 hipError_t launch_dropout_mask(const Dropout& d, int n_heads, int T, uint8_t* mask,
                                hipStream_t stream);
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_prep_bf16(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_main_bf16(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_prep_f32(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_main_f32(const BwdArgs& a, hipStream_t stream);
+// 16-bit inputs (bf16, or fp16 when fp16 is set) on the matrix cores, and
+// fp32 inputs on the vector ALUs; D is 32 or 64.
+hipError_t launch_fwd_16(const FwdArgs& a, bool fp16, int D, hipStream_t stream);
+hipError_t launch_bwd_prep_16(const BwdArgs& a, bool fp16, int D, hipStream_t stream);
+hipError_t launch_bwd_main_16(const BwdArgs& a, bool fp16, int D, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, int D, hipStream_t stream);
+hipError_t launch_bwd_prep_f32(const BwdArgs& a, int D, hipStream_t stream);
+hipError_t launch_bwd_main_f32(const BwdArgs& a, int D, hipStream_t stream);
 
 }  // namespace gpt_attn

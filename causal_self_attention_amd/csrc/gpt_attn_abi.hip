@@ -21,9 +21,10 @@ struct Shape {
 
 // Shape and dtype checks shared by every entry point.
 int check_shape(int dtype, int B, int H, int T, int D, Shape* s) {
-  if (dtype != GPT_ATTN_F32 && dtype != GPT_ATTN_BF16) return GPT_ATTN_E_INVAL;
+  if (dtype != GPT_ATTN_F32 && dtype != GPT_ATTN_BF16 && dtype != GPT_ATTN_F16)
+    return GPT_ATTN_E_INVAL;
   if (B < 0 || H < 0 || T < 0 || D <= 0) return GPT_ATTN_E_INVAL;
-  if (D != 64) return GPT_ATTN_E_UNSUPPORTED;
+  if (D != 32 && D != 64) return GPT_ATTN_E_UNSUPPORTED;
   const long long heads = (long long)B * (long long)H;
   const long long r = heads * (long long)T;
   if (r >= (1LL << 31)) return GPT_ATTN_E_INVAL;
@@ -40,7 +41,7 @@ int check_shape(int dtype, int B, int H, int T, int D, Shape* s) {
   s->T = T;
   s->D = D;
   s->rows = r;
-  s->esize = dtype == GPT_ATTN_BF16 ? 2 : 4;
+  s->esize = dtype == GPT_ATTN_F32 ? 4 : 2;
   return GPT_ATTN_OK;
 }
 
@@ -139,11 +140,11 @@ int bwd_args(const Shape& s, int which, const void* q, const gpt_attn_layout* lq
              const gpt_attn_layout* ldv, const void* workspace, size_t workspace_bytes,
              const gpt_attn_dropout* dropout, gpt_attn::BwdArgs* a) {
   const bool prep = which & 1, main = which & 2;
-  const bool bf16 = s.dtype == GPT_ATTN_BF16;
+  const bool half = s.dtype != GPT_ATTN_F32;  // 16-bit inputs: dQ by atomics, o_lo allowed
   if (!dout) return GPT_ATTN_E_INVAL;
-  if (prep && (!o || (bf16 && !dq))) return GPT_ATTN_E_INVAL;
+  if (prep && (!o || (half && !dq))) return GPT_ATTN_E_INVAL;
   if (main && (!q || !k || !v || !lse || !dq || !dk || !dv)) return GPT_ATTN_E_INVAL;
-  if (o_lo && !bf16) return GPT_ATTN_E_INVAL;
+  if (o_lo && !half) return GPT_ATTN_E_INVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(o_lo) ||
       !aligned16(dout) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return GPT_ATTN_E_ALIGN;
@@ -191,13 +192,15 @@ int bwd_args(const Shape& s, int which, const void* q, const gpt_attn_layout* lq
 }
 
 int run_prep(const Shape& s, const gpt_attn::BwdArgs& a, hipStream_t st) {
-  return launch_status(s.dtype == GPT_ATTN_BF16 ? gpt_attn::launch_bwd_prep_bf16(a, st)
-                                                : gpt_attn::launch_bwd_prep_f32(a, st));
+  return launch_status(s.dtype == GPT_ATTN_F32
+                           ? gpt_attn::launch_bwd_prep_f32(a, s.D, st)
+                           : gpt_attn::launch_bwd_prep_16(a, s.dtype == GPT_ATTN_F16, s.D, st));
 }
 
 int run_main(const Shape& s, const gpt_attn::BwdArgs& a, hipStream_t st) {
-  return launch_status(s.dtype == GPT_ATTN_BF16 ? gpt_attn::launch_bwd_main_bf16(a, st)
-                                                : gpt_attn::launch_bwd_main_f32(a, st));
+  return launch_status(s.dtype == GPT_ATTN_F32
+                           ? gpt_attn::launch_bwd_main_f32(a, s.D, st)
+                           : gpt_attn::launch_bwd_main_16(a, s.dtype == GPT_ATTN_F16, s.D, st));
 }
 
 }  // namespace
@@ -211,9 +214,10 @@ const char* gpt_attn_status_string(int status) {
     case GPT_ATTN_OK:
       return "ok";
     case GPT_ATTN_E_INVAL:
-      return "invalid argument (null pointer, negative or overflowing size, or bad dtype)";
+      return "invalid argument (null pointer, negative or overflowing size, bad dtype, or bad "
+             "dropout probability)";
     case GPT_ATTN_E_UNSUPPORTED:
-      return "unsupported head dimension (only D = 64 has kernels)";
+      return "unsupported head dimension (kernels exist for D = 32 and D = 64)";
     case GPT_ATTN_E_ALIGN:
       return "pointer not 16-byte aligned";
     case GPT_ATTN_E_WORKSPACE:
@@ -237,7 +241,7 @@ int gpt_attn_fwd_strided(int dtype, int B, int H, int T, int D, const void* q,
   GA_TRY(check_shape(dtype, B, H, T, D, &s));
   if (s.rows == 0) return GPT_ATTN_OK;
   if (!q || !k || !v || !o || !lse) return GPT_ATTN_E_INVAL;
-  if (o_lo && dtype != GPT_ATTN_BF16) return GPT_ATTN_E_INVAL;
+  if (o_lo && dtype == GPT_ATTN_F32) return GPT_ATTN_E_INVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
       !aligned16(o_lo))
     return GPT_ATTN_E_ALIGN;
@@ -263,8 +267,9 @@ int gpt_attn_fwd_strided(int dtype, int B, int H, int T, int D, const void* q,
   a.H = H;
   a.T = T;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return launch_status(dtype == GPT_ATTN_BF16 ? gpt_attn::launch_fwd_bf16(a, st)
-                                              : gpt_attn::launch_fwd_f32(a, st));
+  return launch_status(dtype == GPT_ATTN_F32
+                           ? gpt_attn::launch_fwd_f32(a, D, st)
+                           : gpt_attn::launch_fwd_16(a, dtype == GPT_ATTN_F16, D, st));
 }
 
 int gpt_attn_fwd(int dtype, int B, int H, int T, int D, const void* q, const void* k,
@@ -404,9 +409,7 @@ int gpt_attn_decode(int dtype, int B, int H, int L, int D, const void* q,
   a.n_heads = (int)heads;
   a.H = H;
   a.L = L;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  return launch_status(dtype == GPT_ATTN_BF16 ? gpt_attn::launch_decode_bf16(a, st)
-                                              : gpt_attn::launch_decode_f32(a, st));
+  return launch_status(gpt_attn::launch_decode(a, dtype, D, static_cast<hipStream_t>(stream)));
 }
 
 int gpt_attn_dropout_mask(int B, int H, int T, const gpt_attn_dropout* dropout,

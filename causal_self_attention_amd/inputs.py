@@ -13,8 +13,9 @@ Recipe (one ``torch.Generator('cpu')`` per call, seeded with ``seed``):
 
 The shapes are the attention layers of the models the nanoGPT pages train:
 the "baby GPT" Shakespeare-char model (6 heads of 64 channels, block size
-256) and GPT-2 124M / 774M / 1558M (12 / 20 / 25 heads of 64, block size
-1024). The pages give no activation statistics, so i.i.d. N(0, 1) draws stand
+256), the smaller Shakespeare-char run on a laptop (4 heads of 32 channels,
+block size 64, batch 12) and GPT-2 124M / 774M / 1558M (12 / 20 / 25 heads
+of 64, block size 1024). The pages give no activation statistics, so i.i.d. N(0, 1) draws stand
 in for real activations.
 
 Decode inputs (one new query per sequence against a key/value cache, as
@@ -39,7 +40,7 @@ class Workload:
     """One attention-layer shape with its input dtype and Q/K draw scale."""
 
     name: str
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "f16"
     B: int
     H: int
     T: int
@@ -61,6 +62,12 @@ WORKLOADS: dict[str, Workload] = {
         # GPT-2 1558M attention layer, and the same heads at twice the context.
         Workload("gpt2_1558m_bf16_b4_h25_t1024", "bf16", 4, 25, 1024, 64),
         Workload("gpt2_1558m_long_bf16_b2_h25_t2048", "bf16", 2, 25, 2048, 64),
+        # GPT-2 124M layer under fp16 mixed precision.
+        Workload("gpt2_124m_f16_b12_h12_t1024", "f16", 12, 12, 1024, 64),
+        # The laptop Shakespeare-char run: batch 12, 4 heads of 32 channels,
+        # block 64 (head size 128 / 4), in fp32 and bf16.
+        Workload("shakespeare_char_small_f32_b12_h4_t64_d32", "f32", 12, 4, 64, 32),
+        Workload("shakespeare_char_small_bf16_b12_h4_t64_d32", "bf16", 12, 4, 64, 32),
     )
 }
 
@@ -70,6 +77,8 @@ def torch_dtype(dtype: str) -> torch.dtype:
         return torch.float32
     if dtype == "bf16":
         return torch.bfloat16
+    if dtype == "f16":
+        return torch.float16
     raise ValueError(f"unknown dtype {dtype!r}")
 
 

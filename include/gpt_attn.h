@@ -31,8 +31,11 @@
  *   - stream is a hipStream_t (NULL = the default stream). Calls only enqueue
  *     work and return; results are visible after the caller synchronizes.
  *   - Sizes: B, H, T >= 0; a call with B*H*T == 0 does nothing and returns
- *     GPT_ATTN_OK (pointers are not inspected). D must be 64. B*H*T must be
- *     below 2^31 and B*H*T*D below 2^40.
+ *     GPT_ATTN_OK (pointers are not inspected). D must be 32 or 64 (the head
+ *     sizes of the pages' models: 768/12 = 64 for GPT-2, 128/4 = 32 for the
+ *     small Shakespeare-char run on a laptop, page "nanoGPT: a real GPT in
+ *     two 300-line files", section 3 "Run it, tested"). B*H*T must be below
+ *     2^31 and B*H*T*D below 2^40.
  *   - Errors: argument errors are returned before any device work is
  *     enqueued and leave every buffer untouched. GPT_ATTN_E_HIP means the
  *     HIP runtime rejected a launch (hipGetLastError); a fault inside a
@@ -50,14 +53,14 @@
 extern "C" {
 #endif
 
-#define GPT_ATTN_ABI_VERSION 4
+#define GPT_ATTN_ABI_VERSION 5
 
 /* Status codes returned by every int-returning entry point. */
 enum gpt_attn_status {
   GPT_ATTN_OK = 0,
   GPT_ATTN_E_INVAL = 1,       /* null pointer, negative or overflowing size, bad dtype code,
-                                 o_lo given with GPT_ATTN_F32 */
-  GPT_ATTN_E_UNSUPPORTED = 2, /* a head dimension D with no kernel (D != 64) */
+                                 o_lo given with GPT_ATTN_F32, bad dropout probability */
+  GPT_ATTN_E_UNSUPPORTED = 2, /* a head dimension D with no kernel (D not 32 or 64) */
   GPT_ATTN_E_ALIGN = 3,       /* a pointer that is not 16-byte aligned */
   GPT_ATTN_E_WORKSPACE = 4,   /* workspace NULL or smaller than gpt_attn_bwd_workspace_bytes */
   GPT_ATTN_E_HIP = 5,         /* the HIP runtime reported an error when launching */
@@ -121,10 +124,14 @@ typedef struct gpt_attn_dropout {
   unsigned int offset;
 } gpt_attn_dropout;
 
-/* Element type of q, k, v, o and dout. lse, dq, dk, dv are always fp32. */
+/* Element type of q, k, v, o and dout (and of the decode caches). lse, dq,
+ * dk, dv are always fp32. The pages' GPU training runs in automatic mixed
+ * precision, BF16 or FP16 (page "nanoGPT: Minimal, Readable, and Fast
+ * PyTorch Framework for Training Medium GPTs", feature list). */
 enum gpt_attn_dtype {
-  GPT_ATTN_F32 = 0, /* IEEE binary32 inputs, fp32 arithmetic throughout */
-  GPT_ATTN_BF16 = 1 /* bfloat16 inputs; matrix products accumulate in fp32 */
+  GPT_ATTN_F32 = 0,  /* IEEE binary32 inputs, fp32 arithmetic throughout */
+  GPT_ATTN_BF16 = 1, /* bfloat16 inputs; matrix products accumulate in fp32 */
+  GPT_ATTN_F16 = 2   /* IEEE binary16 inputs; matrix products accumulate in fp32 */
 };
 
 /*
@@ -134,17 +141,18 @@ enum gpt_attn_dtype {
  *
  *   q, k, v  in   [B,H,T,D] of dtype
  *   o        out  [B,H,T,D] of dtype (bf16 output is rounded to nearest even)
- *   o_lo     out  OPTIONAL, bf16 only (must be NULL for GPT_ATTN_F32):
- *                 [B,H,T,D] bf16 receiving bf16(O - o), the part of the fp32
- *                 result that rounding o to bf16 dropped. Passing it to
- *                 gpt_attn_bwd gives the backward an O accurate to ~16 bits,
- *                 which its delta = rowsum(dO * O) needs when softmax rows
- *                 are sharp. NULL skips the write.
+ *   o_lo     out  OPTIONAL, 16-bit dtypes only (must be NULL for
+ *                 GPT_ATTN_F32): [B,H,T,D] of dtype receiving round(O - o),
+ *                 the part of the fp32 result that rounding o to the dtype
+ *                 dropped. Passing it to gpt_attn_bwd gives the backward an O
+ *                 accurate to about twice the dtype's precision, which its
+ *                 delta = rowsum(dO * O) needs when softmax rows are sharp.
+ *                 NULL skips the write.
  *   lse      out  [B,H,T] fp32; the backward needs it
  *
- * For bf16, the P V product rounds P to fp16 and converts V to fp16, which is
- * exact for |v| in [2^-14, 65504]; inputs beyond fp16's finite range give
- * non-finite outputs.
+ * For bf16 and fp16, the P V product rounds P to fp16 and converts V to fp16,
+ * which is exact for bf16 |v| in [2^-14, 65504]; bf16 inputs beyond fp16's
+ * finite range give non-finite outputs.
  */
 int gpt_attn_fwd(int dtype, int B, int H, int T, int D, const void* q, const void* k,
                  const void* v, void* o, void* o_lo, float* lse, void* stream);
@@ -163,9 +171,9 @@ size_t gpt_attn_bwd_workspace_bytes(int dtype, int B, int H, int T, int D);
  *
  *   q, k, v      in   [B,H,T,D] of dtype (the forward's inputs)
  *   o            in   [B,H,T,D] of dtype (the forward's output)
- *   o_lo         in   OPTIONAL, bf16 only: the forward's o_lo output; when
- *                     given, delta uses o + o_lo instead of o. Must be NULL
- *                     for GPT_ATTN_F32.
+ *   o_lo         in   OPTIONAL, 16-bit dtypes only: the forward's o_lo
+ *                     output; when given, delta uses o + o_lo instead of o.
+ *                     Must be NULL for GPT_ATTN_F32.
  *   dout         in   [B,H,T,D] of dtype (upstream gradient dL/dO)
  *   lse          in   [B,H,T] fp32 (the forward's output)
  *   dq, dk, dv   out  [B,H,T,D] fp32, fully overwritten
@@ -173,11 +181,11 @@ size_t gpt_attn_bwd_workspace_bytes(int dtype, int B, int H, int T, int D);
  *                bytes, device memory owned by the caller; contents on entry
  *                are ignored and on return are unspecified.
  *
- * For bf16, the products with a rounded operand (P^T dO, dS^T Q, dS K) round
- * P and dS to fp16 and convert dout, q, k to fp16 (exact for magnitudes in
- * [2^-14, 65504]). dk, dv (and o, lse from gpt_attn_fwd) are bitwise
- * reproducible run to run. dq is accumulated with fp32 atomic adds in the
- * bf16 path, so its low bits may vary between runs.
+ * For bf16 and fp16, every product runs on fp16 matrix cores: q, k, v, dout
+ * are converted to fp16 (exact for bf16 magnitudes in [2^-14, 65504]) and P
+ * and dS are rounded to fp16. dk, dv (and o, lse from gpt_attn_fwd) are
+ * bitwise reproducible run to run. dq is accumulated with fp32 atomic adds
+ * for the 16-bit dtypes, so its low bits may vary between runs.
  */
 int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const void* k,
                  const void* v, const void* o, const void* o_lo, const void* dout,
@@ -191,12 +199,13 @@ int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const voi
  *
  * gpt_attn_bwd_prep: the preprocess pass. Writes delta_i = sum_d dout_id O_id
  *   (O = o, or o + o_lo when o_lo is given) into the first B*H*T floats of
- *   workspace; for GPT_ATTN_BF16 it also zero-fills dq, which the main phase
- *   accumulates into (dq may be NULL for GPT_ATTN_F32 and is not touched).
+ *   workspace; for the 16-bit dtypes it also zero-fills dq, which the main
+ *   phase accumulates into (dq may be NULL for GPT_ATTN_F32 and is not
+ *   touched).
  * gpt_attn_bwd_main: everything else. Reads delta from workspace, which must
- *   hold the prep phase's result for the same o and dout (and, for
- *   GPT_ATTN_BF16, dq must still hold the prep phase's zeros). Writes dq, dk,
- *   dv. Arguments mean what they mean for gpt_attn_bwd.
+ *   hold the prep phase's result for the same o and dout (and, for the 16-bit
+ *   dtypes, dq must still hold the prep phase's zeros). Writes dq, dk, dv.
+ *   Arguments mean what they mean for gpt_attn_bwd.
  */
 int gpt_attn_bwd_prep(int dtype, int B, int H, int T, int D, const void* o, const void* o_lo,
                       const void* dout, float* dq, void* workspace, size_t workspace_bytes,

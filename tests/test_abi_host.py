@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "gpt_attn.h")
 
 OK, E_INVAL, E_UNSUP, E_ALIGN, E_WS, E_HIP, E_LAYOUT = 0, 1, 2, 3, 4, 5, 6
 DROP = gattn.GptAttnDropout
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 P = 0x10000  # 16-byte aligned fake device address, never dereferenced
 
 
@@ -72,12 +72,13 @@ def bwd(lib, dtype=BF16, B=1, H=1, T=8, D=64, ptrs=None, ws=P, ws_bytes=1 << 20)
 
 
 def test_forward_validation(lib):
-    assert fwd(lib, dtype=2) == E_INVAL
+    assert fwd(lib, dtype=3) == E_INVAL
+    assert fwd(lib, dtype=-1) == E_INVAL
     assert fwd(lib, B=-1) == E_INVAL
     assert fwd(lib, H=-1) == E_INVAL
     assert fwd(lib, T=-1) == E_INVAL
     assert fwd(lib, D=0) == E_INVAL
-    for D in (1, 32, 63, 65, 128):
+    for D in (1, 16, 48, 63, 65, 96, 128):
         assert fwd(lib, D=D) == E_UNSUP
     for name in ("q", "k", "v", "o", "lse"):
         assert fwd(lib, **{name: None}) == E_INVAL, name
@@ -103,7 +104,7 @@ def test_empty_calls_are_noops(lib):
 
 def test_backward_validation(lib):
     assert bwd(lib, dtype=-1) == E_INVAL
-    assert bwd(lib, D=32) == E_UNSUP
+    assert bwd(lib, D=128) == E_UNSUP
     for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
         assert bwd(lib, ptrs={name: None}) == E_INVAL, name
         assert bwd(lib, ptrs={name: P + 4}) == E_ALIGN, name
@@ -119,7 +120,8 @@ def test_backward_validation(lib):
 def test_workspace_bytes(lib):
     assert lib.gpt_attn_bwd_workspace_bytes(BF16, 12, 12, 1024, 64) == 12 * 12 * 1024 * 4
     assert lib.gpt_attn_bwd_workspace_bytes(F32, 1, 6, 256, 64) == 6 * 256 * 4
-    assert lib.gpt_attn_bwd_workspace_bytes(BF16, 1, 1, 8, 32) == 0
+    assert lib.gpt_attn_bwd_workspace_bytes(BF16, 1, 1, 8, 128) == 0
+    assert lib.gpt_attn_bwd_workspace_bytes(F16, 1, 2, 8, 32) == 2 * 8 * 4
     assert lib.gpt_attn_bwd_workspace_bytes(7, 1, 1, 8, 64) == 0
     assert lib.gpt_attn_bwd_workspace_bytes(BF16, -1, 1, 8, 64) == 0
 
@@ -205,7 +207,7 @@ def test_strided_backward_accepts_the_fused_layout(lib):
 
 def test_plain_calls_equal_strided_calls_with_null_layouts(lib):
     # Same validation outcome either way.
-    assert fwd_s(lib, D=32) == fwd(lib, D=32) == E_UNSUP
+    assert fwd_s(lib, D=128) == fwd(lib, D=128) == E_UNSUP
     assert bwd_s(lib) == E_WS
     assert lib.gpt_attn_bwd_prep_strided(BF16, 1, 1, 8, 64, P, None, None, None, P, None, P,
                                          ctypes.byref(L(0, 0, 32)), P, 1 << 20, None) == E_LAYOUT
@@ -245,7 +247,7 @@ def test_dropout_descriptor_validation(lib):
     for p in (0.0, 0.1, 0.2, 0.99999):
         assert bwd_s(lib, drop=DROP(p, 2**64 - 1, 2**32 - 1)) == E_WS, p
     # Shape errors still come first.
-    assert fwd_s(lib, D=32, drop=DROP(2.0, 0, 0)) == E_UNSUP
+    assert fwd_s(lib, D=128, drop=DROP(2.0, 0, 0)) == E_UNSUP
 
 
 def test_dropout_mask_entry_validation(lib):
@@ -273,7 +275,8 @@ def test_decode_validation(lib):
     assert need == 2 * 3 * 1 * 68 * 4       # one 128-key chunk per head at most
     assert lib.gpt_attn_decode_workspace_bytes(BF16, 64, 12, 1024, 64) == 768 * 8 * 68 * 4
     assert lib.gpt_attn_decode_workspace_bytes(BF16, 2, 3, 0, 64) == 0
-    assert lib.gpt_attn_decode_workspace_bytes(BF16, 2, 3, 100, 32) == 0
+    assert lib.gpt_attn_decode_workspace_bytes(BF16, 2, 3, 100, 128) == 0
+    assert lib.gpt_attn_decode_workspace_bytes(F16, 2, 3, 100, 32) == need
     assert dec(lib, D=128) == E_UNSUP
     assert dec(lib, dtype=5) == E_INVAL
     assert dec(lib, L=-1) == E_INVAL
@@ -287,3 +290,20 @@ def test_decode_validation(lib):
     assert dec(lib, lk=L(-8, 64, 64)) == E_LAYOUT
     assert dec(lib, lo=L(64, 0, 64)) == E_LAYOUT       # heads of O overlap
     assert dec(lib, B=0, q=None, k=None, v=None, o=None, lse=None) == OK
+
+
+def test_sixteen_bit_dtypes_and_head_sizes_share_the_rules(lib):
+    """fp16 and D = 32 go through the same validation (every call below stops
+    at a validation error, before any launch)."""
+    for dt in (BF16, F16):
+        for D in (32, 64):
+            assert fwd(lib, dtype=dt, D=D, q=None) == E_INVAL
+            assert fwd(lib, dtype=dt, D=D, o=P + 2) == E_ALIGN
+            assert bwd(lib, dtype=dt, D=D, ws=None) == E_WS
+            assert bwd(lib, dtype=dt, D=D, ptrs={"dq": None}) == E_INVAL
+    # o_lo is allowed for both 16-bit types, not for fp32.
+    assert fwd(lib, dtype=F16, o_lo=P + 2) == E_ALIGN
+    assert fwd(lib, dtype=F32, D=32, o_lo=P) == E_INVAL
+    # fp16 rows are 16-byte aligned at multiples of 8 elements.
+    assert bwd_s(lib, dtype=F16, q=L(8 * 300, 8 * 40, 8 * 7)) == E_WS
+    assert bwd_s(lib, dtype=F16, q=L(8 * 300, 8 * 40, 60)) == E_LAYOUT

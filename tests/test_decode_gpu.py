@@ -49,16 +49,17 @@ def _run(inp, ragged_on_gpu=True):
     return o, lse
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f32", 64), ("f16", 64), ("bf16", 32),
+                                     ("f32", 32), ("f16", 32)])
 @pytest.mark.parametrize("ragged", [False, True])
 @pytest.mark.parametrize("B,H,L", [(1, 1, 1), (1, 2, 7), (2, 3, 129), (1, 1, 1000), (3, 2, 257),
                                    (5, 1, 128)])
-def test_decode_parity(dtype, ragged, B, H, L):
-    announce(f"decode dtype={dtype} ragged={ragged} B={B} H={H} L={L}")
-    inp = make_decode_inputs(B, H, L, 64, dtype, seed=L + B, ragged=ragged)
+def test_decode_parity(dtype, D, ragged, B, H, L):
+    announce(f"decode dtype={dtype} D={D} ragged={ragged} B={B} H={H} L={L}")
+    inp = make_decode_inputs(B, H, L, D, dtype, seed=L + B, ragged=ragged)
     o, lse = _run(inp)
     o_ref, lse_ref = oracle.attn_decode(inp["q"], inp["k"], inp["v"], inp["lengths"].numpy())
-    _check(o, lse, o_ref, lse_ref, dtype, f"decode {dtype} B={B} H={H} L={L}")
+    _check(o, lse, o_ref, lse_ref, dtype, f"decode {dtype} D={D} B={B} H={H} L={L}")
 
 
 @pytest.mark.parametrize("name", list(DECODE_WORKLOADS))

@@ -40,15 +40,16 @@ def test_keep_mask_bit_exact(B, H, T, p, seed, offset):
     assert np.array_equal(got, ref), f"{int((got != ref).sum())} entries differ"
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f32", 64), ("f16", 64), ("bf16", 32),
+                                     ("f32", 32)])
 @pytest.mark.parametrize("B,H,T", [(1, 1, 1), (1, 1, 31), (1, 2, 65), (2, 3, 333), (1, 1, 300)])
-def test_dropout_parity(dtype, B, H, T):
+def test_dropout_parity(dtype, D, B, H, T):
     drop = (0.2, 1000 + T, 3)
-    announce(f"dropout parity dtype={dtype} B={B} H={H} T={T} drop={drop}")
-    inp = make_inputs(B, H, T, 64, dtype, seed=T + 50)
+    announce(f"dropout parity dtype={dtype} D={D} B={B} H={H} T={T} drop={drop}")
+    inp = make_inputs(B, H, T, D, dtype, seed=T + 50)
     gpu = run_gpu_dropout(inp, drop)
     ref = run_oracle_dropout(inp, drop)
-    assert_parity(errors(gpu, ref), dtype, f"dropout {dtype} B={B} H={H} T={T}")
+    assert_parity(errors(gpu, ref), dtype, f"dropout {dtype} D={D} B={B} H={H} T={T}")
 
 
 @pytest.mark.parametrize("p", [0.1, 0.5, 0.9])

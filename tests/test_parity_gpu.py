@@ -22,15 +22,16 @@ pytestmark = pytest.mark.gpu
 EDGE_T = [1, 2, 3, 7, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257, 300, 1000]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f32", 64), ("f16", 64), ("bf16", 32),
+                                     ("f32", 32), ("f16", 32)])
 @pytest.mark.parametrize("T", EDGE_T)
-def test_small_shapes_full_compare(dtype, T):
+def test_small_shapes_full_compare(dtype, D, T):
     for (B, H) in [(1, 1), (1, 3)]:
-        announce(f"small dtype={dtype} B={B} H={H} T={T} seed={T}")
-        inp = make_inputs(B, H, T, 64, dtype, seed=T)
+        announce(f"small dtype={dtype} D={D} B={B} H={H} T={T} seed={T}")
+        inp = make_inputs(B, H, T, D, dtype, seed=T)
         gpu = run_gpu(inp)
         ref = run_oracle(inp)
-        assert_parity(errors(gpu, ref), dtype, f"{dtype} B={B} H={H} T={T}")
+        assert_parity(errors(gpu, ref), dtype, f"{dtype} D={D} B={B} H={H} T={T}")
 
 
 def test_backward_without_o_lo():
@@ -165,7 +166,7 @@ def test_outputs_stay_in_bounds(dtype):
 
 def test_error_statuses_through_binding():
     dev = torch.device("cuda:0")
-    q = torch.zeros(1, 1, 8, 32, dtype=torch.bfloat16, device=dev)
+    q = torch.zeros(1, 1, 8, 128, dtype=torch.bfloat16, device=dev)
     with pytest.raises(gattn.GptAttnError) as ei:
         gattn.attention_forward(q, q, q)
     assert ei.value.status == 2  # unsupported head dim

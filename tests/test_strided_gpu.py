@@ -84,6 +84,17 @@ def test_fused_layout_parity(dtype, B, H, T):
     _compare_with_contiguous(fused, run_gpu(inp), dtype, f"{dtype} B={B} H={H} T={T}")
 
 
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 32), ("f16", 32), ("f32", 32)])
+def test_fused_layout_other_dtypes_and_head_sizes(dtype, D):
+    B, H, T = 2, 3, 200
+    announce(f"fused layout dtype={dtype} D={D} B={B} H={H} T={T}")
+    inp = make_inputs(B, H, T, D, dtype, seed=300 + D)
+    fused, bufs = run_fused(inp)
+    _check_pads(bufs)
+    assert_parity(errors(fused, run_oracle(inp)), dtype, f"fused {dtype} D={D}")
+    _compare_with_contiguous(fused, run_gpu(inp), dtype, f"{dtype} D={D}")
+
+
 def test_fused_layout_without_o_lo():
     announce("fused layout bf16 no o_lo B=2 H=3 T=200")
     inp = make_inputs(2, 3, 200, 64, "bf16", seed=17)
