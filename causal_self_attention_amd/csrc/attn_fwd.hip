@@ -97,11 +97,9 @@ struct FwdState {
   float l_run;          // this lane's partial row sum
 };
 
-// One 64-key tile for one wave. MASKED = false: every key of the tile
+// One 64-key tile for one wave, off the diagonal: every key of the tile
 // precedes every query of the wave and lies below T (no compares at all).
-// MASKED = true: keys after the lane's query or at/after T get -inf through
-// branch-free selects against one per-lane limit.
-template <typename TIn, int D, bool MASKED, bool DROP>
+template <typename TIn, int D, bool DROP>
 __device__ __forceinline__ void fwd_tile(const TIn* cK, const f16* cV,
                                          const typename In16<TIn>::vec (&qf)[D / 16], int k0,
                                          int my_q, int T, int l32, int hf, int lane,
@@ -119,15 +117,6 @@ __device__ __forceinline__ void fwd_tile(const TIn* cK, const f16* cV,
 #pragma unroll
     for (int kk = 1; kk < D / 16; ++kk)
       s[kb] = In16<TIn>::mfma(*reinterpret_cast<const vec*>(arow + kk * 16), qf[kk], s[kb]);
-  }
-  if (MASKED) {
-    // Visible iff k0 + 32kb + 16c + 8hf + t <= min(my_q, T - 1).
-    const int lim = min(my_q, T - 1) - k0 - 8 * hf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        s[kb][r] = (32 * kb + 16 * (r >> 3) + (r & 7) > lim) ? -INFINITY : s[kb][r];
   }
 
   // Lazy running max: the reference m_run moves only when some row's max
@@ -181,6 +170,73 @@ __device__ __forceinline__ void fwd_tile(const TIn* cK, const f16* cV,
         st.oacc[db] = mfma32x32x16_f16(lds_operand_tr(cV, kRow, ks * 16, db * 32, lane), pw,
                                        st.oacc[db]);
     }
+  }
+}
+
+// One 32-key half (keys k0 + 32kb ..) for one wave on the diagonal tiles,
+// with its own running-max update. KIND is the half's block kind against the
+// wave's 32 queries (wave-uniform; kEmpty halves are never called): kFull
+// has no mask, kDiag the fixed triangle key offset <= query offset, kGeneral
+// the per-lane limit min(query, T - 1).
+template <typename TIn, int D, int KIND, bool DROP>
+__device__ __forceinline__ void fwd_half(const TIn* cK, const f16* cV,
+                                         const typename In16<TIn>::vec (&qf)[D / 16], int kb,
+                                         int k0, int my_q, int T, int l32, int hf, int lane,
+                                         float scale_log2, const Dropout& drop, int head,
+                                         FwdState<D>& st) {
+  typedef typename In16<TIn>::vec vec;
+  constexpr int kRow = row_of<D>();
+  // Register v = 8c + t of half hf holds key k0 + 32kb + 16c + 8hf + t.
+  const TIn* arow = &cK[(kb * 32 + perm32(l32)) * kRow + 8 * hf];
+  f32x16 s = In16<TIn>::mfma(*reinterpret_cast<const vec*>(arow), qf[0], f32x16{});
+#pragma unroll
+  for (int kk = 1; kk < D / 16; ++kk)
+    s = In16<TIn>::mfma(*reinterpret_cast<const vec*>(arow + kk * 16), qf[kk], s);
+  if (KIND == kDiag) {
+    // Key offset 16c + 8hf + t against query offset l32.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = (16 * (r >> 3) + (r & 7) > l32 - 8 * hf) ? -INFINITY : s[r];
+  } else if (KIND == kGeneral) {
+    const int lim = min(my_q, T - 1) - (k0 + 32 * kb) - 8 * hf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = (16 * (r >> 3) + (r & 7) > lim) ? -INFINITY : s[r];
+  }
+  float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+  for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  mx = fmaxf(mx, wave_xor32(mx)) * scale_log2;
+  if (wave_any(mx > st.m_run + kMaxSlack)) {
+    const float m_new = fmaxf(st.m_run, mx);
+    const float alpha = fast_exp2(st.m_run - m_new);
+    st.m_run = m_new;
+    st.l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    float p[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) p[t] = fast_exp2(fmaf(s[8 * c + t], scale_log2, -st.m_run));
+    const f16x8 pb = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+    st.l_run = sum_f16x8(pb, st.l_run);
+    f16x8 pw = pb;
+    if (DROP) {
+      uint32_t m[4];
+      keep_mask8(drop, (uint32_t)head, (uint32_t)my_q,
+                 (uint32_t)((k0 + 32 * kb + 16 * c) >> 3) + hf, m);
+      i32x4 bits = __builtin_bit_cast(i32x4, pb);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) bits[w] &= (int)m[w];
+      pw = __builtin_bit_cast(f16x8, bits);
+    }
+    const int ks = 2 * kb + c;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      st.oacc[db] = mfma32x32x16_f16(lds_operand_tr(cV, kRow, ks * 16, db * 32, lane), pw,
+                                     st.oacc[db]);
   }
 }
 
@@ -268,8 +324,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
     const int k0 = kt * kBN;
     const bool has_next = kt + 1 < n_kt;
     if (has_next) fwd_load_tile<TIn, D>(kh, ldk, vh, ldv, k0 + kBN, T, tid, nxt);
-    fwd_tile<TIn, D, false, DROP>(Kbuf(buf), Vbuf(buf), qf, k0, my_q, T, l32, hf, lane,
-                                  scale_log2, a.drop, tm.head, st);
+    fwd_tile<TIn, D, DROP>(Kbuf(buf), Vbuf(buf), qf, k0, my_q, T, l32, hf, lane, scale_log2,
+                           a.drop, tm.head, st);
     if (has_next) fwd_store_tile<TIn, D>(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid);
     __syncthreads();
   }
@@ -277,38 +333,68 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
     const int k0 = kt * kBN;
     const bool has_next = kt + 1 < n_kt;
     if (has_next) fwd_load_tile<TIn, D>(kh, ldk, vh, ldv, k0 + kBN, T, tid, nxt);
-    fwd_tile<TIn, D, true, DROP>(Kbuf(buf), Vbuf(buf), qf, k0, my_q, T, l32, hf, lane,
-                                 scale_log2, a.drop, tm.head, st);
+    // Diagonal and boundary tiles, half by half: halves wholly in this wave's
+    // future are skipped, the diagonal half gets the fixed triangle.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int kind = block_kind(k0 + 32 * kb, qw0, T);
+      if (kind == kFull)
+        fwd_half<TIn, D, kFull, DROP>(Kbuf(buf), Vbuf(buf), qf, kb, k0, my_q, T, l32, hf, lane,
+                                      scale_log2, a.drop, tm.head, st);
+      else if (kind == kDiag)
+        fwd_half<TIn, D, kDiag, DROP>(Kbuf(buf), Vbuf(buf), qf, kb, k0, my_q, T, l32, hf, lane,
+                                      scale_log2, a.drop, tm.head, st);
+      else if (kind == kGeneral)
+        fwd_half<TIn, D, kGeneral, DROP>(Kbuf(buf), Vbuf(buf), qf, kb, k0, my_q, T, l32, hf,
+                                         lane, scale_log2, a.drop, tm.head, st);
+    }
     if (has_next) fwd_store_tile<TIn, D>(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid);
     __syncthreads();
   }
 
-  // Epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2.
+  // Epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2. The wave's O rows
+  // (and o_lo rows) go through LDS, which every wave finished reading at the
+  // loop's last barrier, so that global stores write whole rows: D/8 lanes
+  // per row, 16 bytes each.
   const float l_tot = st.l_run + wave_xor32(st.l_run);
   const float inv = (DROP ? a.drop.scale : 1.f) / l_tot;
-  if (my_q < T) {
+  {
     typedef typename In16<TIn>::vec4 vec4;
-    TIn* orow = static_cast<TIn*>(a.o) + head_base(a.lo, tm.head, a.H) + my_q * (int)a.lo.t;
-    TIn* lrow = a.o_lo ? static_cast<TIn*>(a.o_lo) + head_base(a.llo, tm.head, a.H) +
-                             my_q * (int)a.llo.t
-                       : nullptr;
+    TIn* so = lds_raw + (wave * 32) * kRow;        // O rows [query][d]
+    TIn* sl = lds_raw + (kBM + wave * 32) * kRow;  // o_lo rows
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        float x[4];
         vec4 hi, lo;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          x[t] = st.oacc[db][4 * g + t] * inv;
-          hi[t] = In16<TIn>::round(x[t]);
-          lo[t] = In16<TIn>::round(x[t] - (float)hi[t]);
+          const float x = st.oacc[db][4 * g + t] * inv;
+          hi[t] = In16<TIn>::round(x);
+          lo[t] = In16<TIn>::round(x - (float)hi[t]);
         }
-        *reinterpret_cast<vec4*>(orow + db * 32 + 8 * g + 4 * hf) = hi;
-        if (lrow) *reinterpret_cast<vec4*>(lrow + db * 32 + 8 * g + 4 * hf) = lo;
+        *reinterpret_cast<vec4*>(&so[l32 * kRow + db * 32 + 8 * g + 4 * hf]) = hi;
+        *reinterpret_cast<vec4*>(&sl[l32 * kRow + db * 32 + 8 * g + 4 * hf]) = lo;
       }
-    if (hf == 0) a.lse[(size_t)tm.head * T + my_q] = (st.m_run + fast_log2(l_tot)) * kLn2;
+    __builtin_amdgcn_wave_barrier();
+    TIn* ob = static_cast<TIn*>(a.o) + head_base(a.lo, tm.head, a.H);
+    TIn* lb = a.o_lo ? static_cast<TIn*>(a.o_lo) + head_base(a.llo, tm.head, a.H) : nullptr;
+    constexpr int kC = D / 8;  // 16-byte chunks per row
+#pragma unroll
+    for (int i = 0; i < 32 * kC / 64; ++i) {
+      const int c = i * 64 + lane;
+      const int row = c / kC, col = (c % kC) * 8;
+      const int qrow = qw0 + row;
+      if (qrow < T) {
+        *reinterpret_cast<vec*>(ob + qrow * (int)a.lo.t + col) =
+            *reinterpret_cast<const vec*>(&so[row * kRow + col]);
+        if (lb)
+          *reinterpret_cast<vec*>(lb + qrow * (int)a.llo.t + col) =
+              *reinterpret_cast<const vec*>(&sl[row * kRow + col]);
+      }
+    }
   }
+  if (my_q < T && hf == 0) a.lse[(size_t)tm.head * T + my_q] = (st.m_run + fast_log2(l_tot)) * kLn2;
 }
 
 template <typename TIn, int D>
