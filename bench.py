@@ -10,6 +10,12 @@ output, dO from and O into [B, T, C], fp32 dQ, dK, dV into one [B, T, 3C].
 ``--dropout P`` applies attention dropout at rate P in the forward and the
 backward (the keep mask regenerated in both); the FLOP count is unchanged.
 
+Timing: the timed region holds only the step's three launches, ``--steps``
+times (no event records between them; ``--graph`` replays them from a HIP
+graph instead, which measured slower than plain launches on this runtime);
+the per-kernel durations behind ``roofline`` come from HIP events around
+each launch in an equal number of separate eager steps.
+
 FLOPs are the causal algorithmic count: only the T(T+1)/2 unmasked (query,
 key) pairs per head, 4*D per pair forward (QK^T and PV) and 10*D per pair
 backward (QK^T recompute, dP, dV, dK, dQ).
@@ -195,6 +201,8 @@ def main(argv=None) -> int:
     ap.add_argument("--mode", choices=("train", "decode"), default="train",
                     help="train: forward + backward (the headline); decode: one query per "
                          "sequence against a key/value cache")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured in a HIP graph")
     ap.add_argument("--layout", choices=("bhtd", "fused"), default="bhtd",
                     help="bhtd: contiguous [B, H, T, D] operands; fused: views of the "
                          "projection's [B, T, 3C] output and of [B, T, C] buffers")
@@ -279,9 +287,10 @@ def main(argv=None) -> int:
 
     def step(i=None):
         if i is None:
-            fwd_call(q, k, v, o, o_lo, lse, stream)
-            prep_call(o, o_lo, do, dq, ws, stream)
-            main_call(q, k, v, do, lse, dq, dk, dv, ws, stream)
+            st = torch.cuda.current_stream(dev)  # the capture stream while capturing
+            fwd_call(q, k, v, o, o_lo, lse, st)
+            prep_call(o, o_lo, do, dq, ws, st)
+            main_call(q, k, v, do, lse, dq, dk, dv, ws, st)
             return
         a, b = ev["fwd"][i]
         a.record(stream)
@@ -300,21 +309,44 @@ def main(argv=None) -> int:
         step()
     torch.cuda.synchronize()
 
+    # Per-kernel durations: eager steps with HIP events on the launch stream.
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    avg = {name: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+           for name, pairs in ev.items()}
+
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
-        step(i)
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    avg = {name: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
-           for name, pairs in ev.items()}
     fwd_flop, bwd_flop = flops(w)
     value = (fwd_flop + bwd_flop) / (ms_per_step * 1e-3) / 1e12
     if not (torch.isfinite(dq).all() and torch.isfinite(o.float()).all()):
@@ -340,6 +372,7 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "D": w.D,
                    "causal": True, "scale": 1.0 / w.D ** 0.5, "seed": args.seed,
                    "layout": "B,T,3C views" if fused else "BHTD", "dropout": args.dropout,
+                   "launch": "eager" if graph is None else "hip_graph",
                    "pct_of_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2)},
         "fwd": {"ms": round(avg["fwd"], 5),
                 "tflops": round(fwd_flop / (avg["fwd"] * 1e-3) / 1e12, 2),

@@ -15,8 +15,8 @@
 // Kernel 1 (prep) forms delta from the stored O (plus its low part o_lo
 // when the forward kept it, which restores fp32 accuracy) and zeroes dQ.
 // Kernel 2 (main): a workgroup of 8 waves owns 256 consecutive keys of one
-// head (32 per wave) and keeps their K, V fragments and dK, dV accumulators
-// in registers. It walks the 64-query tiles from its diagonal to the end of
+// head (32 per wave), stages their K in LDS, and keeps their V fragments and
+// dK, dV accumulators in registers. It walks the 64-query tiles from its diagonal to the end of
 // the sequence; each tile of Q and dO is staged once in LDS as row-major fp16
 // (waves 4..7 prefetch the next tile a step ahead into a second buffer), and
 // the transposed operands (Q^T, dO^T for dK^T += Q^T dS and dV^T += dO^T P)
@@ -251,14 +251,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
   const int kw0 = k0 + wave * 32;
   const int my_key = kw0 + l32;  // the key column this lane owns
 
-  // K and V of this wave's 32 keys as fp16 B operands (lane: its key, 8 dims).
-  f16x8 kf[D / 16], vf[D / 16];
+  // V of this wave's 32 keys as fp16 B operands (lane: its key, 8 dims). The
+  // K operands of S = Q K^T are the same row pieces of the staged K tile and
+  // are read from LDS when used, which keeps 4 * D/16 registers free for the
+  // scheduler.
+  f16x8 vf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     const bool ok = my_key < T;
-    kf[kk] = ok ? In16<TIn>::to_f16(*reinterpret_cast<const vec*>(kh + my_key * ldk + kk * 16 +
-                                                                  8 * hf))
-                : zero_f16x8();
     vf[kk] = ok ? In16<TIn>::to_f16(*reinterpret_cast<const vec*>(vh + my_key * ldv + kk * 16 +
                                                                   8 * hf))
                 : zero_f16x8();
@@ -334,7 +334,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
         const int arow = (mb * 32 + perm32(l32)) * kRowQ + 8 * hf;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-          s = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cQ[arow + kk * 16]), kf[kk], s);
+          const f16x8 kfr =
+              *reinterpret_cast<const f16x8*>(&sK[(wave * 32 + l32) * kRowQ + kk * 16 + 8 * hf]);
+          s = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cQ[arow + kk * 16]), kfr, s);
           dp = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cdO[arow + kk * 16]), vf[kk],
                                 dp);
         }
