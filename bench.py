@@ -27,8 +27,8 @@ second against the HBM roofline.
 
 Prints one JSON line. ``roofline`` describes the dominant kernel (the
 backward main kernel): its algorithmic FLOPs per launch over its average
-launch duration, timed with HIP events on the launch stream inside the timed
-region. ``cpu_baseline`` times the fp64 oracle on a bounded sample of the
+launch duration, timed with HIP events on the launch stream around each of
+its launches in the eager steps that precede the timed region. ``cpu_baseline`` times the fp64 oracle on a bounded sample of the
 same workload on the host cores.
 """
 from __future__ import annotations
