@@ -129,8 +129,12 @@ __device__ __forceinline__ void fwd_tile(const TIn* cK, const f16* cV,
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = fmaxf(mx, wave_xor32(mx)) * scale_log2;
+  // Lanes l and l + 32 hold the two halves of one query's keys and share
+  // m_run, so a half's own max decides as well as the row's max would; the
+  // cross-half exchange runs only when the reference moves.
+  mx *= scale_log2;
   if (wave_any(mx > st.m_run + kMaxSlack)) {
+    mx = fmaxf(mx, wave_xor32(mx));
     const float m_new = fmaxf(st.m_run, mx);
     const float alpha = fast_exp2(st.m_run - m_new);
     st.m_run = m_new;
@@ -204,8 +208,9 @@ __device__ __forceinline__ void fwd_half(const TIn* cK, const f16* cV,
   float mx = fmaxf(s[0], s[1]);
 #pragma unroll
   for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  mx = fmaxf(mx, wave_xor32(mx)) * scale_log2;
+  mx *= scale_log2;  // this half's max; exchanged only when m_run moves
   if (wave_any(mx > st.m_run + kMaxSlack)) {
+    mx = fmaxf(mx, wave_xor32(mx));
     const float m_new = fmaxf(st.m_run, mx);
     const float alpha = fast_exp2(st.m_run - m_new);
     st.m_run = m_new;
