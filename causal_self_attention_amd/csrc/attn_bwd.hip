@@ -22,11 +22,20 @@
 // the transposed operands (Q^T, dO^T for dK^T += Q^T dS and dV^T += dO^T P)
 // come from transposing LDS reads. Per tile each wave recomputes P from the
 // saved LSE, forms dS and writes its dS^T rows to LDS; then dQ = dS K over
-// the 256 keys is formed as 2 * D/32 blocks of 32x32, each split into
-// 8 / (2 * D/32) key parts whose sums meet in LDS, and the waves of part 0
-// add the result into the fp32 dQ with atomic adds (which the memory side
-// performs; 256 keys per workgroup keep their number at T/256 per dQ
-// element).
+// the 256 keys is formed as 2 * D/32 blocks of 32x32 and added into the fp32
+// dQ with atomic adds (which the memory side performs; 256 keys per
+// workgroup keep their number at T/256 per dQ element). Waves 0..3 alone
+// issue the atomics, so a loader's wait for its prefetched tile never waits
+// on atomics too.
+//
+// Who forms dQ depends on the shape. D = 64 without dropout: each of waves
+// 0..3 forms one whole 32x32 block over all 256 keys while the loaders go on
+// to the next tile's S, P and dS; dS is double-buffered, so one barrier per
+// step suffices and the two waves that share a SIMD (w and w + 4) are out of
+// phase, one on the matrix cores while the other is on the vector unit.
+// Otherwise (D = 32, or dropout, whose keep-mask tiles leave no LDS for a
+// second dS buffer): every wave forms one block over a part of the keys,
+// the parts meet in LDS after a second barrier, and waves 0..3 add the sums.
 //
 // Precision: every product runs on fp16 MFMA with fp32 accumulation. Q, K,
 // V and dO are converted to fp16 when staged (exact for bf16 in fp16's
@@ -202,6 +211,26 @@ __device__ __forceinline__ void bwd_p_ds(const f32x16& s, const f32x16& dp, cons
   }
 }
 
+// dQ[queries qb0.., dims 32db..] += scale * acc for one 32x32 block, with
+// atomic adds; register r of lane (l32, hf) is query 8(r/4) + 4hf + r%4, dim
+// l32. Rows at or past T are skipped.
+__device__ __forceinline__ void add_dq_block(const BwdArgs& a, int head, int qb0, int db, int l32,
+                                             int hf, int T, float scale, const f32x16& acc) {
+  const int lddq = (int)a.ldq.t;
+  float* dqh = a.dq + head_base(a.ldq, head, a.H) + qb0 * lddq + db * 32 + l32;
+  if (qb0 + 32 <= T) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      atomicAdd(dqh + (8 * (r >> 2) + 4 * hf + (r & 3)) * lddq, acc[r] * scale);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qr = 8 * (r >> 2) + 4 * hf + (r & 3);
+      if (qb0 + qr < T) atomicAdd(dqh + qr * lddq, acc[r] * scale);
+    }
+  }
+}
+
 // Row strides inside one head are 32-bit (the host checks T * stride < 2^31);
 // head offsets are 64-bit.
 template <typename TIn, int D, bool DROP>
@@ -214,12 +243,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
   constexpr int kBlk = 2 * kDB;        // 32x32 blocks of a tile's dQ
   constexpr int kParts = 8 / kBlk;     // key parts per block (one wave each)
   constexpr int kSteps = kBK / 16 / kParts;  // 16-key MFMA steps per part
+  // Waves 0..3 form whole dQ blocks (see the top of the file) when there is
+  // one block per wave and LDS for a second dS buffer.
+  constexpr bool kSplit = !DROP && kBlk == 4;
+  constexpr int kNdS = kSplit ? 2 : 1;
   // All tiles fp16, row-major; transposed operands come from lds_operand_tr.
   __shared__ __attribute__((aligned(16))) f16 sK[kBK * kRowQ];          // [key][d]
   __shared__ __attribute__((aligned(16))) f16 sQ[2][kBQ * kRowQ];       // [q][d]
   __shared__ __attribute__((aligned(16))) f16 sdO[2][kBQ * kRowQ];      // [q][d]
-  __shared__ __attribute__((aligned(16))) f16 sdS[kBK * kRowS];         // [key][q]
-  __shared__ __attribute__((aligned(16))) float sPart[(kParts - 1) * kBlk][16][64];  // partial dQ
+  __shared__ __attribute__((aligned(16))) f16 sdS_buf[kNdS][kBK * kRowS];  // [key][q]
+  __shared__ __attribute__((aligned(16))) float sPart[kSplit ? 1 : (kParts - 1) * kBlk][16][64];
   __shared__ __attribute__((aligned(16))) float sL[2][kBQ];             // LSE * log2(e)
   __shared__ __attribute__((aligned(16))) float sD[2][kBQ];             // delta
   __shared__ __attribute__((aligned(16))) uint16_t sMask[DROP ? 8 : 1][DROP ? 32 * kRowM : 8];
@@ -298,6 +331,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
     if (loader && has_next)
       bwd_load_tile<TIn, D>(qh, ldq, doh, lddo, lseh, delh, qs + kBQ, T, ltid, nxt);
 
+    f16* sdS = sdS_buf[kSplit ? buf : 0];
     const f16* cQ = sQ[buf];
     const f16* cdO = sdO[buf];
     const float* cL = sL[buf];
@@ -384,10 +418,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
     __syncthreads();
 
     // dQ of the 64-query tile = dS K over the 256 keys, as kBlk 32x32 blocks
-    // (queries 32qb.., dims 32db..). Wave w takes block w % kBlk over key
-    // part w / kBlk (kSteps steps of 16 keys); the other parts pass their sums
-    // to part 0 through LDS, whose waves add the total into dQ with atomics.
-    // Every wave wrote its dS rows (zeros where nothing is visible).
+    // (queries 32qb.., dims 32db..). Every wave wrote its dS rows (zeros where
+    // nothing is visible).
+    if (kSplit) {
+      // Wave w < 4 forms block w over all keys and adds it into dQ; the
+      // loaders go straight on to the next tile. This step's dS buffer is
+      // rewritten two steps on, after the next barrier, which waves 0..3
+      // reach only after these reads.
+      if (!loader) {
+        const int qb = wave / kDB, db = wave % kDB;
+        const int qb0 = qs + qb * 32;
+        if (qb0 < T) {
+          f32x16 acc;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < kBK / 16; ++ks)
+            acc = mfma32x32x16_f16(lds_operand_tr(sdS, kRowS, ks * 16, qb * 32, lane),
+                                   lds_operand_tr(sK, kRowQ, ks * 16, db * 32, lane), acc);
+          add_dq_block(a, tm.head, qb0, db, l32, hf, T, scale, acc);
+        }
+      }
+      continue;
+    }
+    // Wave w takes block w % kBlk over key part w / kBlk (kSteps steps of 16
+    // keys); the other parts pass their sums to part 0 through LDS, whose
+    // waves add the total into dQ.
     const int blk = wave % kBlk, kpart = wave / kBlk;
     const int qb = blk / kDB, db = blk % kDB;
     const int qb0 = qs + qb * 32;
@@ -412,19 +468,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
       for (int p = 0; p < kParts - 1; ++p)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] += sPart[p * kBlk + blk][r][lane];
-      const int lddq = (int)a.ldq.t;
-      float* dqh = a.dq + head_base(a.ldq, tm.head, a.H) + qb0 * lddq + db * 32 + l32;
-      if (qb0 + 32 <= T) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          atomicAdd(dqh + (8 * (r >> 2) + 4 * hf + (r & 3)) * lddq, acc[r] * scale);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qr = 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (qb0 + qr < T) atomicAdd(dqh + qr * lddq, acc[r] * scale);
-        }
-      }
+      add_dq_block(a, tm.head, qb0, db, l32, hf, T, scale, acc);
     }
     // The next step's dS and half-sum writes come after its first barrier,
     // which every wave reaches only after the reads above.
