@@ -211,6 +211,34 @@ __device__ __forceinline__ void bwd_p_ds(const f32x16& s, const f32x16& dp, cons
   }
 }
 
+// rows[kw0 + k][d] = mul * acc for the wave's 32 keys k, through the wave's
+// LDS staging area (pitch D + 4 floats): register r of block db of lane
+// (l32, hf) is key l32, dim 32db + 8(r/4) + 4hf + r%4. Rows at or past T are
+// skipped. Wave-local: LDS runs one wave's operations in order.
+template <int D>
+__device__ __forceinline__ void store_rows(float* stage, const f32x16 (&acc)[D / 32], float mul,
+                                           float* rows, int ld, int kw0, int T, int l32, int hf,
+                                           int lane) {
+  constexpr int kEp = D + 4, kLpr = D / 4, kRpi = 64 / kLpr;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 x = {acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul, acc[db][4 * g + 2] * mul,
+                       acc[db][4 * g + 3] * mul};
+      *reinterpret_cast<f32x4*>(&stage[l32 * kEp + db * 32 + 8 * g + 4 * hf]) = x;
+    }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < 32 / kRpi; ++j) {
+    const int row = j * kRpi + lane / kLpr, col = (lane % kLpr) * 4;
+    if (kw0 + row < T)
+      *reinterpret_cast<f32x4*>(rows + (kw0 + row) * ld + col) =
+          *reinterpret_cast<const f32x4*>(&stage[row * kEp + col]);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 // dQ[queries qb0.., dims 32db..] += scale * acc for one 32x32 block, with
 // atomic adds; register r of lane (l32, hf) is query 8(r/4) + 4hf + r%4, dim
 // l32. Rows at or past T are skipped.
@@ -474,24 +502,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
     // which every wave reaches only after the reads above.
   }
 
-  // ---- epilogue: dV, dK = s * acc (lane: its key; 4 consecutive dims per store)
-  if (my_key < T) {
-    float* dvr = a.dv + head_base(a.ldv, tm.head, a.H) + my_key * a.ldv.t;
-    float* dkr = a.dk + head_base(a.ldk, tm.head, a.H) + my_key * a.ldk.t;
-#pragma unroll
-    for (int db2 = 0; db2 < kDB; ++db2)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = db2 * 32 + 8 * g + 4 * hf;
-        const float zs = DROP ? a.drop.scale : 1.f;
-        f32x4 x = {dvacc[db2][4 * g] * zs, dvacc[db2][4 * g + 1] * zs, dvacc[db2][4 * g + 2] * zs,
-                   dvacc[db2][4 * g + 3] * zs};
-        f32x4 y = {dkacc[db2][4 * g] * scale, dkacc[db2][4 * g + 1] * scale,
-                   dkacc[db2][4 * g + 2] * scale, dkacc[db2][4 * g + 3] * scale};
-        *reinterpret_cast<f32x4*>(dvr + d) = x;
-        *reinterpret_cast<f32x4*>(dkr + d) = y;
-      }
-  }
+  // ---- epilogue: dV = z * dV_acc, dK = s * dK_acc, written as whole rows.
+  // Each wave stages its 32 key rows in LDS (waves 0..3 in the K tile's
+  // space, waves 4..7 in the first dS buffer), then each store covers
+  // 64 / (D/4) complete rows, D/4 lanes of 16 bytes per row. The barrier
+  // ends the last step's reads of both areas.
+  __syncthreads();
+  constexpr int kEp = D + 4;  // staging row pitch, floats
+  static_assert(sizeof(sK) >= 4 * 32 * kEp * sizeof(float), "staging must fit in sK");
+  static_assert(sizeof(sdS_buf[0]) >= 4 * 32 * kEp * sizeof(float), "staging must fit in dS");
+  float* stage =
+      reinterpret_cast<float*>(wave < 4 ? static_cast<void*>(sK) : static_cast<void*>(sdS_buf[0])) +
+      (wave & 3) * 32 * kEp;
+  store_rows<D>(stage, dvacc, DROP ? a.drop.scale : 1.f, a.dv + head_base(a.ldv, tm.head, a.H),
+                (int)a.ldv.t, kw0, T, l32, hf, lane);
+  store_rows<D>(stage, dkacc, scale, a.dk + head_base(a.ldk, tm.head, a.H), (int)a.ldk.t, kw0, T,
+                l32, hf, lane);
 }
 
 template <typename TIn, int D>
