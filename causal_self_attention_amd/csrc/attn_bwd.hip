@@ -316,24 +316,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
   // K operands of S = Q K^T are the same row pieces of the staged K tile and
   // are read from LDS when used, which keeps 4 * D/16 registers free for the
   // scheduler.
-  f16x8 vf[D / 16];
+  // All 256 keys of K, row-major fp16, for the dQ product. Every load of the
+  // prologue is issued before any result is used (rows clamped to T - 1, so
+  // every address is valid; rows past T are zeroed when converted), so their
+  // latencies overlap.
+  constexpr int kKP = kBK * D / 8 / kThreads;  // K chunks per thread
+  vec kraw[kKP], vraw[D / 16];
+  const int vrow = min(my_key, T - 1);
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const bool ok = my_key < T;
-    vf[kk] = ok ? In16<TIn>::to_f16(*reinterpret_cast<const vec*>(vh + my_key * ldv + kk * 16 +
-                                                                  8 * hf))
-                : zero_f16x8();
-  }
-  // All 256 keys of K, row-major fp16, for the dQ product.
+  for (int kk = 0; kk < D / 16; ++kk)
+    vraw[kk] = *reinterpret_cast<const vec*>(vh + vrow * ldv + kk * 16 + 8 * hf);
 #pragma unroll
-  for (int p = 0; p < kBK * D / 8 / kThreads; ++p) {
+  for (int p = 0; p < kKP; ++p) {
     constexpr int kC = D / 8;
     const int c = tid + kThreads * p;  // key c/kC, 8 dims at (c%kC)*8
+    kraw[p] = *reinterpret_cast<const vec*>(kh + min(k0 + c / kC, T - 1) * ldk + (c % kC) * 8);
+  }
+  TileRegs<TIn, D> nxt;
+  if (loader) bwd_load_tile<TIn, D>(qh, ldq, doh, lddo, lseh, delh, k0, T, ltid, nxt);
+  f16x8 vf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    vf[kk] = my_key < T ? In16<TIn>::to_f16(vraw[kk]) : zero_f16x8();
+#pragma unroll
+  for (int p = 0; p < kKP; ++p) {
+    constexpr int kC = D / 8;
+    const int c = tid + kThreads * p;
     const int row = c / kC, col = (c % kC) * 8;
     *reinterpret_cast<f16x8*>(&sK[row * kRowQ + col]) =
-        k0 + row < T ? In16<TIn>::to_f16(*reinterpret_cast<const vec*>(kh + (k0 + row) * ldk +
-                                                                        col))
-                     : zero_f16x8();
+        k0 + row < T ? In16<TIn>::to_f16(kraw[p]) : zero_f16x8();
   }
 
   f32x16 dvacc[kDB], dkacc[kDB];
@@ -345,11 +356,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
       dkacc[db][r] = 0.f;
     }
 
-  TileRegs<TIn, D> nxt;
-  if (loader) {
-    bwd_load_tile<TIn, D>(qh, ldq, doh, lddo, lseh, delh, k0, T, ltid, nxt);
-    bwd_store_tile<TIn, D>(sQ[0], sdO[0], sL[0], sD[0], nxt, k0, T, ltid);
-  }
+  if (loader) bwd_store_tile<TIn, D>(sQ[0], sdO[0], sL[0], sD[0], nxt, k0, T, ltid);
   __syncthreads();
 
   int buf = 0;
