@@ -11,10 +11,13 @@ output, dO from and O into [B, T, C], fp32 dQ, dK, dV into one [B, T, 3C].
 backward (the keep mask regenerated in both); the FLOP count is unchanged.
 
 Timing: the timed region holds only the step's three launches, ``--steps``
-times (no event records between them; ``--graph`` replays them from a HIP
-graph instead, which measured slower than plain launches on this runtime);
-the per-kernel durations behind ``roofline`` come from HIP events around
-each launch in an equal number of separate eager steps.
+times, between two HIP events (nothing recorded between launches, since an
+event between two kernels adds a gap; ``--graph`` replays the step from a
+HIP graph instead, which measured slower than plain launches on this
+runtime). Per-kernel durations come from three more runs of ``--steps``
+back-to-back eager steps, each between two events: cut after the forward,
+cut after the preprocess, and whole; a kernel's duration is what it adds to
+the step.
 
 FLOPs are the causal algorithmic count: only the T(T+1)/2 unmasked (query,
 key) pairs per head, 4*D per pair forward (QK^T and PV) and 10*D per pair
@@ -27,8 +30,8 @@ second against the HBM roofline.
 
 Prints one JSON line. ``roofline`` describes the dominant kernel (the
 backward main kernel): its algorithmic FLOPs per launch over its average
-launch duration, timed with HIP events on the launch stream around each of
-its launches in the eager steps that precede the timed region. ``cpu_baseline`` times the fp64 oracle on a bounded sample of the
+launch duration, from ``--steps`` back-to-back launches of it between two
+HIP events on the launch stream. ``cpu_baseline`` times the fp64 oracle on a bounded sample of the
 same workload on the host cores.
 """
 from __future__ import annotations
@@ -132,22 +135,21 @@ def run_decode(args) -> int:
     for _ in range(args.warmup):
         gattn.gpt_attn_decode(q, k, v, lengths, o, lse, ws, stream)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # One step is one call (split + merge kernels): back-to-back calls between
+    # two HIP events on the launch stream, so the per-call duration behind
+    # the roofline is the timed region's time per step.
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
-    for a, b in ev:
-        a.record(stream)
+    for _ in range(args.steps):
         gattn.gpt_attn_decode(q, k, v, lengths, o, lse, ws, stream)
-        b.record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / args.steps
-    avg = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    avg = ms_per_step
     nbytes = decode_bytes(w, inp["lengths"].tolist())
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (avg * 1e-3) / 1e9
@@ -281,40 +283,32 @@ def main(argv=None) -> int:
                      dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    n_ev = args.steps
-    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(n_ev)] for name in ("fwd", "prep", "main")}
-
-    def step(i=None):
-        if i is None:
-            st = torch.cuda.current_stream(dev)  # the capture stream while capturing
-            fwd_call(q, k, v, o, o_lo, lse, st)
+    def step(upto=3):
+        """One step's launches on the current stream (the capture stream while
+        capturing); upto < 3 launches only the first `upto` kernels."""
+        st = torch.cuda.current_stream(dev)
+        fwd_call(q, k, v, o, o_lo, lse, st)
+        if upto > 1:
             prep_call(o, o_lo, do, dq, ws, st)
+        if upto > 2:
             main_call(q, k, v, do, lse, dq, dk, dv, ws, st)
-            return
-        a, b = ev["fwd"][i]
+
+    def timed(fn, n):
+        """ms per call of fn over n back-to-back calls, from two HIP events on
+        the launch stream around them (nothing recorded in between)."""
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         a.record(stream)
-        fwd_call(q, k, v, o, o_lo, lse, stream)
+        for _ in range(n):
+            fn()
         b.record(stream)
-        a, b = ev["prep"][i]
-        a.record(stream)
-        prep_call(o, o_lo, do, dq, ws, stream)
-        b.record(stream)
-        a, b = ev["main"][i]
-        a.record(stream)
-        main_call(q, k, v, do, lse, dq, dk, dv, ws, stream)
-        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
-    # Per-kernel durations: eager steps with HIP events on the launch stream.
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    avg = {name: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
-           for name, pairs in ev.items()}
 
     graph = None
     if args.graph:
@@ -331,6 +325,20 @@ def main(argv=None) -> int:
             graph.replay()
         torch.cuda.synchronize()
 
+    # Per-kernel durations by difference (before the timed region, which they
+    # also keep the clocks warm for): the same number of back-to-back eager
+    # steps cut after the forward, after the preprocess, and whole; each
+    # kernel's time is what it adds to its step (its launch gap included).
+    timed(step, args.steps)  # not used: brings the clocks to their working level
+    t_f = timed(lambda: step(1), args.steps)
+    t_fp = timed(lambda: step(2), args.steps)
+    t_all = timed(step, args.steps)
+    avg = {"fwd": t_f, "prep": t_fp - t_f, "main": t_all - t_fp}
+    # The dominant kernel alone: back-to-back launches between two events
+    # (its inputs are the last step's; each launch adds into dQ again).
+    t_main = timed(lambda: main_call(q, k, v, do, lse, dq, dk, dv, ws, stream), args.steps)
+
+    # The timed region: --steps whole steps, launches only.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -353,7 +361,7 @@ def main(argv=None) -> int:
         print("non-finite outputs", file=sys.stderr)
         return 1
 
-    main_tflops = bwd_flop / (avg["main"] * 1e-3) / 1e12
+    main_tflops = bwd_flop / (t_main * 1e-3) / 1e12
     traffic = (None if (fused or args.dropout > 0.0 or w.name != DEFAULT_WORKLOAD)
                else load_traffic(bwd_flop))
     out = {
@@ -386,7 +394,7 @@ def main(argv=None) -> int:
         "roofline": {"kernel": DOMINANT_KERNEL, "bound": "mfma",
                      "achieved": round(main_tflops, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(main_tflops / PEAK_MFMA_TFLOPS, 4),
-                     "avg_launch_ms": round(avg["main"], 5),
+                     "avg_launch_ms": round(t_main, 5),
                      "flop_per_launch": bwd_flop, "traffic": traffic},
         "wall_s_timed": round(wall, 4),
     }
