@@ -505,8 +505,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
         for (int r = 0; r < 16; ++r) acc[r] += sPart[p * kBlk + blk][r][lane];
       add_dq_block(a, tm.head, qb0, db, l32, hf, T, scale, acc);
     }
-    // The next step's dS and half-sum writes come after its first barrier,
-    // which every wave reaches only after the reads above.
+    // The next step's dS and partial-sum writes come after its first
+    // barrier, which every wave reaches only after the reads above.
   }
 
   // ---- epilogue: dV = z * dV_acc, dK = s * dK_acc, written as whole rows.
