@@ -178,9 +178,12 @@ def main():
                              300)
         stats = read_rows(find_csv(os.path.join(out, "trace"), "kernel_stats.csv"))
         lines = [f"# Kernel trace: {args.workload}", "",
-                 f"Workload: B={w.B} H={w.H} T={w.T} D={w.D} {w.dtype}, causal; 5 warm-up "
-                 "+ 20 timed steps of bench.py (one step = forward, backward prep, backward "
-                 "main).", "", "Command (run from /tmp with TMPDIR=/tmp; paths relative to the repository root):", "",
+                 f"Workload: B={w.B} H={w.H} T={w.T} D={w.D} {w.dtype}, causal. bench.py with "
+                 "--steps 20 --warmup 5: 5 warm-up steps (one step = forward, backward prep, "
+                 "backward main), then runs of 20 steps whole and cut after each kernel for "
+                 "the per-kernel times, 20 back-to-back backward-main launches for the "
+                 "roofline, and the 20 timed steps; every launch of each kernel is counted "
+                 "below.", "", "Command (run from /tmp with TMPDIR=/tmp; paths relative to the repository root):", "",
                  "    " + portable(cmd[4:]), "",
                  "| kernel | calls | avg us | min us | max us | share of GPU time |",
                  "|---|---|---|---|---|---|"]
