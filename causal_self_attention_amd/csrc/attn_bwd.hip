@@ -70,40 +70,56 @@ constexpr int row_of() {
 }
 
 // D/8 threads per (head, row), 8 elements each: row r of the flattened
-// [B*H, T] index space is head r / T, position r % T.
+// [B*H, T] index space is head r / T, position r % T. Each thread takes
+// kPrepRows rows (a block covers kPrepRows consecutive runs of 256/(D/8)
+// rows) and issues all of their loads before using any, which keeps more
+// bytes in flight per thread than one row would; rows past the end are
+// clamped for the loads and skipped for the stores.
+constexpr int kPrepRows = 4;
+
 template <typename TIn, int D>
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const BwdArgs a, int rows) {
   typedef typename In16<TIn>::vec vec;
-  constexpr int kTPR = D / 8;
-  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  const int row = (int)(gid / kTPR);  // rows < 2^31
-  const int part = (int)(gid % kTPR);
-  float acc = 0.f;
-  if (row < rows) {
-    const int hd = row / a.T, t = row - hd * a.T;
-    const TIn* o = static_cast<const TIn*>(a.o) + head_base(a.lo, hd, a.H) + t * a.lo.t;
-    const TIn* dout = static_cast<const TIn*>(a.dout) + head_base(a.ldo, hd, a.H) + t * a.ldo.t;
-    const vec x = *reinterpret_cast<const vec*>(o + part * 8);
-    const vec y = *reinterpret_cast<const vec*>(dout + part * 8);
-    if (a.o_lo) {
-      const TIn* o_lo =
-          static_cast<const TIn*>(a.o_lo) + head_base(a.llo, hd, a.H) + t * a.llo.t;
-      const vec c = *reinterpret_cast<const vec*>(o_lo + part * 8);
+  constexpr int kTPR = D / 8, kRPB = 256 / kTPR;  // threads per row, rows per pass
+  const int part = threadIdx.x % kTPR;
+  const long long row0 = (long long)blockIdx.x * (kRPB * kPrepRows) + threadIdx.x / kTPR;
+  vec x[kPrepRows], y[kPrepRows], c[kPrepRows];
+  int hd[kPrepRows], t[kPrepRows];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc = fmaf((float)x[i] + (float)c[i], (float)y[i], acc);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc = fmaf((float)x[i], (float)y[i], acc);
-    }
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    f32x4* dst = reinterpret_cast<f32x4*>(a.dq + head_base(a.ldq, hd, a.H) + t * a.ldq.t +
-                                          part * 8);
-    dst[0] = z;
-    dst[1] = z;
+  for (int i = 0; i < kPrepRows; ++i) {
+    const int row = (int)min(row0 + (long long)i * kRPB, (long long)rows - 1);  // rows < 2^31
+    hd[i] = row / a.T;
+    t[i] = row - hd[i] * a.T;
+    x[i] = *reinterpret_cast<const vec*>(static_cast<const TIn*>(a.o) + head_base(a.lo, hd[i], a.H) +
+                                         t[i] * a.lo.t + part * 8);
+    y[i] = *reinterpret_cast<const vec*>(static_cast<const TIn*>(a.dout) +
+                                         head_base(a.ldo, hd[i], a.H) + t[i] * a.ldo.t + part * 8);
+    if (a.o_lo)
+      c[i] = *reinterpret_cast<const vec*>(static_cast<const TIn*>(a.o_lo) +
+                                           head_base(a.llo, hd[i], a.H) + t[i] * a.llo.t + part * 8);
   }
 #pragma unroll
-  for (int m = 1; m < kTPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < rows && part == 0) a.delta[row] = acc;
+  for (int i = 0; i < kPrepRows; ++i) {
+    const long long row = row0 + (long long)i * kRPB;
+    float acc = 0.f;
+    if (a.o_lo) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)x[i][e] + (float)c[i][e], (float)y[i][e], acc);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)x[i][e], (float)y[i][e], acc);
+    }
+#pragma unroll
+    for (int m = 1; m < kTPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+    if (row < rows) {
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      f32x4* dst = reinterpret_cast<f32x4*>(a.dq + head_base(a.ldq, hd[i], a.H) + t[i] * a.ldq.t +
+                                            part * 8);
+      dst[0] = z;
+      dst[1] = z;
+      if (part == 0) a.delta[row] = acc;
+    }
+  }
 }
 
 // Loading a 64-query tile is split in two so the global loads can be issued
@@ -530,7 +546,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
 template <typename TIn, int D>
 hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
   const int rows = a.n_heads * a.T;
-  const unsigned blocks = (unsigned)(((long long)rows * (D / 8) + 255) / 256);
+  constexpr int kRowsPerBlock = 256 / (D / 8) * kPrepRows;
+  const unsigned blocks = (unsigned)(((long long)rows + kRowsPerBlock - 1) / kRowsPerBlock);
   hipLaunchKernelGGL((attn_bwd_prep_kernel<TIn, D>), dim3(blocks), dim3(256), 0, stream, a, rows);
   return hipGetLastError();
 }
