@@ -85,7 +85,7 @@ def load_traffic(n_launch_flop: int):
 
 def cpu_baseline(w, inp, max_heads: int, threads: int):
     """Oracle (fp64, plain C, threads over heads) on the first max_heads heads
-    of the same inputs: forward plus backward. Scaled to TFLOP/s with the
+    (by default all of them) of the same inputs: forward plus backward. Scaled to TFLOP/s with the
     same algorithmic FLOP count as the GPU figure."""
     import oracle
     n_heads = w.B * w.H
@@ -101,8 +101,9 @@ def cpu_baseline(w, inp, max_heads: int, threads: int):
     fl = 14 * w.D * pairs
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": min(threads, heads),
             "kind": "oracle",
-            "sample": f"{heads} of {n_heads} heads (T={w.T}, D={w.D}), forward + backward, "
-                      f"fp64, {dt:.2f} s wall"}
+            "sample": (f"all {n_heads} heads" if heads == n_heads else
+                       f"{heads} of {n_heads} heads") +
+                      f" (T={w.T}, D={w.D}), forward + backward, fp64, {dt:.2f} s wall"}
 
 
 def decode_bytes(w, lengths) -> int:
@@ -195,7 +196,7 @@ def main(argv=None) -> int:
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run 5 plain device-to-device copies of this many MiB (the "
                          "known-size reference for HBM byte counters) and exit")
-    ap.add_argument("--cpu-heads", type=int, default=64,
+    ap.add_argument("--cpu-heads", type=int, default=1 << 30,
                     help="heads of the workload the oracle baseline runs")
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--dropout", type=float, default=0.0,
