@@ -1,7 +1,7 @@
 // Causal attention backward, bf16 or fp16 inputs, fp32 accumulation and fp32
 // gradients, head dim D in {32, 64}, for gfx950 (CDNA4).
 //
-// The gradient of sum(dO * O) for O = softmax(Q K^T / sqrt(64), causal) V:
+// The gradient of sum(dO * O) for O = softmax(Q K^T / sqrt(D), causal) V:
 // what autograd forms for nanoGPT's loss.backward() through the fused
 // attention call (page "nanoGPT: a real GPT in two 300-line files", sections
 // 1 "Summary" and 2 "How the code works"). With s = 1/sqrt(D):
@@ -16,8 +16,9 @@
 // when the forward kept it, which restores fp32 accuracy) and zeroes dQ.
 // Kernel 2 (main): a workgroup of 8 waves owns 256 consecutive keys of one
 // head (32 per wave), stages their K in LDS, and keeps their V fragments and
-// dK, dV accumulators in registers. It walks the 64-query tiles from its diagonal to the end of
-// the sequence; each tile of Q and dO is staged once in LDS as row-major fp16
+// dK, dV accumulators in registers. It walks the 64-query tiles from its
+// diagonal to the end of the sequence; each tile of Q and dO is staged once
+// in LDS as row-major fp16
 // (waves 4..7 prefetch the next tile a step ahead into a second buffer), and
 // the transposed operands (Q^T, dO^T for dK^T += Q^T dS and dV^T += dO^T P)
 // come from transposing LDS reads. Per tile each wave recomputes P from the

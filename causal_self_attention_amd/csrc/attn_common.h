@@ -1,15 +1,17 @@
 // Device-side building blocks shared by the gfx950 attention kernels:
-// vector types, the bf16 MFMA wrapper and its register layout, conversions,
-// and the launch-side helpers the host code needs.
+// vector types, the MFMA wrappers for bf16 and fp16 operands and their
+// register layout, conversions, and the launch-side helpers the host code
+// needs.
 //
-// MFMA v_mfma_f32_32x32x16_bf16 (CDNA4), one wave of 64 lanes, lane l,
-// h = l / 32:
+// MFMA v_mfma_f32_32x32x16_bf16 / _f16 (CDNA4), one wave of 64 lanes, lane
+// l, h = l / 32:
 //   A (32 x 16, row-major M x K): lane l holds row l % 32, k = 8h .. 8h+7.
 //   B (16 x 32, K x N):           lane l holds col l % 32, k = 8h .. 8h+7.
 //   C (32 x 32, fp32, 16 regs):   lane l holds col l % 32; register v holds
 //                                 row 8 * (v / 4) + 4h + (v % 4).
-// These layouts are checked on the device by a layout test before any
-// kernel result is trusted.
+// These layouts were confirmed on the device with an in-bounds probe (every
+// element of a known product in the expected lane and register), and every
+// parity test of the kernels depends on them.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -62,7 +62,7 @@ struct FwdArgs {
   const void* k;
   const void* v;
   void* o;
-  void* o_lo;  // may be null (bf16 only)
+  void* o_lo;  // may be null (16-bit inputs only)
   float* lse;
   Layout lq, lk, lv, lo, llo;
   int n_heads, H, T;
@@ -74,7 +74,7 @@ struct BwdArgs {
   const void* k;
   const void* v;
   const void* o;
-  const void* o_lo;  // may be null (bf16 only)
+  const void* o_lo;  // may be null (16-bit inputs only)
   const void* dout;
   const float* lse;
   float* delta;
