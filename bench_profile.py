@@ -2,6 +2,7 @@
 into profiles/.
 
   python bench_profile.py [--out gpurun_out/prof] [--workload NAME]
+  python bench_profile.py --decode NAME     (a decode workload: trace + traffic)
 
 Summaries are written to <out>/summaries/ (copy them into profiles/ to
 commit them). Runs, each as its own rocprofv3 process over bench.py (the
@@ -130,11 +131,15 @@ def main():
                     help="run only the SQ counter passes -> sq_counters_<workload>.md")
     ap.add_argument("--summarize-only", action="store_true",
                     help="rebuild the summaries from CSVs already under --out")
+    ap.add_argument("--decode", default=None, metavar="NAME",
+                    help="profile bench.py --mode decode on decode workload NAME instead")
     args = ap.parse_args()
     global SUMMARIZE_ONLY
     SUMMARIZE_ONLY = args.summarize_only
     out = os.path.abspath(args.out)
     bench_py = os.path.join(ROOT, "bench.py")
+    if args.decode:
+        return profile_decode(args.decode, out, bench_py)
     from causal_self_attention_amd.inputs import WORKLOADS
     w = WORKLOADS[args.workload]
     short = args.workload
@@ -259,6 +264,79 @@ def main():
         with open(os.path.join(prof_dir, os.path.basename(bench.TRAFFIC_FILE)), "w") as f:
             json.dump(rec, f, indent=1)
     log("traffic summaries written")
+    return 0
+
+
+def copy_scales(out, bench_py):
+    """FETCH_SIZE and WRITE_SIZE of a plain device copy of known size: the
+    factors that turn the counters' KiB into bytes, and their commands."""
+    calib = [bench_py, "--calibrate-copy-mib", str(CALIB_MIB)]
+    scale, cmds = {}, []
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = os.path.join(out, f"pmc_{counter}_copy")
+        cmd, _ = run_rocprof(["--pmc", counter], calib, d, 120)
+        cmds.append(portable(cmd[4:]))
+        kib = max(v for v, n in counter_per_dispatch(find_csv(d, "counter_collection.csv"),
+                                                      counter).values())
+        scale[counter] = (CALIB_MIB << 20) / (kib * 1024.0)
+    return scale, cmds
+
+
+def profile_decode(name, out, bench_py):
+    """Kernel trace and HBM traffic of bench.py --mode decode on one decode
+    workload -> kernel_trace_<name>.md, hbm_traffic_<name>.md."""
+    from causal_self_attention_amd.inputs import DECODE_WORKLOADS, decode_inputs
+    w = DECODE_WORKLOADS[name]
+    prof_dir = os.path.join(out, "summaries")
+    os.makedirs(prof_dir, exist_ok=True)
+    base = [bench_py, "--mode", "decode", "--workload", name, "--no-cpu-baseline"]
+    tprog = base + ["--steps", "50", "--warmup", "10"]
+    d = os.path.join(out, f"trace_{name}")
+    cmd, _ = run_rocprof(["--kernel-trace", "--stats"], tprog, d, 300)
+    lines = [f"# Kernel trace: {name}", "",
+             f"Decode workload: B={w.B} sequences, H={w.H}, cache L={w.L}, D={w.D}, {w.dtype}"
+             f"{', lengths uniform in 1..L' if w.ragged else ''}. bench.py --mode decode: 10 "
+             "warm-up calls, then 50 timed calls (one call = split kernel + merge kernel).",
+             "", "Command (run from /tmp with TMPDIR=/tmp; paths relative to the repository "
+             "root):", "", "    " + portable(cmd[4:]), "",
+             "| kernel | calls | avg us | min us | max us | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for row in read_rows(find_csv(d, "kernel_stats.csv")):
+        lines.append("| {} | {} | {:.2f} | {:.2f} | {:.2f} | {:.1f}% |".format(
+            short_name(col(row, "Name", "KernelName", "Kernel_Name")), col(row, "Calls"),
+            float(col(row, "AverageNs")) / 1e3, float(col(row, "MinNs")) / 1e3,
+            float(col(row, "MaxNs")) / 1e3, float(col(row, "Percentage"))))
+    with open(os.path.join(prof_dir, f"kernel_trace_{name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("decode kernel trace summary written")
+
+    scale, cmds = copy_scales(out, bench_py)
+    pprog = base + ["--steps", "3", "--warmup", "1"]
+    res = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = os.path.join(out, f"pmc_{counter}_{name}")
+        cmd, _ = run_rocprof(["--pmc", counter], pprog, d, 120)
+        cmds.append(portable(cmd[4:]))
+        res[counter] = counter_per_dispatch(find_csv(d, "counter_collection.csv"), counter)
+    nbytes = bench.decode_bytes(w, decode_inputs(w, seed=0)["lengths"].tolist())
+    lines = [f"# HBM traffic per dispatch: {name}", "",
+             "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one rocprofv3 --pmc run "
+             f"each), scaled by what the same counters read for a plain {CALIB_MIB} MiB "
+             f"device copy: fetch x{scale['FETCH_SIZE']:.4f}, write x{scale['WRITE_SIZE']:.4f}. "
+             f"Algorithmic bytes of one call (split + merge): the cache rows read plus q, O "
+             f"and LSE, {nbytes / 1e6:.2f} MB.", "",
+             "Commands (run from /tmp with TMPDIR=/tmp; paths relative to the repository "
+             "root):", ""] + [f"    {c}" for c in cmds] + [
+             "", "| kernel | fetch MB | write MB | total MB |", "|---|---|---|---|"]
+    for k in sorted(res["FETCH_SIZE"]):
+        if k not in KERNELS:
+            continue
+        fk = res["FETCH_SIZE"][k][0] * 1024 * scale["FETCH_SIZE"]
+        wk = res["WRITE_SIZE"].get(k, (0.0, 0))[0] * 1024 * scale["WRITE_SIZE"]
+        lines.append(f"| {k} | {fk / 1e6:.2f} | {wk / 1e6:.2f} | {(fk + wk) / 1e6:.2f} |")
+    with open(os.path.join(prof_dir, f"hbm_traffic_{name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("decode traffic summary written")
     return 0
 
 

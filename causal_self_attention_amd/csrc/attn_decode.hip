@@ -189,13 +189,37 @@ __global__ __launch_bounds__(D) void attn_decode_merge_kernel(const DecArgs a, i
   }
   const int nc = (n + chunk - 1) / chunk;
   const float* part = a.part + (size_t)head * n_chunks * kDecPart;
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, part[c * kDecPart + kDecMax]);
-  float L = 0.f, O = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const float w = fast_exp2(part[c * kDecPart + kDecMax] - M);
-    L = fmaf(part[c * kDecPart + kDecSum], w, L);
-    O = fmaf(part[c * kDecPart + d], w, O);
+  // One pass with a running max (the online rule the split kernel uses),
+  // kMergeUnroll chunks at a time with every load issued before any is used,
+  // so the chunks cost one memory round trip per group rather than two each.
+  // Chunk 0 always holds keys (n > 0), so M is finite after the first group.
+  constexpr int kMergeUnroll = 4;
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int c0 = 0; c0 < nc; c0 += kMergeUnroll) {
+    float mc[kMergeUnroll], lc[kMergeUnroll], oc[kMergeUnroll];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int c = min(c0 + u, nc - 1);  // a valid chunk; repeats are dropped below
+      mc[u] = part[c * kDecPart + kDecMax];
+      lc[u] = part[c * kDecPart + kDecSum];
+      oc[u] = part[c * kDecPart + d];
+    }
+    float mx = M;
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u)
+      if (c0 + u < nc) mx = fmaxf(mx, mc[u]);
+    const float alpha = fast_exp2(M - mx);  // M = -inf on the first group: 0
+    L *= alpha;
+    O *= alpha;
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      if (c0 + u < nc) {
+        const float w = fast_exp2(mc[u] - mx);
+        L = fmaf(lc[u], w, L);
+        O = fmaf(oc[u], w, O);
+      }
+    }
+    M = mx;
   }
   store_out<TOut>(oh + d, O / L);
   if (d == 0) a.lse[head] = (M + fast_log2(L)) * kLn2;
