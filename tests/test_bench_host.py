@@ -1,0 +1,49 @@
+"""Host-side checks of the benchmark: its FLOP and byte arithmetic, and that it
+refuses a multi-GPU run before touching any device."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from types import SimpleNamespace
+
+import pytest
+
+import bench
+from causal_self_attention_amd.inputs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (workload, forward FLOP, backward FLOP): 4*D and 10*D per visible (query,
+# key) pair, B*H*T(T+1)/2 pairs per launch.
+FLOPS = [
+    ("shakespeare_char_f32_b1_h6_t256", 50_528_256, 126_320_640),
+    ("shakespeare_char_bf16_b64_h6_t256", 3_233_808_384, 8_084_520_960),
+    ("gpt2_124m_bf16_b12_h12_t1024", 19_346_227_200, 48_365_568_000),
+    ("gpt2_774m_sharp_bf16_b8_h20_t1024", 21_495_808_000, 53_739_520_000),
+    ("gpt2_1558m_bf16_b4_h25_t1024", 13_434_880_000, 33_587_200_000),
+    ("gpt2_1558m_long_bf16_b2_h25_t2048", 26_856_652_800, 67_141_632_000),
+]
+
+
+@pytest.mark.parametrize("name,fwd,bwd", FLOPS)
+def test_flop_counts(name, fwd, bwd):
+    assert bench.flops(WORKLOADS[name]) == (fwd, bwd)
+
+
+def test_decode_bytes_counts_rows_up_to_each_length():
+    w = SimpleNamespace(B=2, H=3, D=64, dtype="bf16")
+    # cache rows 5 + 7 per head, K and V, 2 bytes; q and O 2 bytes; LSE 4 bytes
+    expect = (5 + 7) * 3 * 64 * 2 * 2 + 2 * 2 * 3 * 64 * 2 + 4 * 2 * 3
+    assert bench.decode_bytes(w, [5, 7]) == expect
+    w32 = SimpleNamespace(B=1, H=1, D=32, dtype="f32")
+    assert bench.decode_bytes(w32, [0]) == 2 * 32 * 4 + 4
+
+
+@pytest.mark.parametrize("args,env", [(["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})])
+def test_more_than_one_gpu_is_refused(args, env):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                       env={**os.environ, **env}, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
