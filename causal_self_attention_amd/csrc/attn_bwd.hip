@@ -29,14 +29,13 @@
 // issue the atomics, so a loader's wait for its prefetched tile never waits
 // on atomics too.
 //
-// Who forms dQ depends on the shape. D = 64 without dropout: each of waves
-// 0..3 forms one whole 32x32 block over all 256 keys while the loaders go on
-// to the next tile's S, P and dS; dS is double-buffered, so one barrier per
-// step suffices and the two waves that share a SIMD (w and w + 4) are out of
-// phase, one on the matrix cores while the other is on the vector unit.
-// Otherwise (D = 32, or dropout, whose keep-mask tiles leave no LDS for a
-// second dS buffer): every wave forms one block over a part of the keys,
-// the parts meet in LDS after a second barrier, and waves 0..3 add the sums.
+// Who forms dQ depends on the shape. D = 64: each of waves 0..3 forms one
+// whole 32x32 block over all 256 keys while the loaders go on to the next
+// tile's S, P and dS; dS is double-buffered, so one barrier per step suffices
+// and the two waves that share a SIMD (w and w + 4) are out of phase, one on
+// the matrix cores while the other is on the vector unit. D = 32 (two
+// blocks): every wave forms one block over a part of the keys, the parts
+// meet in LDS after a second barrier, and waves 0..3 add the sums.
 //
 // Precision: every product runs on fp16 MFMA with fp32 accumulation. Q, K,
 // V and dO are converted to fp16 when staged (exact for bf16 in fp16's
@@ -46,9 +45,11 @@
 //
 // Attention dropout (a separate instantiation) regenerates the forward's
 // keep mask M: per 32x32 block each lane draws the Philox blocks of one query
-// and 16 keys, writes the 0 / 0xFFFF masks to a per-wave LDS tile, and reads
+// and 16 keys, writes the 0 / 0xFFFF masks to a 32 x 32 LDS tile, and reads
 // them back transposed (ds_read_b64_tr_b16) into its own register order (its
-// key, 8 consecutive queries). With z the survivor scale: dV accumulates
+// key, 8 consecutive queries). The tile is the window of the wave's own dS
+// rows that the block's dS overwrites afterwards, so it needs no LDS of its
+// own. With z the survivor scale: dV accumulates
 // (M P)^T dO and is scaled by z at the end, and dS = P (z M dP - delta);
 // delta = rowsum(dO * O) holds with dropout too (O is the dropped output).
 #include "attn_common.h"
@@ -62,7 +63,6 @@ constexpr int kBQ = 64;       // queries per step
 constexpr int kThreads = 512;
 constexpr int kLoaders = 256; // threads of waves 4..7: they alone load Q/dO tiles
 constexpr int kRowS = 72;     // row of the dS^T tile: 64 queries + 8 (144 bytes)
-constexpr int kRowM = 40;     // row of a wave's 32 x 32 keep-mask tile (80 bytes)
 
 // Padded LDS row of a D-wide 16-bit tile (D + 8 elements).
 template <int D>
@@ -289,8 +289,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
   constexpr int kParts = 8 / kBlk;     // key parts per block (one wave each)
   constexpr int kSteps = kBK / 16 / kParts;  // 16-key MFMA steps per part
   // Waves 0..3 form whole dQ blocks (see the top of the file) when there is
-  // one block per wave and LDS for a second dS buffer.
-  constexpr bool kSplit = !DROP && kBlk == 4;
+  // one block per wave (D = 64).
+  constexpr bool kSplit = kBlk == 4;
   constexpr int kNdS = kSplit ? 2 : 1;
   // All tiles fp16, row-major; transposed operands come from lds_operand_tr.
   __shared__ __attribute__((aligned(16))) f16 sK[kBK * kRowQ];          // [key][d]
@@ -300,7 +300,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
   __shared__ __attribute__((aligned(16))) float sPart[kSplit ? 1 : (kParts - 1) * kBlk][16][64];
   __shared__ __attribute__((aligned(16))) float sL[2][kBQ];             // LSE * log2(e)
   __shared__ __attribute__((aligned(16))) float sD[2][kBQ];             // delta
-  __shared__ __attribute__((aligned(16))) uint16_t sMask[DROP ? 8 : 1][DROP ? 32 * kRowM : 8];
 
   const int T = a.T;
   const TileMap tm = map_tile_xcd(blockIdx.x, a.n_heads, n_ktiles, false);
@@ -400,13 +399,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
         f16x8 mk[2];
         if (DROP) {
           // Lane L draws query qb0 + L/2, keys kw0 + 16 (L%2) .. +15 (two
-          // Philox blocks) into row L/2 of the wave's tile [query][key].
-          uint16_t* tile = sMask[wave];
+          // Philox blocks) into row L/2 of the wave's tile [query][key]. The
+          // tile lives in the 32 x 32 window of this wave's dS rows that the
+          // block's dS overwrites below, after the tile has been read back.
+          uint16_t* tile = reinterpret_cast<uint16_t*>(sdS + (wave * 32) * kRowS + mb * 32);
           uint32_t m0[4], m1[4];
           const uint32_t grp = (uint32_t)(kw0 >> 3) + 2u * (uint32_t)(lane & 1);
           keep_mask8(a.drop, (uint32_t)tm.head, (uint32_t)(qb0 + (lane >> 1)), grp, m0);
           keep_mask8(a.drop, (uint32_t)tm.head, (uint32_t)(qb0 + (lane >> 1)), grp + 1, m1);
-          i32x4* dst = reinterpret_cast<i32x4*>(tile + (lane >> 1) * kRowM + 16 * (lane & 1));
+          i32x4* dst = reinterpret_cast<i32x4*>(tile + (lane >> 1) * kRowS + 16 * (lane & 1));
           dst[0] = i32x4{(int)m0[0], (int)m0[1], (int)m0[2], (int)m0[3]};
           dst[1] = i32x4{(int)m1[0], (int)m1[1], (int)m1[2], (int)m1[3]};
           __builtin_amdgcn_wave_barrier();
@@ -428,9 +429,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
         }
         if (DROP) {
           // Lane (key l32, half hf): queries 16c + 8hf .. +7 of its key.
-          const f16* tile = reinterpret_cast<const f16*>(sMask[wave]);
+          const f16* tile = sdS + (wave * 32) * kRowS + mb * 32;
 #pragma unroll
-          for (int c = 0; c < 2; ++c) mk[c] = lds_operand_tr(tile, kRowM, 16 * c, 0, lane);
+          for (int c = 0; c < 2; ++c) mk[c] = lds_operand_tr(tile, kRowS, 16 * c, 0, lane);
           __builtin_amdgcn_wave_barrier();
         } else {
           mk[0] = mk[1] = zero_f16x8();
