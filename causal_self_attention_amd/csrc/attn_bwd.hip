@@ -22,7 +22,9 @@
 // (waves 4..7 prefetch the next tile a step ahead into a second buffer), and
 // the transposed operands (Q^T, dO^T for dK^T += Q^T dS and dV^T += dO^T P)
 // come from transposing LDS reads. Per tile each wave recomputes P from the
-// saved LSE, forms dS and writes its dS^T rows to LDS; then dQ = dS K over
+// saved LSE, forms dS and writes its dS^T rows to LDS (without dropout the
+// dP accumulators start from -delta, so the MFMA chain yields dP - delta
+// directly); then dQ = dS K over
 // the 256 keys is formed as 2 * D/32 blocks of 32x32 and added into the fp32
 // dQ with atomic adds (which the memory side performs; 256 keys per
 // workgroup keep their number at T/256 per dQ element). Waves 0..3 alone
@@ -174,13 +176,15 @@ __device__ __forceinline__ void bwd_store_tile(f16* sQ, f16* sdO, float* sL, flo
   if (tid < kBQ) {
     const bool ok = qs + tid < T;
     sL[tid] = ok ? r.lse * kLog2e : 0.f;
-    sD[tid] = ok ? r.del : 0.f;
+    sD[tid] = ok ? -r.del : 0.f;
   }
 }
 
 // P = exp2(S s log2(e) - LSE log2(e)) and dS = P (dP - delta) for the 16
 // (query, key) pairs of one lane in one 32x32 block, as fp16. Register
 // 8c + t of half hf is query q0 + 16c + 8hf + t; the lane's key is key0 + l32.
+// cD holds -delta. Without dropout the dP accumulator already holds
+// dP - delta (its MFMA chain started from -delta); with dropout it holds dP.
 template <int KIND, bool DROP>
 __device__ __forceinline__ void bwd_p_ds(const f32x16& s, const f32x16& dp, const float* cL,
                                          const float* cD, int qoff0, int q0, int key0, int T,
@@ -192,13 +196,15 @@ __device__ __forceinline__ void bwd_p_ds(const f32x16& s, const f32x16& dp, cons
     const int qoff = qoff0 + 16 * c + 8 * hf;
     const f32x4 L0 = *reinterpret_cast<const f32x4*>(&cL[qoff]);
     const f32x4 L1 = *reinterpret_cast<const f32x4*>(&cL[qoff + 4]);
-    const f32x4 E0 = *reinterpret_cast<const f32x4*>(&cD[qoff]);
-    const f32x4 E1 = *reinterpret_cast<const f32x4*>(&cD[qoff + 4]);
+    f32x4 E0 = {}, E1 = {};
+    if (DROP) {
+      E0 = *reinterpret_cast<const f32x4*>(&cD[qoff]);
+      E1 = *reinterpret_cast<const f32x4*>(&cD[qoff + 4]);
+    }
     float p[8], ds[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const float lse2 = t < 4 ? L0[t] : L1[t - 4];
-      const float del = t < 4 ? E0[t] : E1[t - 4];
       float pv = fast_exp2(fmaf(s[8 * c + t], scale_log2, -lse2));
       if (KIND == kDiag) {
         // key0 == q0: visible iff l32 <= 16c + 8hf + t.
@@ -211,9 +217,10 @@ __device__ __forceinline__ void bwd_p_ds(const f32x16& s, const f32x16& dp, cons
       if (DROP) {
         const uint32_t w = (uint32_t)__builtin_bit_cast(i32x4, mk[c])[t >> 1];
         const bool kept = (w >> (16 * (t & 1))) & 1u;
-        ds[t] = pv * ((kept ? dp[8 * c + t] * zscale : 0.f) - del);
+        const float ndel = t < 4 ? E0[t] : E1[t - 4];
+        ds[t] = pv * ((kept ? dp[8 * c + t] * zscale : 0.f) + ndel);
       } else {
-        ds[t] = pv * (dp[8 * c + t] - del);
+        ds[t] = pv * dp[8 * c + t];
       }
     }
     pf[c] = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
@@ -299,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
   __shared__ __attribute__((aligned(16))) f16 sdS_buf[kNdS][kBK * kRowS];  // [key][q]
   __shared__ __attribute__((aligned(16))) float sPart[kSplit ? 1 : (kParts - 1) * kBlk][16][64];
   __shared__ __attribute__((aligned(16))) float sL[2][kBQ];             // LSE * log2(e)
-  __shared__ __attribute__((aligned(16))) float sD[2][kBQ];             // delta
+  __shared__ __attribute__((aligned(16))) float sD[2][kBQ];             // -delta
 
   const int T = a.T;
   const TileMap tm = map_tile_xcd(blockIdx.x, a.n_heads, n_ktiles, false);
@@ -328,10 +335,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
   const int kw0 = k0 + wave * 32;
   const int my_key = kw0 + l32;  // the key column this lane owns
 
-  // V of this wave's 32 keys as fp16 B operands (lane: its key, 8 dims). The
-  // K operands of S = Q K^T are the same row pieces of the staged K tile and
-  // are read from LDS when used, which keeps 4 * D/16 registers free for the
-  // scheduler.
+  // V of this wave's 32 keys as fp16 B operands (lane: its key, 8 dims).
   // All 256 keys of K, row-major fp16, for the dQ product. Every load of the
   // prologue is issued before any result is used (rows clamped to T - 1, so
   // every address is valid; rows past T are zeroed when converted), so their
@@ -375,6 +379,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
   if (loader) bwd_store_tile<TIn, D>(sQ[0], sdO[0], sL[0], sD[0], nxt, k0, T, ltid);
   __syncthreads();
 
+  // The K operands of S = Q K^T (this wave's 32 keys): held in registers
+  // without dropout; the dropout build, short of registers, reads them from
+  // the staged K tile when used.
+  f16x8 kreg[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    kreg[kk] = DROP ? zero_f16x8()
+                    : *reinterpret_cast<const f16x8*>(
+                          &sK[(wave * 32 + l32) * kRowQ + kk * 16 + 8 * hf]);
   int buf = 0;
   for (int qs = k0; qs < T; qs += kBQ, buf ^= 1) {
     // Prefetch the next tile into registers while this one is computed.
@@ -412,17 +425,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
           dst[1] = i32x4{(int)m1[0], (int)m1[1], (int)m1[2], (int)m1[3]};
           __builtin_amdgcn_wave_barrier();
         }
+        // Without dropout the dP chain starts from -delta (register 8c + t of
+        // half hf is query qb0 + 16c + 8hf + t), so it ends at dP - delta.
         f32x16 s, dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[r] = 0.f;
-          dp[r] = 0.f;
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+        if (DROP) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+        } else {
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const f32x4 nd =
+                  *reinterpret_cast<const f32x4*>(&cD[mb * 32 + 16 * c + 8 * hf + 4 * h]);
+#pragma unroll
+              for (int t = 0; t < 4; ++t) dp[8 * c + 4 * h + t] = nd[t];
+            }
         }
         const int arow = (mb * 32 + perm32(l32)) * kRowQ + 8 * hf;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-          const f16x8 kfr =
-              *reinterpret_cast<const f16x8*>(&sK[(wave * 32 + l32) * kRowQ + kk * 16 + 8 * hf]);
+          const f16x8 kfr = DROP ? *reinterpret_cast<const f16x8*>(
+                                        &sK[(wave * 32 + l32) * kRowQ + kk * 16 + 8 * hf])
+                                  : kreg[kk];
           s = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cQ[arow + kk * 16]), kfr, s);
           dp = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cdO[arow + kk * 16]), vf[kk],
                                 dp);
