@@ -47,3 +47,11 @@ def test_more_than_one_gpu_is_refused(args, env):
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_committed_traffic_record_matches_the_kernel_source():
+    # The HBM-traffic record under profiles/ is keyed by a hash of the
+    # backward-main sources; a record taken on other source is reported as
+    # null by the benchmark, so the committed one must match the tree.
+    rec = bench.load_traffic(0)
+    assert rec is not None and rec > 0
