@@ -10,6 +10,13 @@ output, dO from and O into [B, T, C], fp32 dQ, dK, dV into one [B, T, 3C].
 ``--dropout P`` applies attention dropout at rate P in the forward and the
 backward (the keep mask regenerated in both); the FLOP count is unchanged.
 
+Data sets: MI355X keeps a 256 MB Infinity Cache in front of HBM, which one
+layer's attention tensors fit. A training step or a decode step of a real
+model touches each layer's tensors once, so consecutive steps here rotate
+over ``--sets`` independent copies of the inputs and outputs (by default as
+many as make at least 1 GiB), and no step finds its data left in that cache
+by the step before; ``--sets 1`` reuses one copy (a warm-cache figure).
+
 Timing: the timed region holds only the step's three launches, ``--steps``
 times, between two HIP events (nothing recorded between launches, since an
 event between two kernels adds a gap; ``--graph`` replays the step from a
@@ -49,6 +56,7 @@ if ROOT not in sys.path:
 
 PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0
+ROTATE_BYTES = 1 << 30  # data rotated over per run: 4x the 256 MB Infinity Cache
 DEFAULT_WORKLOAD = "gpt2_124m_bf16_b12_h12_t1024"
 DEFAULT_DECODE_WORKLOAD = "gpt2_124m_decode_bf16_b64_h12_l1024"
 DOMINANT_KERNEL = "attn_bwd_main_kernel"
@@ -106,6 +114,14 @@ def cpu_baseline(w, inp, max_heads: int, threads: int):
                       f" (T={w.T}, D={w.D}), forward + backward, fp64, {dt:.2f} s wall"}
 
 
+def n_sets(requested: int, set_bytes: int) -> int:
+    """Copies of the data to rotate over: ``requested`` if positive, else the
+    fewest whose total reaches ROTATE_BYTES (at most 16)."""
+    if requested > 0:
+        return requested
+    return max(1, min(16, -(-ROTATE_BYTES // max(1, set_bytes))))
+
+
 def decode_bytes(w, lengths) -> int:
     """Algorithmic bytes of one decode call: every cached K and V row up to
     each sequence's length, q, O (input dtype) and LSE (fp32)."""
@@ -126,15 +142,26 @@ def run_decode(args) -> int:
     w = DECODE_WORKLOADS[name]
     dev = torch.device("cuda:0")
     inp = decode_inputs(w, seed=args.seed)
-    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
     lengths = inp["lengths"].to(dev) if w.ragged else None
-    o = torch.empty_like(q)
-    lse = torch.empty(w.B, w.H, dtype=torch.float32, device=dev)
-    ws = torch.empty(max(1, gattn.gpt_attn_decode_workspace_bytes(w.dtype, w.B, w.H, w.L, w.D)
-                         // 4), dtype=torch.float32, device=dev)
+    esize = 4 if w.dtype == "f32" else 2
+    ns = n_sets(args.sets, 2 * w.B * w.H * w.L * w.D * esize)
+    sets = []
+    for _ in range(ns):
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty(w.B, w.H, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, gattn.gpt_attn_decode_workspace_bytes(w.dtype, w.B, w.H, w.L,
+                                                                      w.D) // 4),
+                         dtype=torch.float32, device=dev)
+        sets.append((q, k, v, o, lse, ws))
     stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
+
+    def call(i):
+        q, k, v, o, lse, ws = sets[i % ns]
         gattn.gpt_attn_decode(q, k, v, lengths, o, lse, ws, stream)
+
+    for i in range(args.warmup):
+        call(i)
     torch.cuda.synchronize()
     # One step is one call (split + merge kernels): back-to-back calls between
     # two HIP events on the launch stream, so the per-call duration behind
@@ -144,8 +171,8 @@ def run_decode(args) -> int:
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
-    for _ in range(args.steps):
-        gattn.gpt_attn_decode(q, k, v, lengths, o, lse, ws, stream)
+    for i in range(args.steps):
+        call(i)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -154,6 +181,7 @@ def run_decode(args) -> int:
     nbytes = decode_bytes(w, inp["lengths"].tolist())
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (avg * 1e-3) / 1e9
+    o, lse = sets[(args.steps - 1) % ns][3:5]
     if not (torch.isfinite(o.float()).all() and torch.isfinite(lse).all()):
         print("non-finite outputs", file=sys.stderr)
         return 1
@@ -163,7 +191,8 @@ def run_decode(args) -> int:
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "D": w.D,
-                   "ragged": w.ragged, "seed": args.seed, "bytes_per_step": nbytes},
+                   "ragged": w.ragged, "seed": args.seed, "bytes_per_step": nbytes,
+                   "data_sets": ns},
         "roofline": {"kernel": "attn_decode_split_kernel + attn_decode_merge_kernel",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -192,6 +221,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--sets", type=int, default=0,
+                    help="copies of the step's data to rotate over (0: enough for 1 GiB, so "
+                         "no step finds its data in the 256 MB Infinity Cache; 1: warm cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run 5 plain device-to-device copies of this many MiB (the "
@@ -250,26 +282,41 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     inp = workload_inputs(w, seed=args.seed)
     fused = args.layout == "fused"
+    E, R = w.B * w.H * w.T * w.D, w.B * w.H * w.T
+    esize = 2
+    # q, k, v, dO, O, o_lo (input type), fp32 dQ, dK, dV, LSE and delta.
+    ns = n_sets(args.sets, 6 * E * esize + 3 * E * 4 + 2 * R * 4)
+
+    def make_set():
+        if fused:
+            C = w.H * w.D
+            qkv = torch.empty(w.B, w.T, 3 * C, dtype=td, device=dev)
+            q, k, v = gattn.split_qkv_heads(qkv, w.H)
+            for view, name in ((q, "q"), (k, "k"), (v, "v")):
+                view.copy_(inp[name].to(dev))
+            do = gattn.merged_heads_view(torch.empty(w.B, w.T, C, dtype=td, device=dev), w.H)
+            do.copy_(inp["do"].to(dev))
+            o = gattn.merged_heads_view(torch.empty(w.B, w.T, C, dtype=td, device=dev), w.H)
+            dq, dk, dv = gattn.split_qkv_heads(
+                torch.empty(w.B, w.T, 3 * C, dtype=torch.float32, device=dev), w.H)
+        else:
+            q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+            o = torch.empty_like(q)
+            dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+            dk = torch.empty_like(dq)
+            dv = torch.empty_like(dq)
+        o_lo = torch.empty(q.shape, dtype=td, device=dev)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+        ws = torch.empty(gattn.gpt_attn_bwd_workspace_bytes(w.dtype, w.B, w.H, w.T, w.D) // 4,
+                         dtype=torch.float32, device=dev)
+        return dict(q=q, k=k, v=v, do=do, o=o, o_lo=o_lo, lse=lse, dq=dq, dk=dk, dv=dv, ws=ws)
+
+    sets = [make_set() for _ in range(ns)]
     if fused:
-        C = w.H * w.D
-        qkv = torch.empty(w.B, w.T, 3 * C, dtype=td, device=dev)
-        q, k, v = gattn.split_qkv_heads(qkv, w.H)
-        for view, name in ((q, "q"), (k, "k"), (v, "v")):
-            view.copy_(inp[name].to(dev))
-        do = gattn.merged_heads_view(torch.empty(w.B, w.T, C, dtype=td, device=dev), w.H)
-        do.copy_(inp["do"].to(dev))
-        o = gattn.merged_heads_view(torch.empty(w.B, w.T, C, dtype=td, device=dev), w.H)
-        dq, dk, dv = gattn.split_qkv_heads(
-            torch.empty(w.B, w.T, 3 * C, dtype=torch.float32, device=dev), w.H)
         fwd_call = gattn.gpt_attn_fwd_strided
         prep_call = gattn.gpt_attn_bwd_prep_strided
         main_call = gattn.gpt_attn_bwd_main_strided
     else:
-        q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
-        o = torch.empty_like(q)
-        dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
-        dk = torch.empty_like(dq)
-        dv = torch.empty_like(dq)
         fwd_call, prep_call, main_call = (gattn.gpt_attn_fwd, gattn.gpt_attn_bwd_prep,
                                           gattn.gpt_attn_bwd_main)
     if args.dropout > 0.0:
@@ -278,52 +325,61 @@ def main(argv=None) -> int:
         fwd_call = functools.partial(gattn.gpt_attn_fwd_strided, dropout=drop)
         prep_call = gattn.gpt_attn_bwd_prep_strided
         main_call = functools.partial(gattn.gpt_attn_bwd_main_strided, dropout=drop)
-    o_lo = torch.empty(q.shape, dtype=td, device=dev)
-    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
-    ws = torch.empty(gattn.gpt_attn_bwd_workspace_bytes(w.dtype, w.B, w.H, w.T, w.D) // 4,
-                     dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(upto=3):
-        """One step's launches on the current stream (the capture stream while
-        capturing); upto < 3 launches only the first `upto` kernels."""
+    def step(i, upto=3):
+        """Step i's launches on the current stream (the capture stream while
+        capturing), on data set i mod ns; upto < 3 launches only the first
+        `upto` kernels."""
+        d = sets[i % ns]
         st = torch.cuda.current_stream(dev)
-        fwd_call(q, k, v, o, o_lo, lse, st)
+        fwd_call(d["q"], d["k"], d["v"], d["o"], d["o_lo"], d["lse"], st)
         if upto > 1:
-            prep_call(o, o_lo, do, dq, ws, st)
+            prep_call(d["o"], d["o_lo"], d["do"], d["dq"], d["ws"], st)
         if upto > 2:
-            main_call(q, k, v, do, lse, dq, dk, dv, ws, st)
+            main_call(d["q"], d["k"], d["v"], d["do"], d["lse"], d["dq"], d["dk"], d["dv"],
+                      d["ws"], st)
+
+    def main_only(i):
+        d = sets[i % ns]
+        main_call(d["q"], d["k"], d["v"], d["do"], d["lse"], d["dq"], d["dk"], d["dv"], d["ws"],
+                  stream)
 
     def timed(fn, n):
-        """ms per call of fn over n back-to-back calls, from two HIP events on
-        the launch stream around them (nothing recorded in between)."""
+        """ms per call of fn(i), i = 0..n-1, over n back-to-back calls, from two
+        HIP events on the launch stream around them (nothing recorded in
+        between)."""
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a.record(stream)
-        for _ in range(n):
-            fn()
+        for i in range(n):
+            fn(i)
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(max(args.warmup, ns)):
+        step(i)
     torch.cuda.synchronize()
 
-    graph = None
+    graphs = None
     if args.graph:
+        # One graph per data set, each holding that set's step.
         side = torch.cuda.Stream(dev)
         side.wait_stream(torch.cuda.current_stream(dev))
         with torch.cuda.stream(side):
-            step()
+            step(0)
         torch.cuda.current_stream(dev).wait_stream(side)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        for _ in range(args.warmup):
-            graph.replay()
+        graphs = []
+        for j in range(ns):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(j)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % ns].replay()
         torch.cuda.synchronize()
 
     # Per-kernel durations by difference (before the timed region, which they
@@ -331,13 +387,14 @@ def main(argv=None) -> int:
     # steps cut after the forward, after the preprocess, and whole; each
     # kernel's time is what it adds to its step (its launch gap included).
     timed(step, args.steps)  # not used: brings the clocks to their working level
-    t_f = timed(lambda: step(1), args.steps)
-    t_fp = timed(lambda: step(2), args.steps)
+    t_f = timed(lambda i: step(i, 1), args.steps)
+    t_fp = timed(lambda i: step(i, 2), args.steps)
     t_all = timed(step, args.steps)
     avg = {"fwd": t_f, "prep": t_fp - t_f, "main": t_all - t_fp}
-    # The dominant kernel alone: back-to-back launches between two events
-    # (its inputs are the last step's; each launch adds into dQ again).
-    t_main = timed(lambda: main_call(q, k, v, do, lse, dq, dk, dv, ws, stream), args.steps)
+    # The dominant kernel alone: back-to-back launches between two events,
+    # rotating over the data sets like the steps (each set's inputs are from
+    # its last step; each launch adds into that set's dQ again).
+    t_main = timed(main_only, args.steps)
 
     # The timed region: --steps whole steps, launches only.
     t_start = torch.cuda.Event(enable_timing=True)
@@ -346,10 +403,10 @@ def main(argv=None) -> int:
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
-        if graph is not None:
-            graph.replay()
+        if graphs is not None:
+            graphs[i % ns].replay()
         else:
-            step()
+            step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -358,7 +415,8 @@ def main(argv=None) -> int:
     ms_per_step = total_ms / args.steps
     fwd_flop, bwd_flop = flops(w)
     value = (fwd_flop + bwd_flop) / (ms_per_step * 1e-3) / 1e12
-    if not (torch.isfinite(dq).all() and torch.isfinite(o.float()).all()):
+    last = sets[(args.steps - 1) % ns]
+    if not (torch.isfinite(last["dq"]).all() and torch.isfinite(last["o"].float()).all()):
         print("non-finite outputs", file=sys.stderr)
         return 1
 
@@ -381,7 +439,8 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "D": w.D,
                    "causal": True, "scale": 1.0 / w.D ** 0.5, "seed": args.seed,
                    "layout": "B,T,3C views" if fused else "BHTD", "dropout": args.dropout,
-                   "launch": "eager" if graph is None else "hip_graph",
+                   "launch": "eager" if graphs is None else "hip_graph",
+                   "data_sets": ns,
                    "pct_of_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2)},
         "fwd": {"ms": round(avg["fwd"], 5),
                 "tflops": round(fwd_flop / (avg["fwd"] * 1e-3) / 1e12, 2),

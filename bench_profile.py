@@ -187,7 +187,9 @@ def main():
                  "--steps 20 --warmup 5: 5 warm-up steps (one step = forward, backward prep, "
                  "backward main), then runs of 20 steps whole and cut after each kernel for "
                  "the per-kernel times, 20 back-to-back backward-main launches for the "
-                 "roofline, and the 20 timed steps; every launch of each kernel is counted "
+                 "roofline, and the 20 timed steps, each step and launch on the next of the "
+                 "rotated copies of the step's data (at least 1 GiB in all, so none finds its "
+                 "data in the 256 MB Infinity Cache); every launch of each kernel is counted "
                  "below.", "", "Command (run from /tmp with TMPDIR=/tmp; paths relative to the repository root):", "",
                  "    " + portable(cmd[4:]), "",
                  "| kernel | calls | avg us | min us | max us | share of GPU time |",
@@ -296,7 +298,9 @@ def profile_decode(name, out, bench_py):
     lines = [f"# Kernel trace: {name}", "",
              f"Decode workload: B={w.B} sequences, H={w.H}, cache L={w.L}, D={w.D}, {w.dtype}"
              f"{', lengths uniform in 1..L' if w.ragged else ''}. bench.py --mode decode: 10 "
-             "warm-up calls, then 50 timed calls (one call = split kernel + merge kernel).",
+             "warm-up calls, then 50 timed calls (one call = split kernel + merge kernel), "
+             "each on the next of the rotated copies of the cache (at least 1 GiB in all, so "
+             "none is found in the 256 MB Infinity Cache).",
              "", "Command (run from /tmp with TMPDIR=/tmp; paths relative to the repository "
              "root):", "", "    " + portable(cmd[4:]), "",
              "| kernel | calls | avg us | min us | max us | share of GPU time |",
