@@ -93,13 +93,18 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const BwdArgs a, int
     const int row = (int)min(row0 + (long long)i * kRPB, (long long)rows - 1);  // rows < 2^31
     hd[i] = row / a.T;
     t[i] = row - hd[i] * a.T;
-    x[i] = *reinterpret_cast<const vec*>(static_cast<const TIn*>(a.o) + head_base(a.lo, hd[i], a.H) +
-                                         t[i] * a.lo.t + part * 8);
-    y[i] = *reinterpret_cast<const vec*>(static_cast<const TIn*>(a.dout) +
-                                         head_base(a.ldo, hd[i], a.H) + t[i] * a.ldo.t + part * 8);
+    // Nontemporal loads: each row is read once here. (They measured 2%
+    // faster over a whole step, the main kernel's time included, with the
+    // step's data not already in the Infinity Cache.)
+    x[i] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(
+        static_cast<const TIn*>(a.o) + head_base(a.lo, hd[i], a.H) + t[i] * a.lo.t + part * 8));
+    y[i] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(
+        static_cast<const TIn*>(a.dout) + head_base(a.ldo, hd[i], a.H) + t[i] * a.ldo.t +
+        part * 8));
     if (a.o_lo)
-      c[i] = *reinterpret_cast<const vec*>(static_cast<const TIn*>(a.o_lo) +
-                                           head_base(a.llo, hd[i], a.H) + t[i] * a.llo.t + part * 8);
+      c[i] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(
+          static_cast<const TIn*>(a.o_lo) + head_base(a.llo, hd[i], a.H) + t[i] * a.llo.t +
+          part * 8));
   }
 #pragma unroll
   for (int i = 0; i < kPrepRows; ++i) {
