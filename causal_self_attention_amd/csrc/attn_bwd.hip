@@ -261,9 +261,9 @@ __device__ __forceinline__ void store_rows(float* stage, const f32x16 (&acc)[D /
 #pragma unroll
   for (int j = 0; j < 32 / kRpi; ++j) {
     const int row = j * kRpi + lane / kLpr, col = (lane % kLpr) * 4;
-    if (kw0 + row < T)
-      *reinterpret_cast<f32x4*>(rows + (kw0 + row) * ld + col) =
-          *reinterpret_cast<const f32x4*>(&stage[row * kEp + col]);
+    if (kw0 + row < T)  // nontemporal: nothing here reads dK, dV again
+      __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&stage[row * kEp + col]),
+                                  reinterpret_cast<f32x4*>(rows + (kw0 + row) * ld + col));
   }
   __builtin_amdgcn_wave_barrier();
 }

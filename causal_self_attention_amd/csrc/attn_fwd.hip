@@ -390,12 +390,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
       const int c = i * 64 + lane;
       const int row = c / kC, col = (c % kC) * 8;
       const int qrow = qw0 + row;
-      if (qrow < T) {
-        *reinterpret_cast<vec*>(ob + qrow * (int)a.lo.t + col) =
-            *reinterpret_cast<const vec*>(&so[row * kRow + col]);
+      if (qrow < T) {  // nontemporal: O is read again only by the backward
+        __builtin_nontemporal_store(*reinterpret_cast<const vec*>(&so[row * kRow + col]),
+                                    reinterpret_cast<vec*>(ob + qrow * (int)a.lo.t + col));
         if (lb)
-          *reinterpret_cast<vec*>(lb + qrow * (int)a.llo.t + col) =
-              *reinterpret_cast<const vec*>(&sl[row * kRow + col]);
+          __builtin_nontemporal_store(*reinterpret_cast<const vec*>(&sl[row * kRow + col]),
+                                      reinterpret_cast<vec*>(lb + qrow * (int)a.llo.t + col));
       }
     }
   }
