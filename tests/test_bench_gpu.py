@@ -51,6 +51,16 @@ def test_training_step_report():
     total = (19_346_227_200 + 48_365_568_000) / (d["ms_per_step"] * 1e-3) / 1e12
     assert abs(total - d["value"]) <= 0.01 * total
     assert "cpu_baseline" not in d
+    # The default rotates over enough copies of the step's data (228 MB each
+    # here) to exceed the 256 MB Infinity Cache several times over.
+    assert d["config"]["data_sets"] >= 4
+
+
+def test_training_step_warm_cache_option():
+    announce("bench.py train --sets 1 --steps 3")
+    d = run_bench("--sets", "1", "--steps", "3", "--warmup", "1", "--no-cpu-baseline")
+    check_common(d, 3)
+    assert d["config"]["data_sets"] == 1
 
 
 def test_decode_report():
@@ -59,3 +69,4 @@ def test_decode_report():
     r = check_common(d, 3)
     assert d["unit"] == "GB/s" and r["bound"] == "hbm" and r["peak"] == 8000.0
     assert d["config"]["bytes_per_step"] == r["bytes_per_launch"] > 0
+    assert d["config"]["data_sets"] >= 4
