@@ -55,3 +55,14 @@ def test_committed_traffic_record_matches_the_kernel_source():
     # null by the benchmark, so the committed one must match the tree.
     rec = bench.load_traffic(0)
     assert rec is not None and rec > 0
+
+
+def test_data_set_rotation_count():
+    # Enough copies of a step's data to reach 1 GiB (four times the 256 MB
+    # Infinity Cache), at most 16; an explicit count is taken as given.
+    assert bench.n_sets(0, 227_600_000) == 5   # GPT-2 124M training step
+    assert bench.n_sets(0, 201_326_592) == 6   # its 201 MB decode cache
+    assert bench.n_sets(0, 3 << 30) == 1
+    assert bench.n_sets(0, 1000) == 16
+    assert bench.n_sets(1, 227_600_000) == 1
+    assert bench.n_sets(3, 10) == 3
