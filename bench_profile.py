@@ -227,11 +227,12 @@ def main():
     fwd_flop, bwd_flop = bench.flops(w)
     E = w.B * w.H * w.T * w.D
     R = w.B * w.H * w.T
-    algo = {  # compulsory bytes per launch, bf16 inputs, fp32 gradients
-        "attn_fwd_kernel": 3 * 2 * E + 2 * 2 * E + 4 * R,            # q,k,v in; o, o_lo, lse out
-        "attn_bwd_prep_kernel": 3 * 2 * E + 4 * R + 4 * E,           # o, o_lo, dout in; delta, dq=0
-        "attn_bwd_main_kernel": 4 * 2 * E + 8 * R + 3 * 4 * E,       # q,k,v,dout,lse,delta; dq,dk,dv
-    }
+    stats = 16 * w.B * w.H * ((w.T + 127) // 128)  # per-chunk maxima in the workspace
+    algo = {  # compulsory bytes per launch of the plain calls, 16-bit inputs, fp32 gradients
+        "attn_fwd_kernel": 3 * 2 * E + 2 * E + 4 * R,                # q,k,v in; o, lse out
+        "attn_bwd_prep_kernel": 3 * 2 * E + 4 * R + 4 * E + stats,   # q,o,dout in; delta, dq=0
+        "attn_bwd_main_kernel": 4 * 2 * E + 8 * R + 3 * 4 * E + stats,  # q,k,v,dout,lse,delta,
+    }                                                                # maxima in; dq,dk,dv out
     lines = [f"# HBM traffic per dispatch: {args.workload}", "",
              f"Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one rocprofv3 --pmc run "
              f"each), scaled by what the same counters read for a plain {CALIB_MIB} MiB "

@@ -9,16 +9,17 @@ HIP kernels. If the library is missing or cannot be loaded, every call raises
 
 The names mirror the C entry points:
 
-  gpt_attn_fwd(q, k, v, o, o_lo, lse)                -> None (writes o, o_lo, lse)
-  gpt_attn_bwd(q, k, v, o, o_lo, dout, lse, dq, dk, dv, workspace) -> None
-  gpt_attn_bwd_prep(o, o_lo, dout, dq, workspace)     -> None (phase 1 of bwd)
+  gpt_attn_fwd(q, k, v, o, lse)                      -> None (writes o, lse)
+  gpt_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace) -> None
+  gpt_attn_bwd_prep(q, o, dout, dq, workspace)        -> None (phase 1 of bwd)
   gpt_attn_bwd_main(q, k, v, dout, lse, dq, dk, dv, workspace) -> None (phase 2)
-  gpt_attn_bwd_workspace_bytes(dtype, B, H, T, D)    -> int
+  gpt_attn_bwd_workspace_bytes(B, H, T, D)           -> int
   gpt_attn_status_string(status)                     -> str
   gpt_attn_abi_version()                             -> int
 
 and the strided forms gpt_attn_fwd_strided, gpt_attn_bwd_strided,
-gpt_attn_bwd_prep_strided, gpt_attn_bwd_main_strided (same arguments; each
+gpt_attn_bwd_prep_strided, gpt_attn_bwd_main_strided (the same arguments
+plus the optional o_lo, the low part of the forward's fp32 O; each
 tensor's own strides become its gpt_attn_layout; the forward and backward
 ones take an optional ``dropout=(p, seed, offset)``), gpt_attn_dropout_mask
 (the keep mask the kernels derive, written out), gpt_attn_decode (one query
@@ -65,7 +66,7 @@ EXPORTED_SYMBOLS = ("gpt_attn_fwd", "gpt_attn_bwd", "gpt_attn_bwd_prep", "gpt_at
                     "gpt_attn_decode_workspace_bytes", "gpt_attn_bwd_workspace_bytes",
                     "gpt_attn_status_string", "gpt_attn_abi_version")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class GptAttnLayout(ctypes.Structure):
@@ -113,10 +114,9 @@ def load_library():
         raise RuntimeError(f"{path} is not built; run `python -m causal_self_attention_amd.build`")
     lib = ctypes.CDLL(path)
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
-    lib.gpt_attn_fwd.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp]
+    lib.gpt_attn_fwd.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp]
     lib.gpt_attn_fwd.restype = i
-    lib.gpt_attn_bwd.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
-                                 vp]
+    lib.gpt_attn_bwd.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gpt_attn_bwd.restype = i
     lib.gpt_attn_bwd_prep.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
     lib.gpt_attn_bwd_prep.restype = i
@@ -131,7 +131,7 @@ def load_library():
                                          vp, lp, vp, vp, lp, vp, lp, vp, lp, vp, sz, dp_, vp]
     lib.gpt_attn_bwd_strided.restype = i
     lib.gpt_attn_bwd_prep_strided.argtypes = [i, i, i, i, i, vp, lp, vp, lp, vp, lp, vp, lp, vp,
-                                              sz, vp]
+                                              lp, vp, sz, vp]
     lib.gpt_attn_bwd_prep_strided.restype = i
     lib.gpt_attn_bwd_main_strided.argtypes = [i, i, i, i, i, vp, lp, vp, lp, vp, lp, vp, lp, vp,
                                               vp, lp, vp, lp, vp, lp, vp, sz, dp_, vp]
@@ -143,7 +143,7 @@ def load_library():
     lib.gpt_attn_decode.restype = i
     lib.gpt_attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.gpt_attn_decode_workspace_bytes.restype = sz
-    lib.gpt_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.gpt_attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.gpt_attn_bwd_workspace_bytes.restype = sz
     lib.gpt_attn_status_string.argtypes = [i]
     lib.gpt_attn_status_string.restype = ctypes.c_char_p
@@ -161,9 +161,8 @@ def gpt_attn_abi_version() -> int:
     return int(load_library().gpt_attn_abi_version())
 
 
-def gpt_attn_bwd_workspace_bytes(dtype: int | str, B: int, H: int, T: int, D: int) -> int:
-    code = DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
-    return int(load_library().gpt_attn_bwd_workspace_bytes(code, B, H, T, D))
+def gpt_attn_bwd_workspace_bytes(B: int, H: int, T: int, D: int) -> int:
+    return int(load_library().gpt_attn_bwd_workspace_bytes(B, H, T, D))
 
 
 # ---- marshalling helpers ------------------------------------------------------
@@ -225,22 +224,21 @@ def _bhtd(q):
     return tuple(int(x) for x in q.shape)
 
 
-def gpt_attn_fwd(q, k, v, o, o_lo, lse, stream=None) -> None:
+def gpt_attn_fwd(q, k, v, o, lse, stream=None) -> None:
     """Enqueue the forward on ``stream`` (default: torch's current stream)."""
     B, H, T, D = _bhtd(q)
     st = load_library().gpt_attn_fwd(_dtype_code(q), B, H, T, D, _ptr(q), _ptr(k), _ptr(v),
-                                     _ptr(o), _ptr(o_lo), _ptr(lse), _stream(q.device, stream))
+                                     _ptr(o), _ptr(lse), _stream(q.device, stream))
     if st != 0:
         raise GptAttnError("gpt_attn_fwd", st)
 
 
-def gpt_attn_bwd(q, k, v, o, o_lo, dout, lse, dq, dk, dv, workspace, stream=None) -> None:
+def gpt_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, stream=None) -> None:
     """Enqueue the backward on ``stream`` (default: torch's current stream)."""
     B, H, T, D = _bhtd(q)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load_library().gpt_attn_bwd(_dtype_code(q), B, H, T, D, _ptr(q), _ptr(k), _ptr(v),
-                                     _ptr(o), _ptr(o_lo), _ptr(dout), _ptr(lse), _ptr(dq),
-                                     _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
+                                     _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                                     _ptr(dv), _ptr(workspace), _ws_bytes(workspace),
                                      _stream(q.device, stream))
     if st != 0:
         raise GptAttnError("gpt_attn_bwd", st)
@@ -250,10 +248,11 @@ def _ws_bytes(workspace) -> int:
     return workspace.numel() * workspace.element_size() if workspace is not None else 0
 
 
-def gpt_attn_bwd_prep(o, o_lo, dout, dq, workspace, stream=None) -> None:
-    """Enqueue the backward's preprocess phase (delta, and dq zeroing)."""
+def gpt_attn_bwd_prep(q, o, dout, dq, workspace, stream=None) -> None:
+    """Enqueue the backward's preprocess phase (delta, per-chunk maxima, and
+    dq zeroing)."""
     B, H, T, D = _bhtd(o)
-    st = load_library().gpt_attn_bwd_prep(_dtype_code(o), B, H, T, D, _ptr(o), _ptr(o_lo),
+    st = load_library().gpt_attn_bwd_prep(_dtype_code(o), B, H, T, D, _ptr(q), _ptr(o),
                                           _ptr(dout), _ptr(dq), _ptr(workspace),
                                           _ws_bytes(workspace), _stream(o.device, stream))
     if st != 0:
@@ -306,12 +305,13 @@ def gpt_attn_bwd_strided(q, k, v, o, o_lo, dout, lse, dq, dk, dv, workspace,
         raise GptAttnError("gpt_attn_bwd_strided", st)
 
 
-def gpt_attn_bwd_prep_strided(o, o_lo, dout, dq, workspace, stream=None) -> None:
-    """gpt_attn_bwd_prep on [B, H, T, D] views (unit D stride)."""
+def gpt_attn_bwd_prep_strided(q, o, o_lo, dout, dq, workspace, stream=None) -> None:
+    """gpt_attn_bwd_prep on [B, H, T, D] views (unit D stride), with the
+    optional o_lo."""
     B, H, T, D = _bhtd(o)
-    _same_shape(o, o_lo, dout, dq)
+    _same_shape(o, q, o_lo, dout, dq)
     args = []
-    for t in (o, o_lo, dout, dq):
+    for t in (q, o, o_lo, dout, dq):
         args.extend(_sptr(t))
     st = load_library().gpt_attn_bwd_prep_strided(_dtype_code(o), B, H, T, D, *args,
                                                   _ptr(workspace), _ws_bytes(workspace),
@@ -456,7 +456,7 @@ def attention_backward(q, k, v, o, dout, lse, o_lo=None, stream=None, workspace=
     else:
         dq, dk, dv = grads
     if workspace is None:
-        nbytes = gpt_attn_bwd_workspace_bytes(_dtype_code(q), B, H, T, D)
+        nbytes = gpt_attn_bwd_workspace_bytes(B, H, T, D)
         workspace = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device=q.device)
     gpt_attn_bwd_strided(q, k, v, o, o_lo, dout, lse, dq, dk, dv, workspace, stream, dropout)
     return dq, dk, dv

@@ -72,45 +72,46 @@ constexpr int row_of() {
   return D + 8;
 }
 
-// D/8 threads per (head, row), 8 elements each: row r of the flattened
-// [B*H, T] index space is head r / T, position r % T. Each thread takes
-// kPrepRows rows (a block covers kPrepRows consecutive runs of 256/(D/8)
-// rows) and issues all of their loads before using any, which keeps more
-// bytes in flight per thread than one row would; rows past the end are
-// clamped for the loads and skipped for the stores.
-constexpr int kPrepRows = 4;
-
+// One workgroup per (head, chunk of kStatRows rows): D/8 threads per row,
+// 8 elements each, kStatRows * D / 2048 rows per thread. Every thread issues
+// all of its loads (q, o, o_lo, dout of each of its rows) before using any,
+// which keeps more bytes in flight per thread than one row would; rows past T
+// are clamped for the loads (they repeat row T - 1, which lies in the same
+// chunk) and skipped for the stores. Besides delta and the dQ zeros, the
+// workgroup records the largest |Q|, |dO| and |delta| of its chunk, from which
+// the main kernel sets its block exponents.
 template <typename TIn, int D>
-__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const BwdArgs a, int rows) {
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const BwdArgs a, int n_chunks) {
   typedef typename In16<TIn>::vec vec;
-  constexpr int kTPR = D / 8, kRPB = 256 / kTPR;  // threads per row, rows per pass
+  constexpr int kTPR = D / 8, kRPP = 256 / kTPR;  // threads per row, rows per pass
+  constexpr int kPass = kStatRows / kRPP;          // rows per thread
+  const int head = blockIdx.x / n_chunks, chunk = blockIdx.x - head * n_chunks;
+  const int T = a.T;
   const int part = threadIdx.x % kTPR;
-  const long long row0 = (long long)blockIdx.x * (kRPB * kPrepRows) + threadIdx.x / kTPR;
-  vec x[kPrepRows], y[kPrepRows], c[kPrepRows];
-  int hd[kPrepRows], t[kPrepRows];
+  const int r0 = chunk * kStatRows + threadIdx.x / kTPR;
+  const TIn* qh = static_cast<const TIn*>(a.q) + head_base(a.lq, head, a.H) + part * 8;
+  const TIn* oh = static_cast<const TIn*>(a.o) + head_base(a.lo, head, a.H) + part * 8;
+  const TIn* doh = static_cast<const TIn*>(a.dout) + head_base(a.ldo, head, a.H) + part * 8;
+  const TIn* loh =
+      a.o_lo ? static_cast<const TIn*>(a.o_lo) + head_base(a.llo, head, a.H) + part * 8 : nullptr;
+  vec xq[kPass], x[kPass], y[kPass], c[kPass];
 #pragma unroll
-  for (int i = 0; i < kPrepRows; ++i) {
-    const int row = (int)min(row0 + (long long)i * kRPB, (long long)rows - 1);  // rows < 2^31
-    hd[i] = row / a.T;
-    t[i] = row - hd[i] * a.T;
-    // Nontemporal loads: each row is read once here. (They measured 2%
-    // faster over a whole step, the main kernel's time included, with the
-    // step's data not already in the Infinity Cache.)
-    x[i] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(
-        static_cast<const TIn*>(a.o) + head_base(a.lo, hd[i], a.H) + t[i] * a.lo.t + part * 8));
-    y[i] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(
-        static_cast<const TIn*>(a.dout) + head_base(a.ldo, hd[i], a.H) + t[i] * a.ldo.t +
-        part * 8));
-    if (a.o_lo)
-      c[i] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(
-          static_cast<const TIn*>(a.o_lo) + head_base(a.llo, hd[i], a.H) + t[i] * a.llo.t +
-          part * 8));
+  for (int i = 0; i < kPass; ++i) {
+    const int t = min(r0 + i * kRPP, T - 1);
+    xq[i] = *reinterpret_cast<const vec*>(qh + t * a.lq.t);
+    // Nontemporal loads: o, o_lo and dout rows are read once here. (They
+    // measured 2% faster over a whole step, the main kernel's time included,
+    // with the step's data not already in the Infinity Cache.)
+    x[i] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(oh + t * a.lo.t));
+    y[i] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(doh + t * a.ldo.t));
+    if (loh) c[i] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(loh + t * a.llo.t));
   }
+  float mq = 0.f, mdo = 0.f, mdel = 0.f;
 #pragma unroll
-  for (int i = 0; i < kPrepRows; ++i) {
-    const long long row = row0 + (long long)i * kRPB;
+  for (int i = 0; i < kPass; ++i) {
+    const int t = r0 + i * kRPP;
     float acc = 0.f;
-    if (a.o_lo) {
+    if (loh) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc = fmaf((float)x[i][e] + (float)c[i][e], (float)y[i][e], acc);
     } else {
@@ -119,22 +120,45 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const BwdArgs a, int
     }
 #pragma unroll
     for (int m = 1; m < kTPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-    if (row < rows) {
+    fold_absmax(xq[i], mq);
+    fold_absmax(y[i], mdo);
+    mdel = fmaxf(mdel, fabsf(acc));
+    if (t < T) {
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      f32x4* dst = reinterpret_cast<f32x4*>(a.dq + head_base(a.ldq, hd[i], a.H) + t[i] * a.ldq.t +
+      f32x4* dst = reinterpret_cast<f32x4*>(a.dq + head_base(a.ldq, head, a.H) + t * a.ldq.t +
                                             part * 8);
       dst[0] = z;
       dst[1] = z;
-      if (part == 0) a.delta[row] = acc;
+      if (part == 0) a.delta[(size_t)head * T + t] = acc;
     }
+  }
+  __shared__ float red[4][3];
+  mq = wave_max(mq);
+  mdo = wave_max(mdo);
+  mdel = wave_max(mdel);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[wave][0] = mq;
+    red[wave][1] = mdo;
+    red[wave][2] = mdel;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    f32x4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) st[j] = fmaxf(st[j], red[w][j]);
+    reinterpret_cast<f32x4*>(a.stats)[(size_t)head * n_chunks + chunk] = st;
   }
 }
 
 // Loading a 64-query tile is split in two so the global loads can be issued
 // a whole step ahead: bwd_load_tile only issues raw loads (rows clamped to
 // T-1, so every address is valid, and nothing is computed from the results);
-// bwd_store_tile, a step later, zeroes rows past T, converts to fp16 and
-// writes the LDS buffers. Only the 256 threads of waves 4..7 take part (tid
+// bwd_store_tile, a step later, zeroes rows past T, scales Q by 2^eq and dO
+// by 2^edo while converting them to fp16, stores -delta * 2^(edo + ev) (the
+// scale of dP), and writes the LDS buffers. Only the 256 threads of waves 4..7 take part (tid
 // below is their index 0..255): each moves D/32 16-byte chunks of Q and of
 // dO (row c/(D/8), dims (c%(D/8))*8 for c = tid, tid+256, ...), and those
 // with tid < 64 also move the LSE and delta of row tid.
@@ -166,7 +190,7 @@ __device__ __forceinline__ void bwd_load_tile(const TIn* qh, int ldq, const TIn*
 template <typename TIn, int D>
 __device__ __forceinline__ void bwd_store_tile(f16* sQ, f16* sdO, float* sL, float* sD,
                                                const TileRegs<TIn, D>& r, int qs, int T,
-                                               int tid) {
+                                               int tid, int eq, int edo, int eds) {
   constexpr int kC = D / 8, kRowQ = row_of<D>();
 #pragma unroll
   for (int p = 0; p < TileRegs<TIn, D>::kN; ++p) {
@@ -174,14 +198,14 @@ __device__ __forceinline__ void bwd_store_tile(f16* sQ, f16* sdO, float* sL, flo
     const int row = c / kC, col = (c % kC) * 8;
     const bool ok = qs + row < T;
     *reinterpret_cast<f16x8*>(&sQ[row * kRowQ + col]) =
-        ok ? In16<TIn>::to_f16(r.q[p]) : zero_f16x8();
+        ok ? cvt_f16_scaled(r.q[p], eq) : zero_f16x8();
     *reinterpret_cast<f16x8*>(&sdO[row * kRowQ + col]) =
-        ok ? In16<TIn>::to_f16(r.d[p]) : zero_f16x8();
+        ok ? cvt_f16_scaled(r.d[p], edo) : zero_f16x8();
   }
   if (tid < kBQ) {
     const bool ok = qs + tid < T;
     sL[tid] = ok ? r.lse * kLog2e : 0.f;
-    sD[tid] = ok ? -r.del : 0.f;
+    sD[tid] = ok ? ldexpf(-r.del, eds) : 0.f;
   }
 }
 
@@ -240,21 +264,21 @@ __device__ __forceinline__ void bwd_p_ds(const f32x16& s, const f32x16& dp, cons
   }
 }
 
-// rows[kw0 + k][d] = mul * acc for the wave's 32 keys k, through the wave's
+// rows[kw0 + k][d] = mul * acc * 2^e for the wave's 32 keys k, through the wave's
 // LDS staging area (pitch D + 4 floats): register r of block db of lane
 // (l32, hf) is key l32, dim 32db + 8(r/4) + 4hf + r%4. Rows at or past T are
 // skipped. Wave-local: LDS runs one wave's operations in order.
 template <int D>
 __device__ __forceinline__ void store_rows(float* stage, const f32x16 (&acc)[D / 32], float mul,
-                                           float* rows, int ld, int kw0, int T, int l32, int hf,
-                                           int lane) {
+                                           int e, float* rows, int ld, int kw0, int T, int l32,
+                                           int hf, int lane) {
   constexpr int kEp = D + 4, kLpr = D / 4, kRpi = 64 / kLpr;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f32x4 x = {acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul, acc[db][4 * g + 2] * mul,
-                       acc[db][4 * g + 3] * mul};
+      const f32x4 x = {ldexpf(acc[db][4 * g] * mul, e), ldexpf(acc[db][4 * g + 1] * mul, e),
+                       ldexpf(acc[db][4 * g + 2] * mul, e), ldexpf(acc[db][4 * g + 3] * mul, e)};
       *reinterpret_cast<f32x4*>(&stage[l32 * kEp + db * 32 + 8 * g + 4 * hf]) = x;
     }
   __builtin_amdgcn_wave_barrier();
@@ -268,22 +292,23 @@ __device__ __forceinline__ void store_rows(float* stage, const f32x16 (&acc)[D /
   __builtin_amdgcn_wave_barrier();
 }
 
-// dQ[queries qb0.., dims 32db..] += scale * acc for one 32x32 block, with
-// atomic adds; register r of lane (l32, hf) is query 8(r/4) + 4hf + r%4, dim
+// dQ[queries qb0.., dims 32db..] += scale * acc * 2^e for one 32x32 block,
+// with atomic adds; register r of lane (l32, hf) is query 8(r/4) + 4hf + r%4, dim
 // l32. Rows at or past T are skipped.
 __device__ __forceinline__ void add_dq_block(const BwdArgs& a, int head, int qb0, int db, int l32,
-                                             int hf, int T, float scale, const f32x16& acc) {
+                                             int hf, int T, float scale, int e,
+                                             const f32x16& acc) {
   const int lddq = (int)a.ldq.t;
   float* dqh = a.dq + head_base(a.ldq, head, a.H) + qb0 * lddq + db * 32 + l32;
   if (qb0 + 32 <= T) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      atomicAdd(dqh + (8 * (r >> 2) + 4 * hf + (r & 3)) * lddq, acc[r] * scale);
+      atomicAdd(dqh + (8 * (r >> 2) + 4 * hf + (r & 3)) * lddq, ldexpf(acc[r] * scale, e));
   } else {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qr = 8 * (r >> 2) + 4 * hf + (r & 3);
-      if (qb0 + qr < T) atomicAdd(dqh + qr * lddq, acc[r] * scale);
+      if (qb0 + qr < T) atomicAdd(dqh + qr * lddq, ldexpf(acc[r] * scale, e));
     }
   }
 }
@@ -312,6 +337,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
   __shared__ __attribute__((aligned(16))) float sPart[kSplit ? 1 : (kParts - 1) * kBlk][16][64];
   __shared__ __attribute__((aligned(16))) float sL[2][kBQ];             // LSE * log2(e)
   __shared__ __attribute__((aligned(16))) float sD[2][kBQ];             // -delta
+  __shared__ float sRed[8][2];  // per wave: largest |K|, |V| of its keys
 
   const int T = a.T;
   const TileMap tm = map_tile_xcd(blockIdx.x, a.n_heads, n_ktiles, false);
@@ -359,17 +385,76 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
   }
   TileRegs<TIn, D> nxt;
   if (loader) bwd_load_tile<TIn, D>(qh, ldq, doh, lddo, lseh, delh, k0, T, ltid, nxt);
+
+  // Block exponents (see block_exp). K and V: this workgroup's 256 keys,
+  // reduced here; Q, dO and delta: every row the workgroup visits, from the
+  // preprocess pass's per-chunk maxima (chunks from k0 on; k0 is a multiple
+  // of kStatRows). Rows past T repeat row T - 1, one of this workgroup's.
+  float mk = 0.f, mv = 0.f, mq = 0.f, mdo = 0.f, mdel = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) fold_absmax(vraw[kk], mv);
+#pragma unroll
+  for (int p = 0; p < kKP; ++p) fold_absmax(kraw[p], mk);
+  {
+    const int n_chunks = (T + kStatRows - 1) / kStatRows;
+    const f32x4* st = reinterpret_cast<const f32x4*>(a.stats) + (size_t)tm.head * n_chunks;
+    for (int c = k0 / kStatRows + lane; c < n_chunks; c += 64) {
+      const f32x4 x = st[c];
+      mq = fmaxf(mq, x[0]);
+      mdo = fmaxf(mdo, x[1]);
+      mdel = fmaxf(mdel, x[2]);
+    }
+  }
+  mk = wave_max(mk);
+  mv = wave_max(mv);
+  mq = wave_max(mq);
+  mdo = wave_max(mdo);
+  mdel = wave_max(mdel);
+  if (lane == 0) {
+    sRed[wave][0] = mk;
+    sRed[wave][1] = mv;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    mk = fmaxf(mk, sRed[w][0]);
+    mv = fmaxf(mv, sRed[w][1]);
+  }
+  // Q and K to [2^13, 2^14) (only their fp16 range matters); V to [1, 2).
+  // dO: the largest exponent with |dS * 2^(edo + ev)| < 2^14, from
+  // |dS| <= z |dP| + |delta| <= z D max|dO| max|V| + max|delta| (z: the
+  // dropout survivor scale, 1 without dropout), so every rounded dS fits
+  // fp16 with a factor of two to spare.
+  const float zs = DROP ? a.drop.scale : 1.f;
+  const int ek = __builtin_amdgcn_readfirstlane(block_exp(mk, 13));
+  const int ev = __builtin_amdgcn_readfirstlane(block_exp(mv, 0));
+  const int eq = __builtin_amdgcn_readfirstlane(block_exp(mq, 13));
+  int edo = 0;
+  {
+    constexpr int kNone = -(1 << 20);
+    int t1 = kNone, t2 = kNone;
+    if (mdo > 0.f && mdo <= 3.402823466e38f) {
+      const int ka = __builtin_amdgcn_frexp_expf(mdo);  // mdo < 2^ka
+      const float x = zs * (float)D * ldexpf(mv, ev) * ldexpf(mdo, -ka);
+      t1 = ka + (x > 0.f ? __builtin_amdgcn_frexp_expf(x) : 0);  // z D max|dO| max|V_s| < 2^t1
+    }
+    if (mdel > 0.f && mdel <= 3.402823466e38f)
+      t2 = __builtin_amdgcn_frexp_expf(mdel) + ev;  // max|delta| 2^ev < 2^t2
+    if (t1 != kNone || t2 != kNone) edo = 13 - max(t1, t2);
+  }
+  edo = __builtin_amdgcn_readfirstlane(edo);
+
   f16x8 vf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    vf[kk] = my_key < T ? In16<TIn>::to_f16(vraw[kk]) : zero_f16x8();
+    vf[kk] = my_key < T ? cvt_f16_scaled(vraw[kk], ev) : zero_f16x8();
 #pragma unroll
   for (int p = 0; p < kKP; ++p) {
     constexpr int kC = D / 8;
     const int c = tid + kThreads * p;
     const int row = c / kC, col = (c % kC) * 8;
     *reinterpret_cast<f16x8*>(&sK[row * kRowQ + col]) =
-        k0 + row < T ? In16<TIn>::to_f16(kraw[p]) : zero_f16x8();
+        k0 + row < T ? cvt_f16_scaled(kraw[p], ek) : zero_f16x8();
   }
 
   f32x16 dvacc[kDB], dkacc[kDB];
@@ -381,8 +466,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
       dkacc[db][r] = 0.f;
     }
 
-  if (loader) bwd_store_tile<TIn, D>(sQ[0], sdO[0], sL[0], sD[0], nxt, k0, T, ltid);
+  if (loader) bwd_store_tile<TIn, D>(sQ[0], sdO[0], sL[0], sD[0], nxt, k0, T, ltid, eq, edo,
+                                     edo + ev);
   __syncthreads();
+
+  // With the operands scaled, S carries 2^(eq + ek), so the exponent's
+  // scale shrinks by that; dV carries 2^edo, dK 2^(edo + ev + eq) and each
+  // dQ block 2^(edo + ev + ek), removed when they are written.
+  const float sl2 = ldexpf(scale_log2, -(eq + ek));
+  const int e_dv = -edo, e_dk = -(edo + ev + eq), e_dq = -(edo + ev + ek);
 
   // The K operands of S = Q K^T (this wave's 32 keys): held in registers
   // without dropout; the dropout build, short of registers, reads them from
@@ -468,15 +560,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
         } else {
           mk[0] = mk[1] = zero_f16x8();
         }
-        const float zs = DROP ? a.drop.scale : 1.f;
         if (kind == kFull)
-          bwd_p_ds<kFull, DROP>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, scale_log2, mk, zs,
+          bwd_p_ds<kFull, DROP>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, sl2, mk, zs,
                                 pf, dsf);
         else if (kind == kDiag)
-          bwd_p_ds<kDiag, DROP>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, scale_log2, mk, zs,
+          bwd_p_ds<kDiag, DROP>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, sl2, mk, zs,
                                 pf, dsf);
         else
-          bwd_p_ds<kGeneral, DROP>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, scale_log2, mk,
+          bwd_p_ds<kGeneral, DROP>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, sl2, mk,
                                    zs, pf, dsf);
       }
 #pragma unroll
@@ -499,7 +590,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
     // previous step before its first barrier.
     if (loader && has_next)
       bwd_store_tile<TIn, D>(sQ[buf ^ 1], sdO[buf ^ 1], sL[buf ^ 1], sD[buf ^ 1], nxt, qs + kBQ,
-                             T, ltid);
+                             T, ltid, eq, edo, edo + ev);
     __syncthreads();
 
     // dQ of the 64-query tile = dS K over the 256 keys, as kBlk 32x32 blocks
@@ -521,7 +612,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
           for (int ks = 0; ks < kBK / 16; ++ks)
             acc = mfma32x32x16_f16(lds_operand_tr(sdS, kRowS, ks * 16, qb * 32, lane),
                                    lds_operand_tr(sK, kRowQ, ks * 16, db * 32, lane), acc);
-          add_dq_block(a, tm.head, qb0, db, l32, hf, T, scale, acc);
+          add_dq_block(a, tm.head, qb0, db, l32, hf, T, scale, e_dq, acc);
         }
       }
       continue;
@@ -553,13 +644,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
       for (int p = 0; p < kParts - 1; ++p)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] += sPart[p * kBlk + blk][r][lane];
-      add_dq_block(a, tm.head, qb0, db, l32, hf, T, scale, acc);
+      add_dq_block(a, tm.head, qb0, db, l32, hf, T, scale, e_dq, acc);
     }
     // The next step's dS and partial-sum writes come after its first
     // barrier, which every wave reaches only after the reads above.
   }
 
-  // ---- epilogue: dV = z * dV_acc, dK = s * dK_acc, written as whole rows.
+  // ---- epilogue: dV = z * dV_acc * 2^e_dv, dK = s * dK_acc * 2^e_dk, written
+  // as whole rows.
   // Each wave stages its 32 key rows in LDS (waves 0..3 in the K tile's
   // space, waves 4..7 in the first dS buffer), then each store covers
   // 64 / (D/4) complete rows, D/4 lanes of 16 bytes per row. The barrier
@@ -571,18 +663,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
   float* stage =
       reinterpret_cast<float*>(wave < 4 ? static_cast<void*>(sK) : static_cast<void*>(sdS_buf[0])) +
       (wave & 3) * 32 * kEp;
-  store_rows<D>(stage, dvacc, DROP ? a.drop.scale : 1.f, a.dv + head_base(a.ldv, tm.head, a.H),
-                (int)a.ldv.t, kw0, T, l32, hf, lane);
-  store_rows<D>(stage, dkacc, scale, a.dk + head_base(a.ldk, tm.head, a.H), (int)a.ldk.t, kw0, T,
-                l32, hf, lane);
+  store_rows<D>(stage, dvacc, zs, e_dv, a.dv + head_base(a.ldv, tm.head, a.H), (int)a.ldv.t, kw0,
+                T, l32, hf, lane);
+  store_rows<D>(stage, dkacc, scale, e_dk, a.dk + head_base(a.ldk, tm.head, a.H), (int)a.ldk.t,
+                kw0, T, l32, hf, lane);
 }
 
 template <typename TIn, int D>
 hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
-  const int rows = a.n_heads * a.T;
-  constexpr int kRowsPerBlock = 256 / (D / 8) * kPrepRows;
-  const unsigned blocks = (unsigned)(((long long)rows + kRowsPerBlock - 1) / kRowsPerBlock);
-  hipLaunchKernelGGL((attn_bwd_prep_kernel<TIn, D>), dim3(blocks), dim3(256), 0, stream, a, rows);
+  const int n_chunks = (int)bwd_stat_chunks(a.T);
+  const unsigned blocks = (unsigned)a.n_heads * (unsigned)n_chunks;
+  hipLaunchKernelGGL((attn_bwd_prep_kernel<TIn, D>), dim3(blocks), dim3(256), 0, stream, a,
+                     n_chunks);
   return hipGetLastError();
 }
 

@@ -137,6 +137,48 @@ __device__ __forceinline__ f16x8 zero_f16x8() {
   return __builtin_bit_cast(f16x8, z);
 }
 
+// Block exponents. The fp16 matrix-core operands carry a power-of-two scale
+// per operand block: x_s = x * 2^e is formed exactly (ldexp) before the
+// rounding to fp16, and every product of scaled operands is unscaled exactly
+// at the end, so fp16's narrow exponent range (normal 2^-14 .. 65504) costs
+// nothing while the block's largest magnitude sits near the top of it. A
+// scale that only moves the exponent commutes with every rounding in
+// between, so outputs are equivariant under power-of-two scaling of the
+// inputs.
+//
+// block_exp(m, target): the e with m * 2^e in [2^target, 2^(target+1)) for
+// finite m > 0, or 0 when m is 0 or not finite (a non-finite input gives
+// non-finite outputs whatever the scale). m = f * 2^k with f in [0.5, 1)
+// gives e = target + 1 - k.
+__device__ __forceinline__ int block_exp(float m, int target) {
+  if (!(m > 0.f) || !(m <= 3.402823466e38f)) return 0;
+  return target + 1 - __builtin_amdgcn_frexp_expf(m);
+}
+
+// Eight 16-bit values times 2^e, rounded to fp16: exact when the scaled
+// value is an fp16 normal number, as it is for every bf16 value of a block
+// down to 2^(-14-target) times the block's largest magnitude.
+template <typename V>
+__device__ __forceinline__ f16x8 cvt_f16_scaled(V x, int e) {
+  return pack_f16x8(ldexpf((float)x[0], e), ldexpf((float)x[1], e), ldexpf((float)x[2], e),
+                    ldexpf((float)x[3], e), ldexpf((float)x[4], e), ldexpf((float)x[5], e),
+                    ldexpf((float)x[6], e), ldexpf((float)x[7], e));
+}
+
+// Largest magnitude of eight 16-bit values folded into mx.
+template <typename V>
+__device__ __forceinline__ void fold_absmax(V x, float& mx) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf((float)x[i]));
+}
+
+// Maximum of a wave-uniform reduction over all 64 lanes.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+
 // The two 16-bit input types of the MFMA kernels. vec is eight elements (one
 // 16-byte load); mfma is the 32x32x16 product of two such operands with fp32
 // accumulation; to_f16 converts for the products that run in fp16 (exact for

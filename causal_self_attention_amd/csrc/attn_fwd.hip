@@ -48,6 +48,10 @@ constexpr int row_of() {
   return D + 8;
 }
 
+// bf16 V can leave fp16's range; fp16 V cannot.
+template <typename TIn>
+constexpr bool kScaleV = !__is_same(TIn, f16);
+
 // K/V tile loads are issued one tile ahead: fwd_load_tile only issues raw
 // 16-byte loads (rows clamped to T-1 so every address is valid);
 // fwd_store_tile zeroes rows past T and writes K (input type) and V (fp16,
@@ -73,9 +77,10 @@ __device__ __forceinline__ void fwd_load_tile(const TIn* kh, int ldk, const TIn*
   }
 }
 
+// For bf16, V is scaled by 2^vexp on its way to fp16 (see attn_fwd_kernel).
 template <typename TIn, int D>
 __device__ __forceinline__ void fwd_store_tile(TIn* Ks, f16* Vs, const KVRegs<TIn, D>& r, int k0,
-                                               int T, int tid) {
+                                               int T, int tid, int vexp) {
   typedef typename In16<TIn>::vec vec;
   constexpr int kC = D / 8, kRow = row_of<D>();
 #pragma unroll
@@ -84,9 +89,19 @@ __device__ __forceinline__ void fwd_store_tile(TIn* Ks, f16* Vs, const KVRegs<TI
     const int row = c / kC, col = (c % kC) * 8;
     const bool ok = k0 + row < T;
     *reinterpret_cast<vec*>(&Ks[row * kRow + col]) = ok ? r.k[p] : In16<TIn>::zero();
-    *reinterpret_cast<f16x8*>(&Vs[row * kRow + col]) =
-        ok ? In16<TIn>::to_f16(r.v[p]) : zero_f16x8();
+    const f16x8 vs = (!kScaleV<TIn> || vexp == 0) ? In16<TIn>::to_f16(r.v[p])
+                                                  : cvt_f16_scaled(r.v[p], vexp);
+    *reinterpret_cast<f16x8*>(&Vs[row * kRow + col]) = ok ? vs : zero_f16x8();
   }
+}
+
+// Largest |V| of the thread's chunks of a loaded tile.
+template <typename TIn, int D>
+__device__ __forceinline__ float tile_vmax(const KVRegs<TIn, D>& r) {
+  float m = 0.f;
+#pragma unroll
+  for (int p = 0; p < KVRegs<TIn, D>::kN; ++p) fold_absmax(r.v[p], m);
+  return m;
 }
 
 // Per-wave state of the online softmax.
@@ -245,6 +260,55 @@ __device__ __forceinline__ void fwd_half(const TIn* cK, const f16* cV,
   }
 }
 
+// V's block exponent for bf16 inputs. P V runs on fp16 operands; V is
+// staged as V * 2^vexp. The first K/V tile fixes vexp: 0 when its largest
+// |V| lies in [2^-4, 2^8) (every bf16 value of such a tile converts exactly,
+// bar fp16 subnormals, whose absolute error stays below 2^-21 of that
+// largest |V|), otherwise the exponent that puts it in [2^8, 2^9). A later
+// tile holding a |V| at or above vthr = 2^(15 - vexp) (or any nonzero V
+// when every V so far was zero) would leave fp16's range: the staging
+// threads flag it per wave, and after the barrier the workgroup lowers vexp
+// to fit the tile, rescales O's accumulators to match, and stages the
+// tile's V again. O is unscaled by 2^-vexp at the end.
+struct VScale {
+  int vexp;
+  float vthr;
+  bool set;  // some V so far was nonzero
+};
+
+__device__ __forceinline__ VScale vscale_first(float m0) {
+  VScale v;
+  v.set = m0 > 0.f;
+  v.vexp = (m0 >= 0.0625f && m0 < 256.f) ? 0 : block_exp(m0, 8);
+  v.vthr = !v.set ? 1.401298464e-45f : (m0 <= 3.402823466e38f ? ldexpf(1.f, 15 - v.vexp)
+                                                              : INFINITY);
+  return v;
+}
+
+// After the barrier that follows the staging of a tile into (Kb, Vb), when
+// some wave flagged the tile: move V's exponent down so that the tile fits,
+// rescale the O accumulators, and stage the tile again.
+template <typename TIn, int D>
+__device__ __forceinline__ void fwd_rescale_v(float* s_red, const KVRegs<TIn, D>& r, TIn* Kb,
+                                           f16* Vb, int k0, int T, int tid, int lane, int wave,
+                                           VScale& vs, FwdState<D>& st) {
+  const float m = wave_max(tile_vmax<TIn, D>(r));
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  const float mt = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  const int e_fit = block_exp(mt, 8);
+  const int e = vs.set ? min(vs.vexp, e_fit) : e_fit;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.oacc[db][i] = ldexpf(st.oacc[db][i], e - vs.vexp);
+  vs.vexp = __builtin_amdgcn_readfirstlane(e);
+  vs.set = true;
+  vs.vthr = mt <= 3.402823466e38f ? ldexpf(1.f, 15 - e) : INFINITY;
+  fwd_store_tile<TIn, D>(Kb, Vb, r, k0, T, tid, vs.vexp);
+  __syncthreads();
+}
+
 // Row strides inside one head are 32-bit (the host checks T * stride < 2^31);
 // head offsets are 64-bit.
 template <typename TIn, int D, bool DROP>
@@ -300,6 +364,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
     }
   }
 
+  __shared__ float s_vred[4];   // per wave: largest |V| of a tile
+  __shared__ __attribute__((aligned(16))) int s_vflag[2][4];  // per tile parity, wave: |V| too large
+  if (kScaleV<TIn>) {
+    const float m = wave_max(tile_vmax<TIn, D>(nxt));
+    if (lane == 0) s_vred[wave] = m;
+  }
+  __syncthreads();  // Q staged, tile 0's largest |V| known
+  VScale vs = {0, INFINITY, true};
+  if (kScaleV<TIn>)
+    vs = vscale_first(fmaxf(fmaxf(s_vred[0], s_vred[1]), fmaxf(s_vred[2], s_vred[3])));
+
   FwdState<D> st;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -314,14 +389,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
   // keys precede query q0 (and hence every query here) and lie below T.
   const int n_full = min(q0, T) / kBN;
 
-  fwd_store_tile<TIn, D>(Kbuf(0), Vbuf(0), nxt, 0, T, tid);
-  __syncthreads();
+  fwd_store_tile<TIn, D>(Kbuf(0), Vbuf(0), nxt, 0, T, tid, vs.vexp);
   // Q^T as the B operand: lane holds d = 16*kk + 8*hf .. +7 of its query.
   vec qf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
     qf[kk] = *reinterpret_cast<const vec*>(&Qs[(wave * 32 + l32) * kRow + kk * 16 + 8 * hf]);
-  __syncthreads();  // every wave holds its Q fragments: buffer 1 is free
+  __syncthreads();  // tile 0 staged; every wave holds its Q fragments: buffer 1 is free
 
   int buf = 0;
   int kt = 0;
@@ -331,8 +405,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
     if (has_next) fwd_load_tile<TIn, D>(kh, ldk, vh, ldv, k0 + kBN, T, tid, nxt);
     fwd_tile<TIn, D, DROP>(Kbuf(buf), Vbuf(buf), qf, k0, my_q, T, l32, hf, lane, scale_log2,
                            a.drop, tm.head, st);
-    if (has_next) fwd_store_tile<TIn, D>(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid);
+    if (has_next) {
+      fwd_store_tile<TIn, D>(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid, vs.vexp);
+      if (kScaleV<TIn>) {
+        const bool big = wave_any(tile_vmax<TIn, D>(nxt) >= vs.vthr);
+        if (lane == 0) s_vflag[kt & 1][wave] = big;
+      }
+    }
     __syncthreads();
+    if (kScaleV<TIn> && has_next) {
+      const i32x4 f = *reinterpret_cast<const i32x4*>(s_vflag[kt & 1]);
+      if (f[0] | f[1] | f[2] | f[3])
+        fwd_rescale_v<TIn, D>(s_vred, nxt, Kbuf(buf ^ 1), Vbuf(buf ^ 1), k0 + kBN, T, tid, lane,
+                              wave, vs, st);
+    }
   }
   for (; kt < n_kt; ++kt, buf ^= 1) {
     const int k0 = kt * kBN;
@@ -353,8 +439,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
         fwd_half<TIn, D, kGeneral, DROP>(Kbuf(buf), Vbuf(buf), qf, kb, k0, my_q, T, l32, hf,
                                          lane, scale_log2, a.drop, tm.head, st);
     }
-    if (has_next) fwd_store_tile<TIn, D>(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid);
+    if (has_next) {
+      fwd_store_tile<TIn, D>(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid, vs.vexp);
+      if (kScaleV<TIn>) {
+        const bool big = wave_any(tile_vmax<TIn, D>(nxt) >= vs.vthr);
+        if (lane == 0) s_vflag[kt & 1][wave] = big;
+      }
+    }
     __syncthreads();
+    if (kScaleV<TIn> && has_next) {
+      const i32x4 f = *reinterpret_cast<const i32x4*>(s_vflag[kt & 1]);
+      if (f[0] | f[1] | f[2] | f[3])
+        fwd_rescale_v<TIn, D>(s_vred, nxt, Kbuf(buf ^ 1), Vbuf(buf ^ 1), k0 + kBN, T, tid, lane,
+                              wave, vs, st);
+    }
   }
 
   // Epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2. The wave's O rows
@@ -362,7 +460,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
   // loop's last barrier, so that global stores write whole rows: D/8 lanes
   // per row, 16 bytes each.
   const float l_tot = st.l_run + wave_xor32(st.l_run);
-  const float inv = (DROP ? a.drop.scale : 1.f) / l_tot;
+  const float inv = ldexpf((DROP ? a.drop.scale : 1.f) / l_tot, -vs.vexp);
   {
     typedef typename In16<TIn>::vec4 vec4;
     TIn* so = lds_raw + (wave * 32) * kRow;        // O rows [query][d]

@@ -78,6 +78,7 @@ struct BwdArgs {
   const void* dout;
   const float* lse;
   float* delta;
+  float* stats;  // per (head, kStatRows-row chunk): max|Q|, max|dO|, max|delta|, 0
   float* dq;
   float* dk;
   float* dv;
@@ -85,6 +86,20 @@ struct BwdArgs {
   int n_heads, H, T;
   Dropout drop;  // drop.thr == 0: no dropout
 };
+
+// Backward workspace: delta [n_heads * T] fp32, then, from the next 16-byte
+// boundary, four floats per (head, chunk of kStatRows rows): the largest
+// |Q|, |dO| and |delta| of the chunk's rows and a zero. The 16-bit main
+// kernel sets its block exponents from them.
+constexpr int kStatRows = 128;
+
+inline long long bwd_stat_chunks(int T) { return ((long long)T + kStatRows - 1) / kStatRows; }
+
+inline long long bwd_stats_offset_bytes(long long rows) { return (rows * 4 + 15) / 16 * 16; }
+
+inline long long bwd_workspace_bytes(long long n_heads, int T) {
+  return bwd_stats_offset_bytes(n_heads * T) + 16 * n_heads * bwd_stat_chunks(T);
+}
 
 // One query per head against a key/value cache. q and o are [B, H, D]
 // (lq.t, lo.t unused), k and v [B, H, L, D]; lengths [B] (device, int32) or

@@ -125,7 +125,8 @@ int resolve_dropout(const gpt_attn_dropout* d, gpt_attn::Dropout* out) {
   } while (0)
 
 int check_workspace(const void* workspace, size_t bytes, const Shape& s) {
-  if (!workspace || bytes < (size_t)s.rows * sizeof(float)) return GPT_ATTN_E_WORKSPACE;
+  if (!workspace || bytes < (size_t)gpt_attn::bwd_workspace_bytes((long long)s.B * s.H, s.T))
+    return GPT_ATTN_E_WORKSPACE;
   if (!aligned16(workspace)) return GPT_ATTN_E_ALIGN;
   return GPT_ATTN_OK;
 }
@@ -142,7 +143,7 @@ int bwd_args(const Shape& s, int which, const void* q, const gpt_attn_layout* lq
   const bool prep = which & 1, main = which & 2;
   const bool half = s.dtype != GPT_ATTN_F32;  // 16-bit inputs: dQ by atomics, o_lo allowed
   if (!dout) return GPT_ATTN_E_INVAL;
-  if (prep && (!o || (half && !dq))) return GPT_ATTN_E_INVAL;
+  if (prep && (!o || (half && (!dq || !q)))) return GPT_ATTN_E_INVAL;
   if (main && (!q || !k || !v || !lse || !dq || !dk || !dv)) return GPT_ATTN_E_INVAL;
   if (o_lo && !half) return GPT_ATTN_E_INVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(o_lo) ||
@@ -156,6 +157,8 @@ int bwd_args(const Shape& s, int which, const void* q, const gpt_attn_layout* lq
   a->dout = dout;
   a->lse = lse;
   a->delta = static_cast<float*>(const_cast<void*>(workspace));
+  a->stats = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) +
+                                      gpt_attn::bwd_stats_offset_bytes(s.rows));
   a->dq = dq;
   a->dk = dk;
   a->dv = dv;
@@ -170,6 +173,7 @@ int bwd_args(const Shape& s, int which, const void* q, const gpt_attn_layout* lq
   a->ldv = resolve(ldv, s);
   GA_TRY(check_layout(a->ldo, s, s.esize, false));
   if (prep) {
+    if (half) GA_TRY(check_layout(a->lq, s, s.esize, false));
     GA_TRY(check_layout(a->lo, s, s.esize, false));
     if (o_lo) GA_TRY(check_layout(a->llo, s, 2, false));
   }
@@ -221,7 +225,7 @@ const char* gpt_attn_status_string(int status) {
     case GPT_ATTN_E_ALIGN:
       return "pointer not 16-byte aligned";
     case GPT_ATTN_E_WORKSPACE:
-      return "workspace missing or smaller than gpt_attn_bwd_workspace_bytes";
+      return "workspace missing or smaller than the size its *_workspace_bytes call gives";
     case GPT_ATTN_E_HIP:
       return "HIP runtime error at kernel launch";
     case GPT_ATTN_E_LAYOUT:
@@ -273,28 +277,28 @@ int gpt_attn_fwd_strided(int dtype, int B, int H, int T, int D, const void* q,
 }
 
 int gpt_attn_fwd(int dtype, int B, int H, int T, int D, const void* q, const void* k,
-                 const void* v, void* o, void* o_lo, float* lse, void* stream) {
+                 const void* v, void* o, float* lse, void* stream) {
   return gpt_attn_fwd_strided(dtype, B, H, T, D, q, nullptr, k, nullptr, v, nullptr, o, nullptr,
-                              o_lo, nullptr, lse, nullptr, stream);
+                              nullptr, nullptr, lse, nullptr, stream);
 }
 
-size_t gpt_attn_bwd_workspace_bytes(int dtype, int B, int H, int T, int D) {
+size_t gpt_attn_bwd_workspace_bytes(int B, int H, int T, int D) {
   Shape s;
-  if (check_shape(dtype, B, H, T, D, &s) != GPT_ATTN_OK) return 0;
-  return (size_t)s.rows * sizeof(float);
+  if (check_shape(GPT_ATTN_BF16, B, H, T, D, &s) != GPT_ATTN_OK || s.rows == 0) return 0;
+  return (size_t)gpt_attn::bwd_workspace_bytes((long long)B * H, T);
 }
 
-int gpt_attn_bwd_prep_strided(int dtype, int B, int H, int T, int D, const void* o,
-                              const gpt_attn_layout* lo, const void* o_lo,
-                              const gpt_attn_layout* llo, const void* dout,
+int gpt_attn_bwd_prep_strided(int dtype, int B, int H, int T, int D, const void* q,
+                              const gpt_attn_layout* lq, const void* o, const gpt_attn_layout* lo,
+                              const void* o_lo, const gpt_attn_layout* llo, const void* dout,
                               const gpt_attn_layout* ldo, float* dq, const gpt_attn_layout* ldq,
                               void* workspace, size_t workspace_bytes, void* stream) {
   Shape s;
   GA_TRY(check_shape(dtype, B, H, T, D, &s));
   if (s.rows == 0) return GPT_ATTN_OK;
   gpt_attn::BwdArgs a;
-  GA_TRY(bwd_args(s, 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, o, lo, o_lo, llo,
-                  dout, ldo, nullptr, dq, ldq, nullptr, nullptr, nullptr, nullptr, workspace,
+  GA_TRY(bwd_args(s, 1, q, lq, nullptr, nullptr, nullptr, nullptr, o, lo, o_lo, llo, dout, ldo,
+                  nullptr, dq, ldq, nullptr, nullptr, nullptr, nullptr, workspace,
                   workspace_bytes, nullptr, &a));
   return run_prep(s, a, static_cast<hipStream_t>(stream));
 }
@@ -337,11 +341,11 @@ int gpt_attn_bwd_strided(int dtype, int B, int H, int T, int D, const void* q,
   return run_main(s, a, st);
 }
 
-int gpt_attn_bwd_prep(int dtype, int B, int H, int T, int D, const void* o, const void* o_lo,
+int gpt_attn_bwd_prep(int dtype, int B, int H, int T, int D, const void* q, const void* o,
                       const void* dout, float* dq, void* workspace, size_t workspace_bytes,
                       void* stream) {
-  return gpt_attn_bwd_prep_strided(dtype, B, H, T, D, o, nullptr, o_lo, nullptr, dout, nullptr,
-                                   dq, nullptr, workspace, workspace_bytes, stream);
+  return gpt_attn_bwd_prep_strided(dtype, B, H, T, D, q, nullptr, o, nullptr, nullptr, nullptr,
+                                   dout, nullptr, dq, nullptr, workspace, workspace_bytes, stream);
 }
 
 int gpt_attn_bwd_main(int dtype, int B, int H, int T, int D, const void* q, const void* k,
@@ -353,11 +357,10 @@ int gpt_attn_bwd_main(int dtype, int B, int H, int T, int D, const void* q, cons
 }
 
 int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const void* k,
-                 const void* v, const void* o, const void* o_lo, const void* dout,
-                 const float* lse, float* dq, float* dk, float* dv, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+                 const void* v, const void* o, const void* dout, const float* lse, float* dq,
+                 float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream) {
   return gpt_attn_bwd_strided(dtype, B, H, T, D, q, nullptr, k, nullptr, v, nullptr, o, nullptr,
-                              o_lo, nullptr, dout, nullptr, lse, dq, nullptr, dk, nullptr, dv,
+                              nullptr, nullptr, dout, nullptr, lse, dq, nullptr, dk, nullptr, dv,
                               nullptr, workspace, workspace_bytes, nullptr, stream);
 }
 

@@ -14,8 +14,8 @@ Recipe (one ``torch.Generator('cpu')`` per call, seeded with ``seed``):
 The shapes are the attention layers of the models the nanoGPT pages train:
 the "baby GPT" Shakespeare-char model (6 heads of 64 channels, block size
 256), the smaller Shakespeare-char run on a laptop (4 heads of 32 channels,
-block size 64, batch 12) and GPT-2 124M / 774M / 1558M (12 / 20 / 25 heads
-of 64, block size 1024). The pages give no activation statistics, so i.i.d. N(0, 1) draws stand
+block size 64, batch 12) and GPT-2 124M / 350M / 774M / 1558M (12 / 16 / 20 /
+25 heads of 64, block size 1024). The pages give no activation statistics, so i.i.d. N(0, 1) draws stand
 in for real activations.
 
 Decode inputs (one new query per sequence against a key/value cache, as
@@ -57,6 +57,9 @@ WORKLOADS: dict[str, Workload] = {
         Workload("shakespeare_char_bf16_b64_h6_t256", "bf16", 64, 6, 256, 64),
         # GPT-2 124M attention layer.
         Workload("gpt2_124m_bf16_b12_h12_t1024", "bf16", 12, 12, 1024, 64),
+        # GPT-2 350M attention layer (16 heads of 64, block 1024) at the same
+        # batch of 12 sequences.
+        Workload("gpt2_350m_bf16_b12_h16_t1024", "bf16", 12, 16, 1024, 64),
         # GPT-2 774M attention layer with Q, K drawn at std 2 (sharper softmax).
         Workload("gpt2_774m_sharp_bf16_b8_h20_t1024", "bf16", 8, 20, 1024, 64, 2.0),
         # GPT-2 1558M attention layer, and the same heads at twice the context.

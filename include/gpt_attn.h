@@ -15,7 +15,8 @@
  * Flash Attention").
  *
  * Conventions shared by every entry point
- *   - Layout: q, k, v, o, o_lo, dout, dq, dk, dv are logically [B, H, T, D].
+ *   - Layout: q, k, v, o, dout, dq, dk, dv (and o_lo of the strided calls)
+ *     are logically [B, H, T, D].
  *     The plain entry points take them contiguous row-major; the *_strided
  *     ones take a gpt_attn_layout per operand (below), so that q, k, v can be
  *     read straight out of a projection's [B, T, 3C] output and o written
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GPT_ATTN_ABI_VERSION 5
+#define GPT_ATTN_ABI_VERSION 6
 
 /* Status codes returned by every int-returning entry point. */
 enum gpt_attn_status {
@@ -62,7 +63,7 @@ enum gpt_attn_status {
                                  o_lo given with GPT_ATTN_F32, bad dropout probability */
   GPT_ATTN_E_UNSUPPORTED = 2, /* a head dimension D with no kernel (D not 32 or 64) */
   GPT_ATTN_E_ALIGN = 3,       /* a pointer that is not 16-byte aligned */
-  GPT_ATTN_E_WORKSPACE = 4,   /* workspace NULL or smaller than gpt_attn_bwd_workspace_bytes */
+  GPT_ATTN_E_WORKSPACE = 4,   /* workspace NULL or smaller than the *_workspace_bytes size */
   GPT_ATTN_E_HIP = 5,         /* the HIP runtime reported an error when launching */
   GPT_ATTN_E_LAYOUT = 6       /* a gpt_attn_layout breaking the rules below */
 };
@@ -135,34 +136,46 @@ enum gpt_attn_dtype {
 };
 
 /*
+ * Precision of the 16-bit dtypes. Matrix products run on the gfx950 matrix
+ * cores with fp32 accumulation; the softmax statistics, delta and all
+ * sums are fp32. Q K^T of the forward multiplies the inputs in their own
+ * type. Every other product (P V of the forward, all five of the backward)
+ * takes fp16 operands, because the rounded operand (the probabilities P,
+ * the score gradient dS) keeps 11 significant bits in fp16 against bf16's
+ * 8. fp16's exponent range (normal 2^-14 .. 65504) is not a limit: each
+ * operand block is scaled by an exact power of two before the rounding to
+ * fp16 and unscaled after the product, the exponent chosen from the block's
+ * largest magnitude -- per workgroup for K and V, from the maxima the
+ * backward's first phase records for Q, dO and delta, and for the forward's
+ * V from the first key tile of each query block, lowered when a later tile
+ * would not fit. Power-of-two scaling of an input therefore scales the
+ * outputs it enters exactly, over bf16's whole range, as long as no fp32
+ * intermediate (the scores Q K^T / sqrt(D), the accumulated sums)
+ * overflows or falls below fp32's normal range. Non-finite inputs give
+ * non-finite outputs.
+ */
+
+/*
  * Forward: O = softmax(Q K^T / sqrt(D), causal) V and the log-sum-exp of
  * each row, LSE_i = ln sum_{j<=i} exp(Q_i . K_j / sqrt(D)) (natural log of
  * the scaled scores).
  *
  *   q, k, v  in   [B,H,T,D] of dtype
- *   o        out  [B,H,T,D] of dtype (bf16 output is rounded to nearest even)
- *   o_lo     out  OPTIONAL, 16-bit dtypes only (must be NULL for
- *                 GPT_ATTN_F32): [B,H,T,D] of dtype receiving round(O - o),
- *                 the part of the fp32 result that rounding o to the dtype
- *                 dropped. Passing it to gpt_attn_bwd gives the backward an O
- *                 accurate to about twice the dtype's precision, which its
- *                 delta = rowsum(dO * O) needs when softmax rows are sharp.
- *                 NULL skips the write.
+ *   o        out  [B,H,T,D] of dtype (16-bit output is rounded to nearest even)
  *   lse      out  [B,H,T] fp32; the backward needs it
  *
- * For bf16 and fp16, the P V product rounds P to fp16 and converts V to fp16,
- * which is exact for bf16 |v| in [2^-14, 65504]; bf16 inputs beyond fp16's
- * finite range give non-finite outputs.
+ * o, lse are bitwise reproducible run to run.
  */
 int gpt_attn_fwd(int dtype, int B, int H, int T, int D, const void* q, const void* k,
-                 const void* v, void* o, void* o_lo, float* lse, void* stream);
+                 const void* v, void* o, float* lse, void* stream);
 
 /*
- * Bytes of device workspace gpt_attn_bwd needs for this shape: the fp32
- * vector delta_i = sum_d dO_id O_id, [B,H,T]. Returns 0 for an invalid shape
- * or dtype, or an empty one.
+ * Bytes of device workspace the backward needs for this shape, for every
+ * dtype: the fp32 vector delta_i = sum_d dO_id O_id, [B,H,T], followed by 16
+ * bytes per (head, 128-row chunk) of per-chunk maxima the main phase reads.
+ * Returns 0 for an invalid or empty shape.
  */
-size_t gpt_attn_bwd_workspace_bytes(int dtype, int B, int H, int T, int D);
+size_t gpt_attn_bwd_workspace_bytes(int B, int H, int T, int D);
 
 /*
  * Backward: the gradient of sum(dout * O) with respect to Q, K and V,
@@ -171,9 +184,6 @@ size_t gpt_attn_bwd_workspace_bytes(int dtype, int B, int H, int T, int D);
  *
  *   q, k, v      in   [B,H,T,D] of dtype (the forward's inputs)
  *   o            in   [B,H,T,D] of dtype (the forward's output)
- *   o_lo         in   OPTIONAL, 16-bit dtypes only: the forward's o_lo
- *                     output; when given, delta uses o + o_lo instead of o.
- *                     Must be NULL for GPT_ATTN_F32.
  *   dout         in   [B,H,T,D] of dtype (upstream gradient dL/dO)
  *   lse          in   [B,H,T] fp32 (the forward's output)
  *   dq, dk, dv   out  [B,H,T,D] fp32, fully overwritten
@@ -181,16 +191,19 @@ size_t gpt_attn_bwd_workspace_bytes(int dtype, int B, int H, int T, int D);
  *                bytes, device memory owned by the caller; contents on entry
  *                are ignored and on return are unspecified.
  *
- * For bf16 and fp16, every product runs on fp16 matrix cores: q, k, v, dout
- * are converted to fp16 (exact for bf16 magnitudes in [2^-14, 65504]) and P
- * and dS are rounded to fp16. dk, dv (and o, lse from gpt_attn_fwd) are
- * bitwise reproducible run to run. dq is accumulated with fp32 atomic adds
- * for the 16-bit dtypes, so its low bits may vary between runs.
+ * delta is formed from o as stored. For the 16-bit dtypes that is O rounded
+ * to the dtype, and the rounding enters dq and dk through delta: with sharp
+ * softmax rows (scores of standard deviation 4, keys concentrated on one
+ * value row) dq then misses the 2e-2 max-abs bar of bf16 parity. The strided
+ * calls below take the forward's optional o_lo, the part of the fp32 O that
+ * the rounding dropped, and remove that error.
+ *
+ * dk, dv are bitwise reproducible run to run. dq is accumulated with fp32
+ * atomic adds for the 16-bit dtypes, so its low bits may vary between runs.
  */
 int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const void* k,
-                 const void* v, const void* o, const void* o_lo, const void* dout,
-                 const float* lse, float* dq, float* dk, float* dv, void* workspace,
-                 size_t workspace_bytes, void* stream);
+                 const void* v, const void* o, const void* dout, const float* lse, float* dq,
+                 float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The two phases of gpt_attn_bwd as separate calls, for callers that
@@ -198,16 +211,17 @@ int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const voi
  * gpt_attn_bwd_prep(...) followed by gpt_attn_bwd_main(...) on one stream.
  *
  * gpt_attn_bwd_prep: the preprocess pass. Writes delta_i = sum_d dout_id O_id
- *   (O = o, or o + o_lo when o_lo is given) into the first B*H*T floats of
- *   workspace; for the 16-bit dtypes it also zero-fills dq, which the main
- *   phase accumulates into (dq may be NULL for GPT_ATTN_F32 and is not
- *   touched).
- * gpt_attn_bwd_main: everything else. Reads delta from workspace, which must
- *   hold the prep phase's result for the same o and dout (and, for the 16-bit
+ *   into the workspace; for the 16-bit dtypes it also zero-fills dq, which
+ *   the main phase accumulates into, and records the largest |q|, |dout| and
+ *   |delta| of every 128-row chunk of each head, from which the main phase
+ *   sets its operand scales (q and dq may be NULL for GPT_ATTN_F32 and are
+ *   not touched).
+ * gpt_attn_bwd_main: everything else. Reads the workspace, which must hold
+ *   the prep phase's result for the same q, o and dout (and, for the 16-bit
  *   dtypes, dq must still hold the prep phase's zeros). Writes dq, dk, dv.
  *   Arguments mean what they mean for gpt_attn_bwd.
  */
-int gpt_attn_bwd_prep(int dtype, int B, int H, int T, int D, const void* o, const void* o_lo,
+int gpt_attn_bwd_prep(int dtype, int B, int H, int T, int D, const void* q, const void* o,
                       const void* dout, float* dq, void* workspace, size_t workspace_bytes,
                       void* stream);
 int gpt_attn_bwd_main(int dtype, int B, int H, int T, int D, const void* q, const void* k,
@@ -218,12 +232,20 @@ int gpt_attn_bwd_main(int dtype, int B, int H, int T, int D, const void* q, cons
  * Strided forms of the four calls above: each operand pointer is followed by
  * its layout (NULL = contiguous [B,H,T,D]). Operand meanings, dtypes,
  * workspace and errors are those of the plain entry points, which are these
- * calls with every layout NULL and no dropout. lse and the workspace's delta
- * stay contiguous [B,H,T]. gpt_attn_bwd_main_strided expects dq in the
+ * calls with every layout NULL, no o_lo and no dropout. lse and the
+ * workspace stay contiguous. gpt_attn_bwd_main_strided expects dq in the
  * layout the preceding gpt_attn_bwd_prep_strided zero-filled.
+ *
+ * o_lo (16-bit dtypes only; must be NULL for GPT_ATTN_F32; NULL skips it):
+ *   the forward writes into it, in the dtype, round(O - o), the part of the
+ *   fp32 result that rounding o to the dtype dropped; the backward and its
+ *   prep phase, given it, form delta from o + o_lo, an O accurate to about
+ *   twice the dtype's precision. It costs one more [B,H,T,D] tensor written
+ *   by the forward and read by the prep phase, and keeps dq within the bf16
+ *   bar when softmax rows are sharp (see gpt_attn_bwd).
  * dropout: NULL, or the descriptor above; the forward, gpt_attn_bwd_strided
- * and gpt_attn_bwd_main_strided take it (the prep phase does not depend on
- * it: delta = rowsum(dout * O) holds for the dropped output O too).
+ *   and gpt_attn_bwd_main_strided take it (the prep phase does not depend on
+ *   it: delta = rowsum(dout * O) holds for the dropped output O too).
  */
 int gpt_attn_fwd_strided(int dtype, int B, int H, int T, int D, const void* q,
                          const gpt_attn_layout* lq, const void* k, const gpt_attn_layout* lk,
@@ -239,9 +261,9 @@ int gpt_attn_bwd_strided(int dtype, int B, int H, int T, int D, const void* q,
                          const gpt_attn_layout* ldk, float* dv, const gpt_attn_layout* ldv,
                          void* workspace, size_t workspace_bytes,
                          const gpt_attn_dropout* dropout, void* stream);
-int gpt_attn_bwd_prep_strided(int dtype, int B, int H, int T, int D, const void* o,
-                              const gpt_attn_layout* lo, const void* o_lo,
-                              const gpt_attn_layout* llo, const void* dout,
+int gpt_attn_bwd_prep_strided(int dtype, int B, int H, int T, int D, const void* q,
+                              const gpt_attn_layout* lq, const void* o, const gpt_attn_layout* lo,
+                              const void* o_lo, const gpt_attn_layout* llo, const void* dout,
                               const gpt_attn_layout* ldo, float* dq, const gpt_attn_layout* ldq,
                               void* workspace, size_t workspace_bytes, void* stream);
 int gpt_attn_bwd_main_strided(int dtype, int B, int H, int T, int D, const void* q,

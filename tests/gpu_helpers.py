@@ -24,13 +24,25 @@ def announce(msg: str) -> None:
     sys.__stderr__.flush()
 
 
-def run_gpu(inp: dict, keep_o_lo: bool = True):
+def run_gpu(inp: dict, o_lo: bool = False):
     """Forward + backward on cuda:0 through the C ABI. Returns CPU tensors
-    o, lse, dq, dk, dv."""
+    o, lse, dq, dk, dv. By default the plain entry points (gpt_attn_fwd,
+    gpt_attn_bwd); with ``o_lo`` the strided ones with the forward's low
+    part of O passed to the backward."""
     dev = torch.device("cuda:0")
     q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
-    o, lse, o_lo = gattn.attention_forward(q, k, v, keep_o_lo=keep_o_lo)
-    dq, dk, dv = gattn.attention_backward(q, k, v, o, do, lse, o_lo)
+    if o_lo:
+        o, lse, lo = gattn.attention_forward(q, k, v, keep_o_lo=True)
+        dq, dk, dv = gattn.attention_backward(q, k, v, o, do, lse, lo)
+    else:
+        B, H, T, D = q.shape
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+        dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+        ws = torch.empty(max(1, gattn.gpt_attn_bwd_workspace_bytes(B, H, T, D) // 4),
+                         dtype=torch.float32, device=dev)
+        gattn.gpt_attn_fwd(q, k, v, o, lse)
+        gattn.gpt_attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws)
     torch.cuda.synchronize()
     return {"o": o.cpu(), "lse": lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
 

@@ -60,15 +60,28 @@ def test_status_strings(lib):
     assert gattn.gpt_attn_status_string(99) == "unknown status"
 
 
-def fwd(lib, dtype=BF16, B=1, H=1, T=8, D=64, q=P, k=P, v=P, o=P, o_lo=None, lse=P):
-    return lib.gpt_attn_fwd(dtype, B, H, T, D, q, k, v, o, o_lo, lse, None)
+def fwd(lib, dtype=BF16, B=1, H=1, T=8, D=64, q=P, k=P, v=P, o=P, lse=P):
+    return lib.gpt_attn_fwd(dtype, B, H, T, D, q, k, v, o, lse, None)
+
+
+def fwd_lo(lib, dtype=BF16, B=1, H=1, T=8, D=64, o_lo=P):
+    """The strided forward with contiguous layouts and an o_lo."""
+    return lib.gpt_attn_fwd_strided(dtype, B, H, T, D, P, None, P, None, P, None, P, None, o_lo,
+                                    None, P, None, None)
 
 
 def bwd(lib, dtype=BF16, B=1, H=1, T=8, D=64, ptrs=None, ws=P, ws_bytes=1 << 20):
-    p = dict(q=P, k=P, v=P, o=P, o_lo=None, do=P, lse=P, dq=P, dk=P, dv=P)
+    p = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P)
     p.update(ptrs or {})
-    return lib.gpt_attn_bwd(dtype, B, H, T, D, p["q"], p["k"], p["v"], p["o"], p["o_lo"],
-                            p["do"], p["lse"], p["dq"], p["dk"], p["dv"], ws, ws_bytes, None)
+    return lib.gpt_attn_bwd(dtype, B, H, T, D, p["q"], p["k"], p["v"], p["o"], p["do"],
+                            p["lse"], p["dq"], p["dk"], p["dv"], ws, ws_bytes, None)
+
+
+def bwd_lo(lib, dtype=BF16, o_lo=P, ws_bytes=1 << 20):
+    """The strided backward with contiguous layouts and an o_lo."""
+    return lib.gpt_attn_bwd_strided(dtype, 1, 1, 8, 64, P, None, P, None, P, None, P, None, o_lo,
+                                    None, P, None, P, P, None, P, None, P, None, P, ws_bytes,
+                                    None, None)
 
 
 def test_forward_validation(lib):
@@ -83,9 +96,9 @@ def test_forward_validation(lib):
     for name in ("q", "k", "v", "o", "lse"):
         assert fwd(lib, **{name: None}) == E_INVAL, name
         assert fwd(lib, **{name: P + 8}) == E_ALIGN, name
-    # o_lo is bf16-only and must be aligned.
-    assert fwd(lib, dtype=F32, o_lo=P) == E_INVAL
-    assert fwd(lib, o_lo=P + 2) == E_ALIGN
+    # o_lo (strided calls) is for the 16-bit dtypes only and must be aligned.
+    assert fwd_lo(lib, dtype=F32) == E_INVAL
+    assert fwd_lo(lib, o_lo=P + 2) == E_ALIGN
     # B*H*T must stay below 2^31.
     assert fwd(lib, B=1 << 16, H=1 << 15, T=1) == E_INVAL
     assert fwd(lib, B=1 << 10, H=1 << 10, T=1 << 11) == E_INVAL
@@ -98,8 +111,8 @@ def test_empty_calls_are_noops(lib):
         assert bwd(lib, B=B, H=H, T=T, ptrs={n: None for n in
                                                 ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv")},
                    ws=None, ws_bytes=0) == OK
-        assert fwd(lib, dtype=F32, B=B, H=H, T=T, o_lo=P) == OK
-        assert lib.gpt_attn_bwd_workspace_bytes(BF16, B, H, T, 64) == 0
+        assert fwd_lo(lib, dtype=F32, B=B, H=H, T=T) == OK
+        assert lib.gpt_attn_bwd_workspace_bytes(B, H, T, 64) == 0
 
 
 def test_backward_validation(lib):
@@ -108,29 +121,32 @@ def test_backward_validation(lib):
     for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
         assert bwd(lib, ptrs={name: None}) == E_INVAL, name
         assert bwd(lib, ptrs={name: P + 4}) == E_ALIGN, name
-    assert bwd(lib, dtype=F32, ptrs={"o_lo": P}) == E_INVAL
-    assert bwd(lib, ptrs={"o_lo": P + 2}) == E_ALIGN
-    need = lib.gpt_attn_bwd_workspace_bytes(BF16, 1, 1, 8, 64)
-    assert need == 8 * 4
+    assert bwd_lo(lib, dtype=F32) == E_INVAL
+    assert bwd_lo(lib, o_lo=P + 2) == E_ALIGN
+    need = lib.gpt_attn_bwd_workspace_bytes(1, 1, 8, 64)
+    assert need == 8 * 4 + 16  # delta, then one chunk's maxima at the next 16-byte boundary
+    assert bwd_lo(lib, ws_bytes=need - 1) == E_WS
     assert bwd(lib, ws=None) == E_WS
     assert bwd(lib, ws_bytes=need - 1) == E_WS
     assert bwd(lib, ws=P + 4, ws_bytes=need) == E_ALIGN
 
 
 def test_workspace_bytes(lib):
-    assert lib.gpt_attn_bwd_workspace_bytes(BF16, 12, 12, 1024, 64) == 12 * 12 * 1024 * 4
-    assert lib.gpt_attn_bwd_workspace_bytes(F32, 1, 6, 256, 64) == 6 * 256 * 4
-    assert lib.gpt_attn_bwd_workspace_bytes(BF16, 1, 1, 8, 128) == 0
-    assert lib.gpt_attn_bwd_workspace_bytes(F16, 1, 2, 8, 32) == 2 * 8 * 4
-    assert lib.gpt_attn_bwd_workspace_bytes(7, 1, 1, 8, 64) == 0
-    assert lib.gpt_attn_bwd_workspace_bytes(BF16, -1, 1, 8, 64) == 0
+    # delta (4 bytes per row), padded to 16 bytes, then 16 bytes per
+    # (head, 128-row chunk).
+    assert lib.gpt_attn_bwd_workspace_bytes(12, 12, 1024, 64) == 144 * 1024 * 4 + 144 * 8 * 16
+    assert lib.gpt_attn_bwd_workspace_bytes(1, 6, 256, 64) == 6 * 256 * 4 + 6 * 2 * 16
+    assert lib.gpt_attn_bwd_workspace_bytes(1, 1, 8, 128) == 0
+    assert lib.gpt_attn_bwd_workspace_bytes(1, 3, 129, 32) == 1552 + 3 * 2 * 16
+    assert lib.gpt_attn_bwd_workspace_bytes(-1, 1, 8, 64) == 0
+    assert lib.gpt_attn_bwd_workspace_bytes(1, 1, 0, 64) == 0
 
 
 def test_binding_refuses_host_tensors(lib):
     import torch
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
-        gattn.gpt_attn_fwd(q, q, q, q, None, torch.zeros(1, 1, 4))
+        gattn.gpt_attn_fwd(q, q, q, q, torch.zeros(1, 1, 4))
 
 
 # ---- strided entry points --------------------------------------------------------
@@ -209,8 +225,12 @@ def test_plain_calls_equal_strided_calls_with_null_layouts(lib):
     # Same validation outcome either way.
     assert fwd_s(lib, D=128) == fwd(lib, D=128) == E_UNSUP
     assert bwd_s(lib) == E_WS
-    assert lib.gpt_attn_bwd_prep_strided(BF16, 1, 1, 8, 64, P, None, None, None, P, None, P,
-                                         ctypes.byref(L(0, 0, 32)), P, 1 << 20, None) == E_LAYOUT
+    assert lib.gpt_attn_bwd_prep_strided(BF16, 1, 1, 8, 64, P, None, P, None, None, None, P, None,
+                                         P, ctypes.byref(L(0, 0, 32)), P, 1 << 20,
+                                         None) == E_LAYOUT
+    # The 16-bit prep phase reads q (for its maxima); fp32 does not need it.
+    assert lib.gpt_attn_bwd_prep(BF16, 1, 1, 8, 64, None, P, P, P, P, 1 << 20, None) == E_INVAL
+    assert lib.gpt_attn_bwd_prep(BF16, 1, 1, 8, 64, P + 2, P, P, P, P, 1 << 20, None) == E_ALIGN
     assert lib.gpt_attn_bwd_main_strided(BF16, 1, 1, 8, 64, P, None, P, None, P, None, P, None,
                                          P, P, None, P, None, P, ctypes.byref(L(0, 0, 32)), None,
                                          0, None, None) == E_LAYOUT
@@ -302,8 +322,8 @@ def test_sixteen_bit_dtypes_and_head_sizes_share_the_rules(lib):
             assert bwd(lib, dtype=dt, D=D, ws=None) == E_WS
             assert bwd(lib, dtype=dt, D=D, ptrs={"dq": None}) == E_INVAL
     # o_lo is allowed for both 16-bit types, not for fp32.
-    assert fwd(lib, dtype=F16, o_lo=P + 2) == E_ALIGN
-    assert fwd(lib, dtype=F32, D=32, o_lo=P) == E_INVAL
+    assert fwd_lo(lib, dtype=F16, o_lo=P + 2) == E_ALIGN
+    assert fwd_lo(lib, dtype=F32, D=32) == E_INVAL
     # fp16 rows are 16-byte aligned at multiples of 8 elements.
     assert bwd_s(lib, dtype=F16, q=L(8 * 300, 8 * 40, 8 * 7)) == E_WS
     assert bwd_s(lib, dtype=F16, q=L(8 * 300, 8 * 40, 60)) == E_LAYOUT

@@ -51,6 +51,11 @@ def test_training_step_report():
     total = (19_346_227_200 + 48_365_568_000) / (d["ms_per_step"] * 1e-3) / 1e12
     assert abs(total - d["value"]) <= 0.01 * total
     assert "cpu_baseline" not in d
+    assert d["config"]["entry_points"] == "plain" and d["config"]["o_lo"] is False
+    for part in ("fwd", "bwd"):
+        assert d[part]["ms"] > 0 and d[part]["pct_peak"] > 0
+    assert 0 < d["fwd"]["min_ms"] <= d["fwd"]["ms"]
+    assert 0 < d["bwd"]["main_min_ms"] <= d["bwd"]["main_ms"] == r["avg_launch_ms"]
     # The default rotates over enough copies of the step's data (228 MB each
     # here) to exceed the 256 MB Infinity Cache several times over.
     assert d["config"]["data_sets"] >= 4
@@ -70,3 +75,19 @@ def test_decode_report():
     assert d["unit"] == "GB/s" and r["bound"] == "hbm" and r["peak"] == 8000.0
     assert d["config"]["bytes_per_step"] == r["bytes_per_launch"] > 0
     assert d["config"]["data_sets"] >= 4
+
+
+def test_all_configs_report_errors_against_the_oracle():
+    announce("bench.py --all-configs --steps 2")
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--all-configs",
+                        "--steps", "2", "--warmup", "1", "--reps", "1", "--settle-ms", "20",
+                        "--no-cpu-baseline"], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    recs = [json.loads(ln) for ln in r.stdout.splitlines() if ln.startswith("{")]
+    import bench
+    assert [d["config"]["workload"] for d in recs] == list(bench.ALL_CONFIGS)
+    for d in recs:
+        tol = (1e-5, None) if d["dtype"] == "f32" else (2e-2, 5e-3)
+        for name, e in d["errors_vs_oracle"].items():
+            assert e["max_abs"] <= tol[0], (d["config"]["workload"], name, e)
+            assert tol[1] is None or e["mean_abs"] <= tol[1], (d["config"]["workload"], name)

@@ -20,6 +20,7 @@ FLOPS = [
     ("shakespeare_char_f32_b1_h6_t256", 50_528_256, 126_320_640),
     ("shakespeare_char_bf16_b64_h6_t256", 3_233_808_384, 8_084_520_960),
     ("gpt2_124m_bf16_b12_h12_t1024", 19_346_227_200, 48_365_568_000),
+    ("gpt2_350m_bf16_b12_h16_t1024", 25_794_969_600, 64_487_424_000),
     ("gpt2_774m_sharp_bf16_b8_h20_t1024", 21_495_808_000, 53_739_520_000),
     ("gpt2_1558m_bf16_b4_h25_t1024", 13_434_880_000, 33_587_200_000),
     ("gpt2_1558m_long_bf16_b2_h25_t2048", 26_856_652_800, 67_141_632_000),
@@ -66,3 +67,17 @@ def test_data_set_rotation_count():
     assert bench.n_sets(0, 1000) == 16
     assert bench.n_sets(1, 227_600_000) == 1
     assert bench.n_sets(3, 10) == 3
+
+
+def test_host_cpu_description():
+    info = bench.host_cpu()
+    assert info["logical_cpus"] >= 1
+    assert isinstance(info["cpu_model"], str) and info["cpu_model"]
+    assert info["physical_cores"] is None or 1 <= info["physical_cores"] <= info["logical_cpus"]
+    assert 1 <= bench.default_threads() <= 16
+
+
+def test_every_benchmark_configuration_is_a_workload():
+    for name in bench.ALL_CONFIGS:
+        assert name in WORKLOADS
+    assert bench.DEFAULT_WORKLOAD in bench.ALL_CONFIGS

@@ -28,12 +28,13 @@ def test_graph_replays_match_eager(dropout):
     dq = torch.empty(q.shape, dtype=torch.float32, device=DEV)
     dk = torch.empty_like(dq)
     dv = torch.empty_like(dq)
-    ws = torch.empty(B * H * T, dtype=torch.float32, device=DEV)
+    ws = torch.empty(gattn.gpt_attn_bwd_workspace_bytes(B, H, T, 64) // 4, dtype=torch.float32,
+                     device=DEV)
 
     def step():
         st = torch.cuda.current_stream(DEV)
         gattn.gpt_attn_fwd_strided(q, k, v, o, o_lo, lse, st, dropout)
-        gattn.gpt_attn_bwd_prep_strided(o, o_lo, do, dq, ws, st)
+        gattn.gpt_attn_bwd_prep_strided(q, o, o_lo, do, dq, ws, st)
         gattn.gpt_attn_bwd_main_strided(q, k, v, do, lse, dq, dk, dv, ws, st, dropout)
 
     step()
