@@ -48,6 +48,7 @@ __all__ = [
     "attention_forward", "attention_backward", "split_qkv_heads", "merged_heads_view",
     "DTYPE_CODES", "GptAttnLayout", "GptAttnDropout", "gpt_attn_dropout_mask",
     "gpt_attn_decode", "gpt_attn_decode_workspace_bytes", "attention_decode",
+    "gpt_attn_bwd_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -61,12 +62,14 @@ DTYPE_CODES = {"f32": GPT_ATTN_F32, "bf16": GPT_ATTN_BF16, "f16": GPT_ATTN_F16}
 
 #: every symbol include/gpt_attn.h declares
 EXPORTED_SYMBOLS = ("gpt_attn_fwd", "gpt_attn_bwd", "gpt_attn_bwd_prep", "gpt_attn_bwd_main",
+                    "gpt_attn_bwd_noalloc",
                     "gpt_attn_fwd_strided", "gpt_attn_bwd_strided", "gpt_attn_bwd_prep_strided",
                     "gpt_attn_bwd_main_strided", "gpt_attn_dropout_mask", "gpt_attn_decode",
                     "gpt_attn_decode_workspace_bytes", "gpt_attn_bwd_workspace_bytes",
                     "gpt_attn_status_string", "gpt_attn_abi_version")
 
 ABI_VERSION = 6
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class GptAttnLayout(ctypes.Structure):
@@ -121,6 +124,8 @@ def load_library():
     lib.gpt_attn_bwd_prep.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
     lib.gpt_attn_bwd_prep.restype = i
     lib.gpt_attn_bwd_main.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gpt_attn_bwd_noalloc.argtypes = [i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gpt_attn_bwd_noalloc.restype = i
     lib.gpt_attn_bwd_main.restype = i
     lp = ctypes.POINTER(GptAttnLayout)
     dp_ = ctypes.POINTER(GptAttnDropout)
@@ -242,6 +247,17 @@ def gpt_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, stream=None) -> N
                                      _stream(q.device, stream))
     if st != 0:
         raise GptAttnError("gpt_attn_bwd", st)
+
+
+def gpt_attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, stream=None) -> None:
+    """gpt_attn_bwd with the library's static per-GPU scratch in place of a
+    workspace (allocates nothing; calls on one GPU must not overlap)."""
+    B, H, T, D = _bhtd(q)
+    st = load_library().gpt_attn_bwd_noalloc(_dtype_code(q), B, H, T, D, _ptr(q), _ptr(k),
+                                             _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                             _ptr(dk), _ptr(dv), _stream(q.device, stream))
+    if st != 0:
+        raise GptAttnError("gpt_attn_bwd_noalloc", st)
 
 
 def _ws_bytes(workspace) -> int:

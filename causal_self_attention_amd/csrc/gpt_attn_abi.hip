@@ -4,8 +4,16 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "attn_launch.h"
 #include "gpt_attn.h"
+
+// Backing store of gpt_attn_bwd_noalloc: the backward's workspace (delta and
+// the per-chunk maxima), one copy per GPU that the library runs on, held
+// until the process ends. In host code this name is only a handle for
+// hipGetSymbolAddress; the device address comes from scratch_address().
+static __device__ __align__(256) unsigned char scratch[GPT_ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -201,6 +209,32 @@ int run_prep(const Shape& s, const gpt_attn::BwdArgs& a, hipStream_t st) {
                            : gpt_attn::launch_bwd_prep_16(a, s.dtype == GPT_ATTN_F16, s.D, st));
 }
 
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream), looked up once per device with that device
+// current and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(hipStream_t stream, void** out) {
+  int cur = 0, dev = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return GPT_ATTN_E_HIP;
+  dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return GPT_ATTN_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return GPT_ATTN_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return GPT_ATTN_E_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return GPT_ATTN_E_HIP;
+    if (e != hipSuccess || !p) return GPT_ATTN_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GPT_ATTN_OK;
+}
+
 int run_main(const Shape& s, const gpt_attn::BwdArgs& a, hipStream_t st) {
   return launch_status(s.dtype == GPT_ATTN_F32
                            ? gpt_attn::launch_bwd_main_f32(a, s.D, st)
@@ -231,6 +265,9 @@ const char* gpt_attn_status_string(int status) {
     case GPT_ATTN_E_LAYOUT:
       return "bad layout (negative or misaligned stride, overlapping output, or offsets "
              "beyond the supported range)";
+    case GPT_ATTN_E_TOO_LARGE:
+      return "shape needs more backward workspace than the allocation-free entry point's "
+             "static scratch holds (GPT_ATTN_NOALLOC_SCRATCH_BYTES)";
     default:
       return "unknown status";
   }
@@ -362,6 +399,26 @@ int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const voi
   return gpt_attn_bwd_strided(dtype, B, H, T, D, q, nullptr, k, nullptr, v, nullptr, o, nullptr,
                               nullptr, nullptr, dout, nullptr, lse, dq, nullptr, dk, nullptr, dv,
                               nullptr, workspace, workspace_bytes, nullptr, stream);
+}
+
+int gpt_attn_bwd_noalloc(int dtype, int B, int H, int T, int D, const void* q, const void* k,
+                         const void* v, const void* o, const void* dout, const float* lse,
+                         float* dq, float* dk, float* dv, void* stream) {
+  Shape s;
+  GA_TRY(check_shape(dtype, B, H, T, D, &s));
+  if (s.rows == 0) return GPT_ATTN_OK;
+  const size_t need = (size_t)gpt_attn::bwd_workspace_bytes((long long)B * H, T);
+  if (need > (size_t)GPT_ATTN_NOALLOC_SCRATCH_BYTES) return GPT_ATTN_E_TOO_LARGE;
+  // Every argument check of the workspace form runs before the first HIP
+  // call (a valid stand-in workspace address and size pass its checks).
+  gpt_attn::BwdArgs a;
+  GA_TRY(bwd_args(s, 3, q, nullptr, k, nullptr, v, nullptr, o, nullptr, nullptr, nullptr, dout,
+                  nullptr, lse, dq, nullptr, dk, nullptr, dv, nullptr,
+                  reinterpret_cast<void*>((uintptr_t)256), need, nullptr, &a));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  GA_TRY(scratch_address(st, &ws));
+  return gpt_attn_bwd(dtype, B, H, T, D, q, k, v, o, dout, lse, dq, dk, dv, ws, need, stream);
 }
 
 size_t gpt_attn_decode_workspace_bytes(int dtype, int B, int H, int L, int D) {

@@ -65,7 +65,8 @@ enum gpt_attn_status {
   GPT_ATTN_E_ALIGN = 3,       /* a pointer that is not 16-byte aligned */
   GPT_ATTN_E_WORKSPACE = 4,   /* workspace NULL or smaller than the *_workspace_bytes size */
   GPT_ATTN_E_HIP = 5,         /* the HIP runtime reported an error when launching */
-  GPT_ATTN_E_LAYOUT = 6       /* a gpt_attn_layout breaking the rules below */
+  GPT_ATTN_E_LAYOUT = 6,      /* a gpt_attn_layout breaking the rules below */
+  GPT_ATTN_E_TOO_LARGE = 7    /* gpt_attn_bwd_noalloc: workspace beyond its static scratch */
 };
 
 /*
@@ -227,6 +228,26 @@ int gpt_attn_bwd_prep(int dtype, int B, int H, int T, int D, const void* q, cons
 int gpt_attn_bwd_main(int dtype, int B, int H, int T, int D, const void* q, const void* k,
                       const void* v, const void* dout, const float* lse, float* dq, float* dk,
                       float* dv, const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gpt_attn_bwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Arguments, outputs and errors are gpt_attn_bwd's without the workspace:
+ * the library keeps the backward's workspace in a static device array of
+ * GPT_ATTN_NOALLOC_SCRATCH_BYTES (8 MiB) per GPU it runs on, held until the
+ * process ends. Shapes whose gpt_attn_bwd_workspace_bytes exceeds that
+ * (B*H*T beyond about two million rows) return GPT_ATTN_E_TOO_LARGE before
+ * any device work. The call allocates nothing; its first call on a device
+ * looks up that device's copy of the array (hipGetSymbolAddress) and keeps
+ * it. Every call on one GPU shares that GPU's copy, so calls that overlap in
+ * time on one GPU (different streams, or host threads) race: serialize
+ * them. Nothing in the array needs to start at zero: each call overwrites
+ * what it reads.
+ */
+#define GPT_ATTN_NOALLOC_SCRATCH_BYTES (8u << 20)
+int gpt_attn_bwd_noalloc(int dtype, int B, int H, int T, int D, const void* q, const void* k,
+                         const void* v, const void* o, const void* dout, const float* lse,
+                         float* dq, float* dk, float* dv, void* stream);
 
 /*
  * Strided forms of the four calls above: each operand pointer is followed by

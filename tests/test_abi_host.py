@@ -55,7 +55,7 @@ def test_abi_version_matches_header(lib):
 
 
 def test_status_strings(lib):
-    for st in range(7):
+    for st in range(8):
         assert gattn.gpt_attn_status_string(st)
     assert gattn.gpt_attn_status_string(99) == "unknown status"
 
@@ -327,3 +327,21 @@ def test_sixteen_bit_dtypes_and_head_sizes_share_the_rules(lib):
     # fp16 rows are 16-byte aligned at multiples of 8 elements.
     assert bwd_s(lib, dtype=F16, q=L(8 * 300, 8 * 40, 8 * 7)) == E_WS
     assert bwd_s(lib, dtype=F16, q=L(8 * 300, 8 * 40, 60)) == E_LAYOUT
+
+
+# ---- the allocation-free backward --------------------------------------------------
+
+def test_noalloc_validation_before_any_device_work(lib):
+    def call(dtype=BF16, B=1, H=1, T=8, D=64, q=P, dq=P):
+        return lib.gpt_attn_bwd_noalloc(dtype, B, H, T, D, q, P, P, P, P, P, dq, P, P, None)
+    assert call(D=128) == E_UNSUP
+    assert call(q=None) == E_INVAL
+    assert call(dq=P + 4) == E_ALIGN
+    # 64 * 64 * 1024 rows need 16.8 MB of workspace, beyond the 8 MiB scratch.
+    assert lib.gpt_attn_bwd_workspace_bytes(64, 64, 1024, 64) > gattn.NOALLOC_SCRATCH_BYTES
+    assert call(B=64, H=64, T=1024) == 7
+    assert call(B=0) == OK
+    text = open(HEADER).read()
+    assert f"#define GPT_ATTN_NOALLOC_SCRATCH_BYTES (8u << 20)" in text
+    assert gattn.NOALLOC_SCRATCH_BYTES == 8 << 20
+    assert "static" in gattn.gpt_attn_status_string(7)
