@@ -1,8 +1,11 @@
 """Build the gfx950 attention library in-tree with hipcc.
 
-Produces causal_self_attention_amd/libgptattn.so from every csrc/*.hip file.
-Run as ``python -m causal_self_attention_amd.build``; it compiles every time
-it is called.
+Produces causal_self_attention_amd/libgptattn.so from every csrc/*.hip file,
+and libgptattn_dbg.so, the same sources with GPT_ATTN_EXTRA_BARRIERS (a
+full workgroup barrier at every marked LDS stage boundary; the race check
+of the test suite compares its results with the release library's). Run as
+``python -m causal_self_attention_amd.build``; it compiles every time it is
+called.
 """
 from __future__ import annotations
 
@@ -14,6 +17,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libgptattn.so")
+DBG_LIB_PATH = os.path.join(HERE, "libgptattn_dbg.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU instructions stay off: the compiler is told the target
@@ -29,15 +33,30 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
+def _command(out: str, extra_flags: list[str] | None) -> list[str]:
+    return [HIPCC, *HIP_FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"),
+            "-I", os.path.join(HERE, "csrc"), *sources(), "-o", out + ".tmp"]
+
+
 def build(verbose: bool = False, extra_flags: list[str] | None = None,
-          out: str | None = None) -> str:
+          out: str | None = None, debug_too: bool = True) -> str:
+    """Build libgptattn.so (and, unless debug_too is false, libgptattn_dbg.so
+    alongside it, the two compilations running at once)."""
     out = out or LIB_PATH
-    cmd = [HIPCC, *HIP_FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"),
-           "-I", os.path.join(HERE, "csrc"), *sources(), "-o", out + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(out + ".tmp", out)
+    jobs = [(out, extra_flags)]
+    if debug_too and out == LIB_PATH:
+        jobs.append((DBG_LIB_PATH, [*(extra_flags or []), "-DGPT_ATTN_EXTRA_BARRIERS"]))
+    procs = []
+    for path, flags in jobs:
+        cmd = _command(path, flags)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((path, subprocess.Popen(cmd)))
+    failed = [path for path, p in procs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, f"hipcc for {', '.join(failed)}")
+    for path, _ in procs:
+        os.replace(path + ".tmp", path)
     return out
 
 

@@ -282,6 +282,7 @@ __device__ __forceinline__ void store_rows(float* stage, const f32x16 (&acc)[D /
       *reinterpret_cast<f32x4*>(&stage[l32 * kEp + db * 32 + 8 * g + 4 * hf]) = x;
     }
   __builtin_amdgcn_wave_barrier();
+  extra_barrier();
 #pragma unroll
   for (int j = 0; j < 32 / kRpi; ++j) {
     const int row = j * kRpi + lane / kLpr, col = (lane % kLpr) * 4;
@@ -290,6 +291,7 @@ __device__ __forceinline__ void store_rows(float* stage, const f32x16 (&acc)[D /
                                   reinterpret_cast<f32x4*>(rows + (kw0 + row) * ld + col));
   }
   __builtin_amdgcn_wave_barrier();
+  extra_barrier();
 }
 
 // dQ[queries qb0.., dims 32db..] += scale * acc * 2^e for one 32x32 block,
@@ -487,6 +489,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
                           &sK[(wave * 32 + l32) * kRowQ + kk * 16 + 8 * hf]);
   int buf = 0;
   for (int qs = k0; qs < T; qs += kBQ, buf ^= 1) {
+    extra_barrier();
     // Prefetch the next tile into registers while this one is computed.
     const bool has_next = qs + kBQ < T;
     if (loader && has_next)
@@ -588,6 +591,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
     }
     // Stage the prefetched tile into the other buffer, last read in the
     // previous step before its first barrier.
+    extra_barrier();
     if (loader && has_next)
       bwd_store_tile<TIn, D>(sQ[buf ^ 1], sdO[buf ^ 1], sL[buf ^ 1], sD[buf ^ 1], nxt, qs + kBQ,
                              T, ltid, eq, edo, edo + ev);

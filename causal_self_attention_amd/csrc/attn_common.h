@@ -19,6 +19,17 @@
 
 namespace gpt_attn {
 
+// Race check for the LDS pipelines: built with GPT_ATTN_EXTRA_BARRIERS, every
+// point marked with extra_barrier() (each reached by every wave of the
+// workgroup) becomes a full workgroup barrier, so every LDS stage completes
+// before the next begins; a race in the release schedule would make that
+// build's results differ from the release build's.
+__device__ __forceinline__ void extra_barrier() {
+#ifdef GPT_ATTN_EXTRA_BARRIERS
+  __syncthreads();
+#endif
+}
+
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));

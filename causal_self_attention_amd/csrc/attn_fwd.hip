@@ -405,6 +405,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
     if (has_next) fwd_load_tile<TIn, D>(kh, ldk, vh, ldv, k0 + kBN, T, tid, nxt);
     fwd_tile<TIn, D, DROP>(Kbuf(buf), Vbuf(buf), qf, k0, my_q, T, l32, hf, lane, scale_log2,
                            a.drop, tm.head, st);
+    extra_barrier();
     if (has_next) {
       fwd_store_tile<TIn, D>(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid, vs.vexp);
       if (kScaleV<TIn>) {
@@ -439,6 +440,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
         fwd_half<TIn, D, kGeneral, DROP>(Kbuf(buf), Vbuf(buf), qf, kb, k0, my_q, T, l32, hf,
                                          lane, scale_log2, a.drop, tm.head, st);
     }
+    extra_barrier();
     if (has_next) {
       fwd_store_tile<TIn, D>(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid, vs.vexp);
       if (kScaleV<TIn>) {
@@ -480,6 +482,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
         *reinterpret_cast<vec4*>(&sl[l32 * kRow + db * 32 + 8 * g + 4 * hf]) = lo;
       }
     __builtin_amdgcn_wave_barrier();
+    extra_barrier();
     TIn* ob = static_cast<TIn*>(a.o) + head_base(a.lo, tm.head, a.H);
     TIn* lb = a.o_lo ? static_cast<TIn*>(a.o_lo) + head_base(a.llo, tm.head, a.H) : nullptr;
     constexpr int kC = D / 8;  // 16-byte chunks per row

@@ -76,10 +76,6 @@ def test_sweep_parity(case):
     inp = make_inputs(B, H, T, D, dtype, seed=7000 + i)
     gpu = _run(inp, fused, drop, keep_o_lo)
     ref = run_oracle_dropout(inp, drop) if drop else run_oracle(inp)
-    errs = errors(gpu, ref)
-    if drop and drop[0] > 0.2:
-        # The survivor scale z = 1/(1-p) multiplies O and the gradients and
-        # with them the 16-bit roundings; the bars are for unit-scale outputs.
-        z = 1.0 / (1.0 - drop[0])
-        errs = {n: (mx / z, mean / z) for n, (mx, mean) in errs.items()}
-    assert_parity(errs, dtype, label)
+    # Dropout rates here are at most 0.5, where the plain bars hold (no
+    # division by the survivor scale).
+    assert_parity(errors(gpu, ref), dtype, label)
