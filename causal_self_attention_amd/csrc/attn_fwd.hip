@@ -40,7 +40,7 @@ namespace {
 constexpr int kBM = 128;     // queries per workgroup
 constexpr int kBN = 64;      // keys per staged tile
 constexpr int kThreads = 256;
-constexpr float kMaxSlack = 8.f;  // lazy-rescale threshold, log2 units
+constexpr float kPMax = 32768.f;  // largest group sum of P taken without a rescale
 
 // Padded LDS row of a D-wide 16-bit tile (D + 8 elements).
 template <int D>
@@ -78,7 +78,8 @@ __device__ __forceinline__ void fwd_load_tile(const TIn* kh, int ldk, const TIn*
 }
 
 // For bf16, V is scaled by 2^vexp on its way to fp16 (see attn_fwd_kernel).
-template <typename TIn, int D>
+// MASK: zero the rows at or past T (only a sequence's last tile has any).
+template <typename TIn, int D, bool MASK>
 __device__ __forceinline__ void fwd_store_tile(TIn* Ks, f16* Vs, const KVRegs<TIn, D>& r, int k0,
                                                int T, int tid, int vexp) {
   typedef typename In16<TIn>::vec vec;
@@ -87,7 +88,7 @@ __device__ __forceinline__ void fwd_store_tile(TIn* Ks, f16* Vs, const KVRegs<TI
   for (int p = 0; p < KVRegs<TIn, D>::kN; ++p) {
     const int c = tid + kThreads * p;
     const int row = c / kC, col = (c % kC) * 8;
-    const bool ok = k0 + row < T;
+    const bool ok = !MASK || k0 + row < T;
     *reinterpret_cast<vec*>(&Ks[row * kRow + col]) = ok ? r.k[p] : In16<TIn>::zero();
     const f16x8 vs = (!kScaleV<TIn> || vexp == 0) ? In16<TIn>::to_f16(r.v[p])
                                                   : cvt_f16_scaled(r.v[p], vexp);
@@ -95,14 +96,35 @@ __device__ __forceinline__ void fwd_store_tile(TIn* Ks, f16* Vs, const KVRegs<TI
   }
 }
 
-// Largest |V| of the thread's chunks of a loaded tile.
+// Stage tile k0 into (Ks, Vs), with the row mask only where it can matter.
 template <typename TIn, int D>
-__device__ __forceinline__ float tile_vmax(const KVRegs<TIn, D>& r) {
-  float m = 0.f;
-#pragma unroll
-  for (int p = 0; p < KVRegs<TIn, D>::kN; ++p) fold_absmax(r.v[p], m);
-  return m;
+__device__ __forceinline__ void fwd_stage(TIn* Ks, f16* Vs, const KVRegs<TIn, D>& r, int k0, int T,
+                                          int tid, int vexp) {
+  if (k0 + kBN <= T)
+    fwd_store_tile<TIn, D, false>(Ks, Vs, r, k0, T, tid, vexp);
+  else
+    fwd_store_tile<TIn, D, true>(Ks, Vs, r, k0, T, tid, vexp);
 }
+
+// Largest |V| among the thread's chunks of a loaded bf16 tile, as the bit
+// pattern of a bf16 magnitude (sign cleared). Such patterns order like the
+// magnitudes they encode, so two 16-bit lanes at a time go through one
+// packed integer max.
+template <typename TIn, int D>
+__device__ __forceinline__ uint32_t tile_vmax_bits(const KVRegs<TIn, D>& r) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = {0, 0};
+#pragma unroll
+  for (int p = 0; p < KVRegs<TIn, D>::kN; ++p) {
+    const i32x4 w = __builtin_bit_cast(i32x4, r.v[p]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)w[i] & 0x7fff7fffu));
+  }
+  return m.x > m.y ? m.x : m.y;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
 
 // Per-wave state of the online softmax.
 template <int D>
@@ -111,6 +133,46 @@ struct FwdState {
   float m_run;          // reference max, scaled log2 units (lazily updated)
   float l_run;          // this lane's partial row sum
 };
+
+// The weights of one group of 8 scores (registers base .. base + 7 of s)
+// against the running reference, P = exp2(S * scale_log2 - m_run), packed to
+// fp16, and their sum, which is added to l. The reference lags the row
+// maximum: any P up to fp16's range is as good as P <= 1 (O and l carry the
+// same reference, which the final division removes), so the reference moves
+// only when a group's sum is not at most kPMax, i.e. some P of it could
+// leave fp16's range (or the reference is still -infinity). Then the wave
+// takes the exact maximum of the scores mx() covers (lanes l and l + 32
+// hold two halves of one query's keys and exchange theirs), rescales O and
+// l by 2^(m_run - m_new) and recomputes the group. Groups already taken
+// this tile were consistent with the old reference and are rescaled with
+// the rest. The group sum uses the fp16 values the P V product multiplies.
+template <int D, typename MaxFn>
+__device__ __forceinline__ f16x8 fwd_group(const f32x16& s, int base, float scale_log2,
+                                           MaxFn mx, FwdState<D>& st) {
+  float p[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) p[t] = fast_exp2(fmaf(s[base + t], scale_log2, -st.m_run));
+  f16x8 pb = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+  float gs = sum_f16x8(pb, 0.f);
+  if (wave_any(!(gs <= kPMax))) {
+    float m = mx();
+    m = fmaxf(m, wave_xor32(m));
+    const float m_new = fmaxf(st.m_run, m);
+    const float alpha = fast_exp2(st.m_run - m_new);
+    st.m_run = m_new;
+    st.l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) p[t] = fast_exp2(fmaf(s[base + t], scale_log2, -st.m_run));
+    pb = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+    gs = sum_f16x8(pb, 0.f);
+  }
+  st.l_run += gs;
+  return pb;
+}
 
 // One 64-key tile for one wave, off the diagonal: every key of the tile
 // precedes every query of the wave and lies below T (no compares at all).
@@ -134,42 +196,20 @@ __device__ __forceinline__ void fwd_tile(const TIn* cK, const f16* cV,
       s[kb] = In16<TIn>::mfma(*reinterpret_cast<const vec*>(arow + kk * 16), qf[kk], s[kb]);
   }
 
-  // Lazy running max: the reference m_run moves only when some row's max
-  // rises by more than kMaxSlack (log2 units); otherwise the exponentials
-  // below may reach 2^kMaxSlack, which the fp32 sums and fp16 P hold exactly
-  // as well, and the final division by l removes the reference. Most tiles
-  // skip the rescale of O and l (wave-uniform branch).
-  float mx = fmaxf(s[0][0], s[0][1]);
+  // The lane's maximum over the tile, scaled log2 units (rescales only).
+  auto tile_max = [&]() {
+    float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  // Lanes l and l + 32 hold the two halves of one query's keys and share
-  // m_run, so a half's own max decides as well as the row's max would; the
-  // cross-half exchange runs only when the reference moves.
-  mx *= scale_log2;
-  if (wave_any(mx > st.m_run + kMaxSlack)) {
-    mx = fmaxf(mx, wave_xor32(mx));
-    const float m_new = fmaxf(st.m_run, mx);
-    const float alpha = fast_exp2(st.m_run - m_new);
-    st.m_run = m_new;
-    st.l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
-  }
-
+      for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    return mx * scale_log2;
+  };
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      float p[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) p[t] = fast_exp2(fmaf(s[kb][8 * c + t], scale_log2, -st.m_run));
-      const f16x8 pb = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-      // The row sum uses the fp16 weights the MFMA multiplies by.
-      st.l_run = sum_f16x8(pb, st.l_run);
+      const f16x8 pb = fwd_group<D>(s[kb], 8 * c, scale_log2, tile_max, st);
       f16x8 pw = pb;
       if (DROP) {
         // Keys k0 + 32kb + 16c + 8hf .. +7 of query my_q: one Philox block.
@@ -220,28 +260,16 @@ __device__ __forceinline__ void fwd_half(const TIn* cK, const f16* cV,
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = (16 * (r >> 3) + (r & 7) > lim) ? -INFINITY : s[r];
   }
-  float mx = fmaxf(s[0], s[1]);
+  // The lane's maximum over the half, scaled log2 units (rescales only).
+  auto half_max = [&]() {
+    float mx = fmaxf(s[0], s[1]);
 #pragma unroll
-  for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  mx *= scale_log2;  // this half's max; exchanged only when m_run moves
-  if (wave_any(mx > st.m_run + kMaxSlack)) {
-    mx = fmaxf(mx, wave_xor32(mx));
-    const float m_new = fmaxf(st.m_run, mx);
-    const float alpha = fast_exp2(st.m_run - m_new);
-    st.m_run = m_new;
-    st.l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
-  }
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    return mx * scale_log2;
+  };
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    float p[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) p[t] = fast_exp2(fmaf(s[8 * c + t], scale_log2, -st.m_run));
-    const f16x8 pb = pack_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-    st.l_run = sum_f16x8(pb, st.l_run);
+    const f16x8 pb = fwd_group<D>(s, 8 * c, scale_log2, half_max, st);
     f16x8 pw = pb;
     if (DROP) {
       uint32_t m[4];
@@ -272,16 +300,21 @@ __device__ __forceinline__ void fwd_half(const TIn* cK, const f16* cV,
 // tile's V again. O is unscaled by 2^-vexp at the end.
 struct VScale {
   int vexp;
-  float vthr;
-  bool set;  // some V so far was nonzero
+  uint32_t thr;  // bf16 magnitude pattern of the smallest |V| that needs a smaller vexp
+  bool set;      // some V so far was nonzero
 };
+
+// The bf16 pattern of 2^(15 - vexp): the top half of the float (an exact
+// power of two, a subnormal, or infinity when no bf16 value can reach it).
+__device__ __forceinline__ uint32_t vscale_thr(int vexp) {
+  return __float_as_uint(ldexpf(1.f, 15 - vexp)) >> 16;
+}
 
 __device__ __forceinline__ VScale vscale_first(float m0) {
   VScale v;
   v.set = m0 > 0.f;
   v.vexp = (m0 >= 0.0625f && m0 < 256.f) ? 0 : block_exp(m0, 8);
-  v.vthr = !v.set ? 1.401298464e-45f : (m0 <= 3.402823466e38f ? ldexpf(1.f, 15 - v.vexp)
-                                                              : INFINITY);
+  v.thr = !v.set ? 1u : (m0 <= 3.402823466e38f ? vscale_thr(v.vexp) : 0x7f80u);
   return v;
 }
 
@@ -292,7 +325,7 @@ template <typename TIn, int D>
 __device__ __forceinline__ void fwd_rescale_v(float* s_red, const KVRegs<TIn, D>& r, TIn* Kb,
                                            f16* Vb, int k0, int T, int tid, int lane, int wave,
                                            VScale& vs, FwdState<D>& st) {
-  const float m = wave_max(tile_vmax<TIn, D>(r));
+  const float m = wave_max(bf16_bits_to_float(tile_vmax_bits<TIn, D>(r)));
   if (lane == 0) s_red[wave] = m;
   __syncthreads();
   const float mt = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
@@ -304,8 +337,8 @@ __device__ __forceinline__ void fwd_rescale_v(float* s_red, const KVRegs<TIn, D>
     for (int i = 0; i < 16; ++i) st.oacc[db][i] = ldexpf(st.oacc[db][i], e - vs.vexp);
   vs.vexp = __builtin_amdgcn_readfirstlane(e);
   vs.set = true;
-  vs.vthr = mt <= 3.402823466e38f ? ldexpf(1.f, 15 - e) : INFINITY;
-  fwd_store_tile<TIn, D>(Kb, Vb, r, k0, T, tid, vs.vexp);
+  vs.thr = mt <= 3.402823466e38f ? vscale_thr(e) : 0x7f80u;
+  fwd_stage<TIn, D>(Kb, Vb, r, k0, T, tid, vs.vexp);
   __syncthreads();
 }
 
@@ -367,11 +400,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
   __shared__ float s_vred[4];   // per wave: largest |V| of a tile
   __shared__ __attribute__((aligned(16))) int s_vflag[2][4];  // per tile parity, wave: |V| too large
   if (kScaleV<TIn>) {
-    const float m = wave_max(tile_vmax<TIn, D>(nxt));
+    const float m = wave_max(bf16_bits_to_float(tile_vmax_bits<TIn, D>(nxt)));
     if (lane == 0) s_vred[wave] = m;
   }
   __syncthreads();  // Q staged, tile 0's largest |V| known
-  VScale vs = {0, INFINITY, true};
+  VScale vs = {0, 0x7f80u, true};
   if (kScaleV<TIn>)
     vs = vscale_first(fmaxf(fmaxf(s_vred[0], s_vred[1]), fmaxf(s_vred[2], s_vred[3])));
 
@@ -389,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
   // keys precede query q0 (and hence every query here) and lie below T.
   const int n_full = min(q0, T) / kBN;
 
-  fwd_store_tile<TIn, D>(Kbuf(0), Vbuf(0), nxt, 0, T, tid, vs.vexp);
+  fwd_stage<TIn, D>(Kbuf(0), Vbuf(0), nxt, 0, T, tid, vs.vexp);
   // Q^T as the B operand: lane holds d = 16*kk + 8*hf .. +7 of its query.
   vec qf[D / 16];
 #pragma unroll
@@ -407,9 +440,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
                            a.drop, tm.head, st);
     extra_barrier();
     if (has_next) {
-      fwd_store_tile<TIn, D>(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid, vs.vexp);
+      fwd_stage<TIn, D>(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid, vs.vexp);
       if (kScaleV<TIn>) {
-        const bool big = wave_any(tile_vmax<TIn, D>(nxt) >= vs.vthr);
+        const bool big = wave_any(tile_vmax_bits<TIn, D>(nxt) >= vs.thr);
         if (lane == 0) s_vflag[kt & 1][wave] = big;
       }
     }
@@ -442,9 +475,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
     }
     extra_barrier();
     if (has_next) {
-      fwd_store_tile<TIn, D>(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid, vs.vexp);
+      fwd_stage<TIn, D>(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid, vs.vexp);
       if (kScaleV<TIn>) {
-        const bool big = wave_any(tile_vmax<TIn, D>(nxt) >= vs.vthr);
+        const bool big = wave_any(tile_vmax_bits<TIn, D>(nxt) >= vs.thr);
         if (lane == 0) s_vflag[kt & 1][wave] = big;
       }
     }
@@ -467,19 +500,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
     typedef typename In16<TIn>::vec4 vec4;
     TIn* so = lds_raw + (wave * 32) * kRow;        // O rows [query][d]
     TIn* sl = lds_raw + (kBM + wave * 32) * kRow;  // o_lo rows
+    const bool want_lo = a.o_lo != nullptr;  // uniform: the low part only when asked for
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        vec4 hi, lo;
+        vec4 hi;
+        float x[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const float x = st.oacc[db][4 * g + t] * inv;
-          hi[t] = In16<TIn>::round(x);
-          lo[t] = In16<TIn>::round(x - (float)hi[t]);
+          x[t] = st.oacc[db][4 * g + t] * inv;
+          hi[t] = In16<TIn>::round(x[t]);
         }
         *reinterpret_cast<vec4*>(&so[l32 * kRow + db * 32 + 8 * g + 4 * hf]) = hi;
-        *reinterpret_cast<vec4*>(&sl[l32 * kRow + db * 32 + 8 * g + 4 * hf]) = lo;
+        if (want_lo) {
+          vec4 lo;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) lo[t] = In16<TIn>::round(x[t] - (float)hi[t]);
+          *reinterpret_cast<vec4*>(&sl[l32 * kRow + db * 32 + 8 * g + 4 * hf]) = lo;
+        }
       }
     __builtin_amdgcn_wave_barrier();
     extra_barrier();

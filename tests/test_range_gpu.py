@@ -1,11 +1,11 @@
 """GPU parity at input magnitudes far from unit scale.
 
-bf16 training without loss scaling hands the backward upstream gradients dO
-of about 1e-6 and smaller (nanoGPT runs bfloat16 autocast on GPUs with its
-gradient scaler disabled for bf16: page "nanoGPT: a real GPT in two 300-line
-files", section 2 "How the code works", train.py). bf16 keeps fp32's
-exponent range, so the kernels' fp16 matrix-core operands must not lose
-such values: each operand block carries a power-of-two scale.
+nanoGPT's train.py can train in bfloat16 on GPUs (page "nanoGPT: a real GPT
+in two 300-line files", section 2 "How the code works"). Read as training
+without loss scaling, which bf16's range allows, that hands the backward
+upstream gradients dO of about 1e-6 and smaller. bf16 keeps fp32's exponent
+range, so the kernels' fp16 matrix-core operands must not lose such values:
+each operand block carries a power-of-two scale.
 
 Each case multiplies one input by 2^k, runs forward + backward through the
 C ABI and the fp64 oracle on the same (exactly scaled) inputs, and holds
