@@ -63,17 +63,58 @@ struct KVRegs {
   typename In16<TIn>::vec k[kN], v[kN];
 };
 
+// A thread's chunk offsets in bytes from its tile's first K and V rows:
+// fixed for the whole loop, so a tile that lies below T is loaded from a
+// workgroup-uniform row pointer plus these (no per-tile address arithmetic
+// on the vector unit). Below 2^32: the host checks T * stride < 2^31.
+template <int D>
+struct KVOffsets {
+  static constexpr int kN = kBN * D / 8 / kThreads;
+  uint32_t k[kN], v[kN];
+};
+
+template <typename TIn, int D>
+__device__ __forceinline__ KVOffsets<D> fwd_tile_offsets(int ldk, int ldv, int tid) {
+  constexpr int kC = D / 8;
+  KVOffsets<D> o;
+#pragma unroll
+  for (int p = 0; p < KVOffsets<D>::kN; ++p) {
+    const int c = tid + kThreads * p;
+    const uint32_t col = (uint32_t)(c % kC) * 8u;
+    o.k[p] = ((uint32_t)(c / kC) * (uint32_t)ldk + col) * (uint32_t)sizeof(TIn);
+    o.v[p] = ((uint32_t)(c / kC) * (uint32_t)ldv + col) * (uint32_t)sizeof(TIn);
+  }
+  return o;
+}
+
 template <typename TIn, int D>
 __device__ __forceinline__ void fwd_load_tile(const TIn* kh, int ldk, const TIn* vh, int ldv,
-                                              int k0, int T, int tid, KVRegs<TIn, D>& r) {
+                                              int k0, int T, int tid, const KVOffsets<D>& off,
+                                              KVRegs<TIn, D>& r) {
   typedef typename In16<TIn>::vec vec;
   constexpr int kC = D / 8;  // chunks per row
+  const char* kb = reinterpret_cast<const char*>(kh + (size_t)k0 * (uint32_t)ldk);
+  const char* vb = reinterpret_cast<const char*>(vh + (size_t)k0 * (uint32_t)ldv);
+  uint32_t ok[KVOffsets<D>::kN], ov[KVOffsets<D>::kN];
+#pragma unroll
+  for (int p = 0; p < KVOffsets<D>::kN; ++p) {
+    ok[p] = off.k[p];
+    ov[p] = off.v[p];
+  }
+  if (k0 + kBN > T) {
+    // The sequence's last tile: rows past T - 1 read row T - 1 instead.
+#pragma unroll
+    for (int p = 0; p < KVOffsets<D>::kN; ++p) {
+      const int c = tid + kThreads * p;
+      const uint32_t row = (uint32_t)min(c / kC, T - 1 - k0), col = (uint32_t)(c % kC) * 8u;
+      ok[p] = (row * (uint32_t)ldk + col) * (uint32_t)sizeof(TIn);
+      ov[p] = (row * (uint32_t)ldv + col) * (uint32_t)sizeof(TIn);
+    }
+  }
 #pragma unroll
   for (int p = 0; p < KVRegs<TIn, D>::kN; ++p) {
-    const int c = tid + kThreads * p;
-    const int row = min(k0 + c / kC, T - 1), col = (c % kC) * 8;
-    r.k[p] = *reinterpret_cast<const vec*>(kh + row * ldk + col);
-    r.v[p] = *reinterpret_cast<const vec*>(vh + row * ldv + col);
+    r.k[p] = *reinterpret_cast<const vec*>(kb + ok[p]);
+    r.v[p] = *reinterpret_cast<const vec*>(vb + ov[p]);
   }
 }
 
@@ -125,6 +166,15 @@ __device__ __forceinline__ uint32_t tile_vmax_bits(const KVRegs<TIn, D>& r) {
 }
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+// x, through an empty volatile asm statement: a value the compiler cannot
+// compute ahead of the branch it sits in. The scores' maxima are only wanted
+// on the rare rescale path and start from such a value; without it the
+// compiler takes them on every tile, ahead of the branch.
+__device__ __forceinline__ float opaque_f32(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 // Per-wave state of the online softmax.
 template <int D>
@@ -196,13 +246,14 @@ __device__ __forceinline__ void fwd_tile(const TIn* cK, const f16* cV,
       s[kb] = In16<TIn>::mfma(*reinterpret_cast<const vec*>(arow + kk * 16), qf[kk], s[kb]);
   }
 
-  // The lane's maximum over the tile, scaled log2 units (rescales only).
+  // The lane's maximum over the tile, scaled log2 units (rescales only:
+  // opaque_f32 keeps the compiler from computing it on every tile).
   auto tile_max = [&]() {
-    float mx = fmaxf(s[0][0], s[0][1]);
+    float mx = opaque_f32(-INFINITY);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     return mx * scale_log2;
   };
 #pragma unroll
@@ -262,9 +313,9 @@ __device__ __forceinline__ void fwd_half(const TIn* cK, const f16* cV,
   }
   // The lane's maximum over the half, scaled log2 units (rescales only).
   auto half_max = [&]() {
-    float mx = fmaxf(s[0], s[1]);
+    float mx = opaque_f32(-INFINITY);
 #pragma unroll
-    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
     return mx * scale_log2;
   };
 #pragma unroll
@@ -378,8 +429,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + l32;  // the query column this lane owns
 
+  const KVOffsets<D> kvoff = fwd_tile_offsets<TIn, D>(ldk, ldv, tid);
   KVRegs<TIn, D> nxt;
-  fwd_load_tile<TIn, D>(kh, ldk, vh, ldv, 0, T, tid, nxt);
+  fwd_load_tile<TIn, D>(kh, ldk, vh, ldv, 0, T, tid, kvoff, nxt);
   {
     constexpr int kC = D / 8, kNQ = kBM * D / 8 / kThreads;
     vec xq[kNQ];
@@ -435,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
   for (; kt < n_full; ++kt, buf ^= 1) {
     const int k0 = kt * kBN;
     const bool has_next = kt + 1 < n_kt;
-    if (has_next) fwd_load_tile<TIn, D>(kh, ldk, vh, ldv, k0 + kBN, T, tid, nxt);
+    if (has_next) fwd_load_tile<TIn, D>(kh, ldk, vh, ldv, k0 + kBN, T, tid, kvoff, nxt);
     fwd_tile<TIn, D, DROP>(Kbuf(buf), Vbuf(buf), qf, k0, my_q, T, l32, hf, lane, scale_log2,
                            a.drop, tm.head, st);
     extra_barrier();
@@ -457,7 +509,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
   for (; kt < n_kt; ++kt, buf ^= 1) {
     const int k0 = kt * kBN;
     const bool has_next = kt + 1 < n_kt;
-    if (has_next) fwd_load_tile<TIn, D>(kh, ldk, vh, ldv, k0 + kBN, T, tid, nxt);
+    if (has_next) fwd_load_tile<TIn, D>(kh, ldk, vh, ldv, k0 + kBN, T, tid, kvoff, nxt);
     // Diagonal and boundary tiles, half by half: halves wholly in this wave's
     // future are skipped, the diagonal half gets the fixed triangle.
 #pragma unroll
