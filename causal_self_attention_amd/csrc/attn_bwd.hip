@@ -300,18 +300,28 @@ __device__ __forceinline__ void store_rows(float* stage, const f32x16 (&acc)[D /
 __device__ __forceinline__ void add_dq_block(const BwdArgs& a, int head, int qb0, int db, int l32,
                                              int hf, int T, float scale, int e,
                                              const f32x16& acc) {
-  const int lddq = (int)a.ldq.t;
-  float* dqh = a.dq + head_base(a.ldq, head, a.H) + qb0 * lddq + db * 32 + l32;
+  // Register r holds row 8(r/4) + 4hf + r%4 of the block, column l32: a
+  // workgroup-uniform row offset per register plus one per-lane byte offset
+  // (4hf rows and l32 columns). Written as one per-lane pointer per
+  // register, the compiler had computed all sixteen 64-bit pointers once and
+  // kept them live across the caller's loop (32 vector registers); here the
+  // row offsets are scalar and formed on every call (opaque_u32_uniform
+  // keeps them from being hoisted).
+  const uint32_t lddq = opaque_u32_uniform((uint32_t)a.ldq.t);
+  const uint32_t voff = (4u * (uint32_t)hf * lddq + (uint32_t)l32) * (uint32_t)sizeof(float);
+  float* blk = a.dq + head_base(a.ldq, head, a.H) + (size_t)(uint32_t)qb0 * lddq + db * 32;
+  auto add = [&](int r) {
+    float* row = blk + (size_t)(8 * (r >> 2) + (r & 3)) * lddq;
+    atomicAdd(reinterpret_cast<float*>(reinterpret_cast<char*>(row) + voff),
+              ldexpf(acc[r] * scale, e));
+  };
   if (qb0 + 32 <= T) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      atomicAdd(dqh + (8 * (r >> 2) + 4 * hf + (r & 3)) * lddq, ldexpf(acc[r] * scale, e));
+    for (int r = 0; r < 16; ++r) add(r);
   } else {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qr = 8 * (r >> 2) + 4 * hf + (r & 3);
-      if (qb0 + qr < T) atomicAdd(dqh + qr * lddq, ldexpf(acc[r] * scale, e));
-    }
+    for (int r = 0; r < 16; ++r)
+      if (qb0 + 8 * (r >> 2) + (r & 3) + 4 * hf < T) add(r);
   }
 }
 
@@ -478,15 +488,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
   const float sl2 = ldexpf(scale_log2, -(eq + ek));
   const int e_dv = -edo, e_dk = -(edo + ev + eq), e_dq = -(edo + ev + ek);
 
-  // The K operands of S = Q K^T (this wave's 32 keys): held in registers
-  // without dropout; the dropout build, short of registers, reads them from
-  // the staged K tile when used.
+  // The K operands of S = Q K^T (this wave's 32 keys), held in registers.
   f16x8 kreg[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    kreg[kk] = DROP ? zero_f16x8()
-                    : *reinterpret_cast<const f16x8*>(
-                          &sK[(wave * 32 + l32) * kRowQ + kk * 16 + 8 * hf]);
+    kreg[kk] = *reinterpret_cast<const f16x8*>(&sK[(wave * 32 + l32) * kRowQ + kk * 16 + 8 * hf]);
   int buf = 0;
   for (int qs = k0; qs < T; qs += kBQ, buf ^= 1) {
     extra_barrier();
@@ -547,10 +553,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
         const int arow = (mb * 32 + perm32(l32)) * kRowQ + 8 * hf;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-          const f16x8 kfr = DROP ? *reinterpret_cast<const f16x8*>(
-                                        &sK[(wave * 32 + l32) * kRowQ + kk * 16 + 8 * hf])
-                                  : kreg[kk];
-          s = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cQ[arow + kk * 16]), kfr, s);
+          s = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cQ[arow + kk * 16]), kreg[kk], s);
           dp = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cdO[arow + kk * 16]), vf[kk],
                                 dp);
         }

@@ -148,6 +148,24 @@ __device__ __forceinline__ f16x8 zero_f16x8() {
   return __builtin_bit_cast(f16x8, z);
 }
 
+// x, through an empty volatile asm statement: a value the compiler cannot
+// compute ahead of the branch it sits in. Work that only a rare branch needs
+// starts from such a value, so the compiler neither does it on every pass
+// nor hoists its invariant parts into registers kept live for the whole
+// loop.
+__device__ __forceinline__ float opaque_f32(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+// The same for a wave-uniform value, kept in a scalar register.
+__device__ __forceinline__ uint32_t opaque_u32_uniform(uint32_t x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
+// The float value of a bf16 bit pattern (the pattern in the low 16 bits).
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
 // Block exponents. The fp16 matrix-core operands carry a power-of-two scale
 // per operand block: x_s = x * 2^e is formed exactly (ldexp) before the
 // rounding to fp16, and every product of scaled operands is unscaled exactly

@@ -165,17 +165,6 @@ __device__ __forceinline__ uint32_t tile_vmax_bits(const KVRegs<TIn, D>& r) {
   return m.x > m.y ? m.x : m.y;
 }
 
-__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
-
-// x, through an empty volatile asm statement: a value the compiler cannot
-// compute ahead of the branch it sits in. The scores' maxima are only wanted
-// on the rare rescale path and start from such a value; without it the
-// compiler takes them on every tile, ahead of the branch.
-__device__ __forceinline__ float opaque_f32(float x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
 // Per-wave state of the online softmax.
 template <int D>
 struct FwdState {
