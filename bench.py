@@ -39,8 +39,9 @@ backward (QK^T recompute, dP, dV, dK, dQ).
 
 ``--all-configs`` prints one line per benchmark configuration (the
 Shakespeare-char layer in fp32 and bf16, the GPT-2 124M, 350M, 774M and
-1558M layers, the last also at T = 2048), each with the max-abs and
-mean-abs error of every output against the fp64 oracle on all heads.
+1558M layers, the last also at T = 2048, and the 774M layer's width as 10
+heads of 128), each with the max-abs and mean-abs error of every output
+against the fp64 oracle on all heads.
 
 ``--mode decode`` measures the inference path instead: one step = one
 gpt_attn_decode call (one new query per sequence and head against a
@@ -77,7 +78,7 @@ DEFAULT_DECODE_WORKLOAD = "gpt2_124m_decode_bf16_b64_h12_l1024"
 ALL_CONFIGS = ("shakespeare_char_f32_b1_h6_t256", "shakespeare_char_bf16_b64_h6_t256",
                "gpt2_124m_bf16_b12_h12_t1024", "gpt2_350m_bf16_b12_h16_t1024",
                "gpt2_774m_sharp_bf16_b8_h20_t1024", "gpt2_1558m_bf16_b4_h25_t1024",
-               "gpt2_1558m_long_bf16_b2_h25_t2048")
+               "gpt2_1558m_long_bf16_b2_h25_t2048", "gpt2_774m_d128_bf16_b8_h10_t1024")
 ONE_THREAD_WORKLOAD = "shakespeare_char_f32_b1_h6_t256"
 DOMINANT_KERNEL = "attn_bwd_main_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bwd_main_gpt2_124m_traffic.json")
@@ -519,8 +520,10 @@ def run_train(w, args, with_errors: bool = False, cpu_base: bool = True):
                 "in_step_ms": round(in_step["prep"] + in_step["main"], 5),
                 "tflops": round(tf(bwd_flop, t_bwd), 2),
                 "pct_peak": round(100 * tf(bwd_flop, t_bwd) / peak, 2)},
-        "roofline": {"kernel": DOMINANT_KERNEL if w.dtype != "f32" else
-                     "attn_bwd_dkdv_f32_kernel + attn_bwd_dq_f32_kernel",
+        "roofline": {"kernel": ("attn_bwd_dkdv_f32_kernel + attn_bwd_dq_f32_kernel"
+                                if w.dtype == "f32" else
+                                "attn_bwd_dkdv_kernel + attn_bwd_dq_kernel" if w.D == 128
+                                else DOMINANT_KERNEL),
                      "bound": "mfma" if w.dtype != "f32" else "alu",
                      "achieved": round(main_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(main_tflops / peak, 4),

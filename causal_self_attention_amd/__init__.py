@@ -30,7 +30,7 @@ conveniences, ``attention_forward``, ``attention_backward`` and
 helpers ``split_qkv_heads`` / ``merged_heads_view`` for the fused [B, T, 3C]
 projection layout. Tensors are logically [B, H, T, D]: contiguous for the
 plain calls, any layout with unit stride along D for the strided ones; q, k,
-v, o, dout are float32, bfloat16 or float16 with D in {32, 64}; lse
+v, o, dout are float32, bfloat16 or float16 with D in {32, 64, 128}; lse
 [B, H, T] (contiguous) and dq, dk, dv are float32. o_lo (16-bit dtypes only,
 may be None) is the low part of the forward's fp32 O in the same dtype,
 which the backward uses for an accurate delta = rowsum(dO * O).
@@ -68,7 +68,7 @@ EXPORTED_SYMBOLS = ("gpt_attn_fwd", "gpt_attn_bwd", "gpt_attn_bwd_prep", "gpt_at
                     "gpt_attn_decode_workspace_bytes", "gpt_attn_bwd_workspace_bytes",
                     "gpt_attn_status_string", "gpt_attn_abi_version")
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 NOALLOC_SCRATCH_BYTES = 8 << 20
 
 

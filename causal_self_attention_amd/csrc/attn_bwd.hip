@@ -1,5 +1,5 @@
 // Causal attention backward, bf16 or fp16 inputs, fp32 accumulation and fp32
-// gradients, head dim D in {32, 64}, for gfx950 (CDNA4).
+// gradients, head dim D in {32, 64, 128}, for gfx950 (CDNA4).
 //
 // The gradient of sum(dO * O) for O = softmax(Q K^T / sqrt(D), causal) V:
 // what autograd forms for nanoGPT's loss.backward() through the fused
@@ -149,8 +149,26 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const BwdArgs a, int
     for (int w = 0; w < 4; ++w)
 #pragma unroll
       for (int j = 0; j < 3; ++j) st[j] = fmaxf(st[j], red[w][j]);
-    reinterpret_cast<f32x4*>(a.stats)[(size_t)head * n_chunks + chunk] = st;
+    reinterpret_cast<f32x4*>(a.stats)[((size_t)head * n_chunks + chunk) * (kStatFloats / 4)] = st;
   }
+}
+
+// dO's block exponent: the largest e with |dS * 2^(e + ev)| < 2^14, from
+// |dS| <= z |dP| + |delta| <= z D max|dO| max|V| + max|delta| (z: the dropout
+// survivor scale, 1 without dropout; V staged as V * 2^ev), so every rounded
+// dS fits fp16 with a factor of two to spare. 0 when both maxima are 0 or
+// not finite.
+__device__ __forceinline__ int dout_exp(float mdo, float mdel, float mv, int ev, float zs, int D) {
+  constexpr int kNone = -(1 << 20);
+  int t1 = kNone, t2 = kNone;
+  if (mdo > 0.f && mdo <= 3.402823466e38f) {
+    const int ka = __builtin_amdgcn_frexp_expf(mdo);  // mdo < 2^ka
+    const float x = zs * (float)D * ldexpf(mv, ev) * ldexpf(mdo, -ka);
+    t1 = ka + (x > 0.f ? __builtin_amdgcn_frexp_expf(x) : 0);  // z D max|dO| max|V_s| < 2^t1
+  }
+  if (mdel > 0.f && mdel <= 3.402823466e38f)
+    t2 = __builtin_amdgcn_frexp_expf(mdel) + ev;  // max|delta| 2^ev < 2^t2
+  return (t1 != kNone || t2 != kNone) ? 13 - max(t1, t2) : 0;
 }
 
 // Loading a 64-query tile is split in two so the global loads can be issued
@@ -409,9 +427,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
   for (int p = 0; p < kKP; ++p) fold_absmax(kraw[p], mk);
   {
     const int n_chunks = (T + kStatRows - 1) / kStatRows;
-    const f32x4* st = reinterpret_cast<const f32x4*>(a.stats) + (size_t)tm.head * n_chunks;
+    const f32x4* st =
+        reinterpret_cast<const f32x4*>(a.stats) + (size_t)tm.head * n_chunks * (kStatFloats / 4);
     for (int c = k0 / kStatRows + lane; c < n_chunks; c += 64) {
-      const f32x4 x = st[c];
+      const f32x4 x = st[c * (kStatFloats / 4)];
       mq = fmaxf(mq, x[0]);
       mdo = fmaxf(mdo, x[1]);
       mdel = fmaxf(mdel, x[2]);
@@ -432,29 +451,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
     mk = fmaxf(mk, sRed[w][0]);
     mv = fmaxf(mv, sRed[w][1]);
   }
-  // Q and K to [2^13, 2^14) (only their fp16 range matters); V to [1, 2).
-  // dO: the largest exponent with |dS * 2^(edo + ev)| < 2^14, from
-  // |dS| <= z |dP| + |delta| <= z D max|dO| max|V| + max|delta| (z: the
-  // dropout survivor scale, 1 without dropout), so every rounded dS fits
-  // fp16 with a factor of two to spare.
+  // Q and K to [2^13, 2^14) (only their fp16 range matters); V to [1, 2);
+  // dO from the dS bound (dout_exp).
   const float zs = DROP ? a.drop.scale : 1.f;
   const int ek = __builtin_amdgcn_readfirstlane(block_exp(mk, 13));
   const int ev = __builtin_amdgcn_readfirstlane(block_exp(mv, 0));
   const int eq = __builtin_amdgcn_readfirstlane(block_exp(mq, 13));
-  int edo = 0;
-  {
-    constexpr int kNone = -(1 << 20);
-    int t1 = kNone, t2 = kNone;
-    if (mdo > 0.f && mdo <= 3.402823466e38f) {
-      const int ka = __builtin_amdgcn_frexp_expf(mdo);  // mdo < 2^ka
-      const float x = zs * (float)D * ldexpf(mv, ev) * ldexpf(mdo, -ka);
-      t1 = ka + (x > 0.f ? __builtin_amdgcn_frexp_expf(x) : 0);  // z D max|dO| max|V_s| < 2^t1
-    }
-    if (mdel > 0.f && mdel <= 3.402823466e38f)
-      t2 = __builtin_amdgcn_frexp_expf(mdel) + ev;  // max|delta| 2^ev < 2^t2
-    if (t1 != kNone || t2 != kNone) edo = 13 - max(t1, t2);
-  }
-  edo = __builtin_amdgcn_readfirstlane(edo);
+  const int edo = __builtin_amdgcn_readfirstlane(dout_exp(mdo, mdel, mv, ev, zs, D));
 
   f16x8 vf[D / 16];
 #pragma unroll
@@ -676,6 +679,466 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
                 kw0, T, l32, hf, lane);
 }
 
+// ---------------------------------------------------------------------------
+// Head dimension 128. A wave that owns 32 keys would hold 128 registers of dK
+// and dV accumulators and 64 of K and V operands, more than two waves per
+// SIMD can hold next to the main kernel's dQ work. So the backward runs as
+// two kernels after the preprocess: attn_bwd_dkdv_kernel (the main kernel's
+// step without dQ, one wave per SIMD) and attn_bwd_dq_kernel (dQ = dS K with
+// S and dP recomputed, one workgroup per 128 queries, like the forward), and
+// dQ is written once instead of accumulated with atomics. The products and
+// their block exponents are those of the main kernel.
+
+constexpr int kW128 = 4;               // waves per workgroup in both kernels
+constexpr int kT128 = 64 * kW128;      // threads
+constexpr int kBK128 = 32 * kW128;     // keys per dK/dV workgroup (one statistics chunk)
+constexpr int kBM128 = 32 * kW128;     // queries per dQ workgroup (one statistics chunk)
+static_assert(kBK128 == kStatRows && kBM128 == kStatRows, "one chunk per workgroup");
+static_assert(kT128 == kLoaders, "every thread of the dK/dV kernel loads query tiles");
+
+// dK and dV for one workgroup of 128 keys: waves 0..3 own 32 keys each, as
+// the main kernel's waves do; all 256 threads load the next query tile a step
+// ahead. Also records the largest |K| and |V| of its keys (one statistics
+// chunk) for the dQ kernel.
+template <typename TIn, int D, bool DROP>
+__global__ __launch_bounds__(kT128, 1) void attn_bwd_dkdv_kernel(const BwdArgs a, int n_ktiles,
+                                                                 float scale, float scale_log2) {
+  typedef typename In16<TIn>::vec vec;
+  constexpr int kRowQ = row_of<D>();
+  constexpr int kDB = D / 32;
+  __shared__ __attribute__((aligned(16))) f16 sQ[2][kBQ * kRowQ];   // [q][d]
+  __shared__ __attribute__((aligned(16))) f16 sdO[2][kBQ * kRowQ];  // [q][d]
+  __shared__ __attribute__((aligned(16))) float sL[2][kBQ];         // LSE * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[2][kBQ];         // -delta
+  // Dropout: each wave's 32 x 32 keep-mask tile [query][key].
+  __shared__ __attribute__((aligned(16))) f16 sM[DROP ? kW128 : 1][32 * kRowS];
+  __shared__ float sRed[kW128][2];
+
+  const int T = a.T;
+  const TileMap tm = map_tile_xcd(blockIdx.x, a.n_heads, n_ktiles, false);
+  if (!tm.valid) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+
+  const size_t roff = (size_t)tm.head * (size_t)T;
+  const TIn* __restrict__ qh = static_cast<const TIn*>(a.q) + head_base(a.lq, tm.head, a.H);
+  const TIn* __restrict__ kh = static_cast<const TIn*>(a.k) + head_base(a.lk, tm.head, a.H);
+  const TIn* __restrict__ vh = static_cast<const TIn*>(a.v) + head_base(a.lv, tm.head, a.H);
+  const TIn* __restrict__ doh = static_cast<const TIn*>(a.dout) + head_base(a.ldo, tm.head, a.H);
+  const int ldq = (int)a.lq.t, ldk = (int)a.lk.t, ldv = (int)a.lv.t, lddo = (int)a.ldo.t;
+  const float* lseh = a.lse + roff;
+  const float* delh = a.delta + roff;
+
+  const int k0 = tm.tile * kBK128;
+  const int kw0 = k0 + wave * 32;
+  const int my_key = kw0 + l32;
+
+  // K and V of this lane's key as the B operands of S and dP (8 dims per
+  // 16-dim step, half hf); the first query tile; all issued before use.
+  vec kraw[D / 16], vraw[D / 16];
+  const int krow = min(my_key, T - 1);
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    kraw[kk] = *reinterpret_cast<const vec*>(kh + krow * ldk + kk * 16 + 8 * hf);
+    vraw[kk] = *reinterpret_cast<const vec*>(vh + krow * ldv + kk * 16 + 8 * hf);
+  }
+  TileRegs<TIn, D> nxt;
+  bwd_load_tile<TIn, D>(qh, ldq, doh, lddo, lseh, delh, k0, T, tid, nxt);
+
+  const int n_chunks = (T + kStatRows - 1) / kStatRows;
+  float mk = 0.f, mv = 0.f, mq = 0.f, mdo = 0.f, mdel = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    fold_absmax(kraw[kk], mk);
+    fold_absmax(vraw[kk], mv);
+  }
+  {
+    const f32x4* st =
+        reinterpret_cast<const f32x4*>(a.stats) + (size_t)tm.head * n_chunks * (kStatFloats / 4);
+    for (int c = k0 / kStatRows + lane; c < n_chunks; c += 64) {
+      const f32x4 x = st[c * (kStatFloats / 4)];
+      mq = fmaxf(mq, x[0]);
+      mdo = fmaxf(mdo, x[1]);
+      mdel = fmaxf(mdel, x[2]);
+    }
+  }
+  mk = wave_max(mk);
+  mv = wave_max(mv);
+  mq = wave_max(mq);
+  mdo = wave_max(mdo);
+  mdel = wave_max(mdel);
+  if (lane == 0) {
+    sRed[wave][0] = mk;
+    sRed[wave][1] = mv;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kW128; ++w) {
+    mk = fmaxf(mk, sRed[w][0]);
+    mv = fmaxf(mv, sRed[w][1]);
+  }
+  if (tid == 0) {
+    const f32x4 kv = {mk, mv, 0.f, 0.f};
+    reinterpret_cast<f32x4*>(a.stats)[((size_t)tm.head * n_chunks + k0 / kStatRows) *
+                                          (kStatFloats / 4) + 1] = kv;
+  }
+  const float zs = DROP ? a.drop.scale : 1.f;
+  const int ek = __builtin_amdgcn_readfirstlane(block_exp(mk, 13));
+  const int ev = __builtin_amdgcn_readfirstlane(block_exp(mv, 0));
+  const int eq = __builtin_amdgcn_readfirstlane(block_exp(mq, 13));
+  const int edo = __builtin_amdgcn_readfirstlane(dout_exp(mdo, mdel, mv, ev, zs, D));
+
+  f16x8 kreg[D / 16], vf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    kreg[kk] = my_key < T ? cvt_f16_scaled(kraw[kk], ek) : zero_f16x8();
+    vf[kk] = my_key < T ? cvt_f16_scaled(vraw[kk], ev) : zero_f16x8();
+  }
+  f32x16 dvacc[kDB], dkacc[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dvacc[db][r] = 0.f;
+      dkacc[db][r] = 0.f;
+    }
+  bwd_store_tile<TIn, D>(sQ[0], sdO[0], sL[0], sD[0], nxt, k0, T, tid, eq, edo, edo + ev);
+  __syncthreads();
+
+  const float sl2 = ldexpf(scale_log2, -(eq + ek));
+  int buf = 0;
+  for (int qs = k0; qs < T; qs += kBQ, buf ^= 1) {
+    extra_barrier();
+    const bool has_next = qs + kBQ < T;
+    if (has_next) bwd_load_tile<TIn, D>(qh, ldq, doh, lddo, lseh, delh, qs + kBQ, T, tid, nxt);
+    const f16* cQ = sQ[buf];
+    const f16* cdO = sdO[buf];
+    const float* cL = sL[buf];
+    const float* cD = sD[buf];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int qb0 = qs + mb * 32;
+      const int kind = block_kind(kw0, qb0, T);
+      if (kind == kEmpty) continue;
+      f16x8 mk2[2];
+      if (DROP) {
+        // Lane L draws query qb0 + L/2, keys kw0 + 16 (L%2) .. +15 into row
+        // L/2 of the wave's mask tile, read back in the lane = key order.
+        uint16_t* tile = reinterpret_cast<uint16_t*>(sM[DROP ? wave : 0]);
+        uint32_t m0[4], m1[4];
+        const uint32_t grp = (uint32_t)(kw0 >> 3) + 2u * (uint32_t)(lane & 1);
+        keep_mask8(a.drop, (uint32_t)tm.head, (uint32_t)(qb0 + (lane >> 1)), grp, m0);
+        keep_mask8(a.drop, (uint32_t)tm.head, (uint32_t)(qb0 + (lane >> 1)), grp + 1, m1);
+        i32x4* dst = reinterpret_cast<i32x4*>(tile + (lane >> 1) * kRowS + 16 * (lane & 1));
+        dst[0] = i32x4{(int)m0[0], (int)m0[1], (int)m0[2], (int)m0[3]};
+        dst[1] = i32x4{(int)m1[0], (int)m1[1], (int)m1[2], (int)m1[3]};
+        __builtin_amdgcn_wave_barrier();
+      }
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+      if (DROP) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const f32x4 nd = *reinterpret_cast<const f32x4*>(&cD[mb * 32 + 16 * c + 8 * hf + 4 * h]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) dp[8 * c + 4 * h + t] = nd[t];
+          }
+      }
+      const int arow = (mb * 32 + perm32(l32)) * kRowQ + 8 * hf;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        s = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cQ[arow + kk * 16]), kreg[kk], s);
+        dp = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&cdO[arow + kk * 16]), vf[kk], dp);
+      }
+      if (DROP) {
+        const f16* tile = sM[DROP ? wave : 0];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) mk2[c] = lds_operand_tr(tile, kRowS, 16 * c, 0, lane);
+        __builtin_amdgcn_wave_barrier();
+      } else {
+        mk2[0] = mk2[1] = zero_f16x8();
+      }
+      f16x8 pf[2], dsf[2];
+      if (kind == kFull)
+        bwd_p_ds<kFull, DROP>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, sl2, mk2, zs, pf, dsf);
+      else if (kind == kDiag)
+        bwd_p_ds<kDiag, DROP>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, sl2, mk2, zs, pf, dsf);
+      else
+        bwd_p_ds<kGeneral, DROP>(s, dp, cL, cD, mb * 32, qb0, kw0, T, l32, hf, sl2, mk2, zs, pf,
+                                 dsf);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int ks = 2 * mb + c;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          dvacc[db] = mfma32x32x16_f16(lds_operand_tr(cdO, kRowQ, ks * 16, db * 32, lane), pf[c],
+                                       dvacc[db]);
+          dkacc[db] = mfma32x32x16_f16(lds_operand_tr(cQ, kRowQ, ks * 16, db * 32, lane), dsf[c],
+                                       dkacc[db]);
+        }
+      }
+    }
+    // Stage the prefetched tile into the other buffer, last read in the
+    // previous step before its barrier.
+    extra_barrier();
+    if (has_next)
+      bwd_store_tile<TIn, D>(sQ[buf ^ 1], sdO[buf ^ 1], sL[buf ^ 1], sD[buf ^ 1], nxt, qs + kBQ,
+                             T, tid, eq, edo, edo + ev);
+    __syncthreads();
+  }
+
+  // dV = z dV_acc 2^-edo and dK = s dK_acc 2^-(edo + ev + eq), whole rows
+  // through LDS (each wave's 32 rows: waves 0, 1 in the Q buffers, waves 2, 3
+  // in the dO buffers, free after the loop's last barrier).
+  constexpr int kEp = D + 4;
+  static_assert(sizeof(sQ) >= 2 * 32 * kEp * sizeof(float), "staging fits");
+  static_assert(sizeof(sdO) >= 2 * 32 * kEp * sizeof(float), "staging fits");
+  float* stage = reinterpret_cast<float*>(wave < 2 ? &sQ[0][0] : &sdO[0][0]) + (wave & 1) * 32 * kEp;
+  store_rows<D>(stage, dvacc, zs, -edo, a.dv + head_base(a.ldv, tm.head, a.H), (int)a.ldv.t, kw0,
+                T, l32, hf, lane);
+  store_rows<D>(stage, dkacc, scale, -(edo + ev + eq), a.dk + head_base(a.ldk, tm.head, a.H),
+                (int)a.ldk.t, kw0, T, l32, hf, lane);
+}
+
+// K and V tiles of the dQ kernel: 64 keys, staged into LDS as fp16 scaled by
+// 2^ek and 2^ev, loaded a tile ahead as raw 16-byte chunks (rows clamped to
+// T - 1; rows past T are zeroed when staged).
+template <typename TIn, int D>
+struct KVTile {
+  static constexpr int kN = 64 * D / 8 / kT128;
+  typename In16<TIn>::vec k[kN], v[kN];
+};
+
+template <typename TIn, int D>
+__device__ __forceinline__ void dq_load_kv(const TIn* kh, int ldk, const TIn* vh, int ldv, int k0,
+                                           int T, int tid, KVTile<TIn, D>& r) {
+  typedef typename In16<TIn>::vec vec;
+  constexpr int kC = D / 8;
+#pragma unroll
+  for (int p = 0; p < KVTile<TIn, D>::kN; ++p) {
+    const int c = tid + kT128 * p;
+    const int row = min(k0 + c / kC, T - 1), col = (c % kC) * 8;
+    r.k[p] = *reinterpret_cast<const vec*>(kh + row * ldk + col);
+    r.v[p] = *reinterpret_cast<const vec*>(vh + row * ldv + col);
+  }
+}
+
+template <typename TIn, int D>
+__device__ __forceinline__ void dq_store_kv(f16* Ks, f16* Vs, const KVTile<TIn, D>& r, int k0,
+                                            int T, int tid, int ek, int ev) {
+  constexpr int kC = D / 8, kRow = row_of<D>();
+#pragma unroll
+  for (int p = 0; p < KVTile<TIn, D>::kN; ++p) {
+    const int c = tid + kT128 * p;
+    const int row = c / kC, col = (c % kC) * 8;
+    const bool ok = k0 + row < T;
+    *reinterpret_cast<f16x8*>(&Ks[row * kRow + col]) = ok ? cvt_f16_scaled(r.k[p], ek) : zero_f16x8();
+    *reinterpret_cast<f16x8*>(&Vs[row * kRow + col]) = ok ? cvt_f16_scaled(r.v[p], ev) : zero_f16x8();
+  }
+}
+
+// One 32-key half (keys key0 ..) of a tile for one wave of the dQ kernel.
+// S^T = K Q^T and dP^T = V dO^T (lane = query, registers = keys in the
+// perm32 order), P = exp2(S s log2 e - LSE log2 e), dS = P (dP - delta), and
+// dQ^T += K^T dS^T with dS^T straight from the registers as the B operand.
+// KIND as in the forward: kFull unmasked, kDiag the fixed triangle, kGeneral
+// the limit min(query, T - 1).
+template <int D, int KIND, bool DROP>
+__device__ __forceinline__ void dq_half(const f16* Ks, const f16* Vs, const f16x8 (&qf)[D / 16],
+                                        const f16x8 (&dof)[D / 16], int kb, int k0, int my_q,
+                                        int T, int l32, int hf, int lane, float sl2, float lse2,
+                                        float ndel, float zs, const Dropout& drop, int head,
+                                        f32x16 (&acc)[D / 32]) {
+  constexpr int kRow = row_of<D>();
+  const int arow = (kb * 32 + perm32(l32)) * kRow + 8 * hf;
+  f32x16 s, dp;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s[r] = 0.f;
+    dp[r] = DROP ? 0.f : ndel;  // without dropout the chain ends at dP - delta
+  }
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    s = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&Ks[arow + kk * 16]), qf[kk], s);
+    dp = mfma32x32x16_f16(*reinterpret_cast<const f16x8*>(&Vs[arow + kk * 16]), dof[kk], dp);
+  }
+  // Register 8c + t of half hf holds key k0 + 32kb + 16c + 8hf + t.
+  const int lim = min(my_q, T - 1) - (k0 + 32 * kb) - 8 * hf;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    uint32_t m[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+    if (DROP)
+      keep_mask8(drop, (uint32_t)head, (uint32_t)my_q, (uint32_t)((k0 + 32 * kb + 16 * c) >> 3) + hf,
+                 m);
+    float ds[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int r = 8 * c + t;
+      float p = fast_exp2(fmaf(s[r], sl2, -lse2));
+      if (KIND == kDiag) p = (16 * c + t > l32 - 8 * hf) ? 0.f : p;
+      if (KIND == kGeneral) p = (16 * c + t > lim) ? 0.f : p;
+      if (DROP) {
+        const bool kept = (m[t >> 1] >> (16 * (t & 1))) & 1u;
+        ds[t] = p * ((kept ? dp[r] * zs : 0.f) + ndel);
+      } else {
+        ds[t] = p * dp[r];
+      }
+    }
+    const f16x8 dsf = pack_f16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+    const int ks = 2 * kb + c;  // 16-key step inside the tile
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      acc[db] = mfma32x32x16_f16(lds_operand_tr(Ks, kRow, ks * 16, db * 32, lane), dsf, acc[db]);
+  }
+}
+
+// dQ for one workgroup of 128 queries (4 waves x 32, one statistics chunk):
+// the forward's loop over 64-key tiles up to the diagonal, with P taken
+// exactly from the saved LSE. One wave per SIMD: the dQ accumulators and the
+// Q and dO operands (128 registers) next to the tile's products exceed what
+// two waves per SIMD can hold. Exponents: Q, dO and delta from this chunk's
+// statistics, K and V from the chunks of every key visited (written by the
+// dK/dV kernel), dO's from the dS bound.
+template <typename TIn, int D, bool DROP>
+__global__ __launch_bounds__(kT128, 1) void attn_bwd_dq_kernel(const BwdArgs a, int n_qtiles,
+                                                               float scale, float scale_log2) {
+  typedef typename In16<TIn>::vec vec;
+  constexpr int kRow = row_of<D>();
+  constexpr int kBN = 64;
+  // Two K/V buffers, fp16 [key][d]. In the prologue the Q rows (buffer 0)
+  // and dO rows (buffer 1), 128 x D each, pass through them.
+  __shared__ __attribute__((aligned(16))) f16 lds[2][2 * kBN * kRow];
+  static_assert(kBM128 * kRow <= 2 * kBN * kRow, "Q / dO rows fit one buffer");
+
+  const int T = a.T;
+  const TileMap tm = map_tile_xcd(blockIdx.x, a.n_heads, n_qtiles, true);
+  if (!tm.valid) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+
+  const size_t roff = (size_t)tm.head * (size_t)T;
+  const TIn* __restrict__ qh = static_cast<const TIn*>(a.q) + head_base(a.lq, tm.head, a.H);
+  const TIn* __restrict__ kh = static_cast<const TIn*>(a.k) + head_base(a.lk, tm.head, a.H);
+  const TIn* __restrict__ vh = static_cast<const TIn*>(a.v) + head_base(a.lv, tm.head, a.H);
+  const TIn* __restrict__ doh = static_cast<const TIn*>(a.dout) + head_base(a.ldo, tm.head, a.H);
+  const int ldq = (int)a.lq.t, ldk = (int)a.lk.t, ldv = (int)a.lv.t, lddo = (int)a.ldo.t;
+
+  const int q0 = tm.tile * kBM128;
+  const int qw0 = q0 + wave * 32;
+  const int my_q = qw0 + l32;
+
+  // Issue the first K/V tile and this workgroup's Q and dO rows.
+  KVTile<TIn, D> nxt;
+  dq_load_kv<TIn, D>(kh, ldk, vh, ldv, 0, T, tid, nxt);
+  constexpr int kC = D / 8, kNQ = kBM128 * D / 8 / kT128;
+  vec xq[kNQ], xd[kNQ];
+#pragma unroll
+  for (int p = 0; p < kNQ; ++p) {
+    const int c = tid + kT128 * p;
+    const int row = min(q0 + c / kC, T - 1);
+    xq[p] = *reinterpret_cast<const vec*>(qh + row * ldq + (c % kC) * 8);
+    xd[p] = *reinterpret_cast<const vec*>(doh + row * lddo + (c % kC) * 8);
+  }
+  const float lse2 = my_q < T ? a.lse[roff + my_q] * kLog2e : 0.f;
+  const float del = my_q < T ? a.delta[roff + my_q] : 0.f;
+
+  // Exponents.
+  const int n_chunks = (T + kStatRows - 1) / kStatRows;
+  const f32x4* st =
+      reinterpret_cast<const f32x4*>(a.stats) + (size_t)tm.head * n_chunks * (kStatFloats / 4);
+  const f32x4 own = st[(q0 / kStatRows) * (kStatFloats / 4)];
+  float mk = 0.f, mv = 0.f;
+  for (int c = lane; c <= q0 / kStatRows; c += 64) {
+    const f32x4 x = st[c * (kStatFloats / 4) + 1];
+    mk = fmaxf(mk, x[0]);
+    mv = fmaxf(mv, x[1]);
+  }
+  mk = wave_max(mk);
+  mv = wave_max(mv);
+  const float zs = DROP ? a.drop.scale : 1.f;
+  const int ek = __builtin_amdgcn_readfirstlane(block_exp(mk, 13));
+  const int ev = __builtin_amdgcn_readfirstlane(block_exp(mv, 0));
+  const int eq = __builtin_amdgcn_readfirstlane(block_exp(own[0], 13));
+  const int edo = __builtin_amdgcn_readfirstlane(dout_exp(own[1], own[2], mv, ev, zs, D));
+  const float sl2 = ldexpf(scale_log2, -(eq + ek));
+  const float ndel = -ldexpf(del, edo + ev);
+
+  // Q and dO rows into LDS (fp16, scaled), then each wave's fragments: lane
+  // holds dims 16kk + 8hf .. +7 of its query (the B operands of S^T, dP^T).
+  f16* Qs = lds[0];
+  f16* dOs = lds[1];
+#pragma unroll
+  for (int p = 0; p < kNQ; ++p) {
+    const int c = tid + kT128 * p;
+    const int row = c / kC, col = (c % kC) * 8;
+    const bool ok = q0 + row < T;
+    *reinterpret_cast<f16x8*>(&Qs[row * kRow + col]) = ok ? cvt_f16_scaled(xq[p], eq) : zero_f16x8();
+    *reinterpret_cast<f16x8*>(&dOs[row * kRow + col]) = ok ? cvt_f16_scaled(xd[p], edo) : zero_f16x8();
+  }
+  __syncthreads();
+  f16x8 qf[D / 16], dof[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    qf[kk] = *reinterpret_cast<const f16x8*>(&Qs[(wave * 32 + l32) * kRow + kk * 16 + 8 * hf]);
+    dof[kk] = *reinterpret_cast<const f16x8*>(&dOs[(wave * 32 + l32) * kRow + kk * 16 + 8 * hf]);
+  }
+  __syncthreads();  // every wave holds its fragments: both buffers are free
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+  auto Kb = [&](int b) { return lds[b]; };
+  auto Vb = [&](int b) { return lds[b] + kBN * kRow; };
+  dq_store_kv<TIn, D>(Kb(0), Vb(0), nxt, 0, T, tid, ek, ev);
+  __syncthreads();
+
+  const int kv_end = min(T, q0 + kBM128);
+  const int n_kt = (kv_end + kBN - 1) / kBN;
+  int buf = 0;
+  for (int kt = 0; kt < n_kt; ++kt, buf ^= 1) {
+    const int k0 = kt * kBN;
+    const bool has_next = kt + 1 < n_kt;
+    if (has_next) dq_load_kv<TIn, D>(kh, ldk, vh, ldv, k0 + kBN, T, tid, nxt);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int kind = block_kind(k0 + 32 * kb, qw0, T);
+      if (kind == kFull)
+        dq_half<D, kFull, DROP>(Kb(buf), Vb(buf), qf, dof, kb, k0, my_q, T, l32, hf, lane, sl2,
+                                lse2, ndel, zs, a.drop, tm.head, acc);
+      else if (kind == kDiag)
+        dq_half<D, kDiag, DROP>(Kb(buf), Vb(buf), qf, dof, kb, k0, my_q, T, l32, hf, lane, sl2,
+                                lse2, ndel, zs, a.drop, tm.head, acc);
+      else if (kind == kGeneral)
+        dq_half<D, kGeneral, DROP>(Kb(buf), Vb(buf), qf, dof, kb, k0, my_q, T, l32, hf, lane,
+                                   sl2, lse2, ndel, zs, a.drop, tm.head, acc);
+    }
+    extra_barrier();
+    if (has_next) dq_store_kv<TIn, D>(Kb(buf ^ 1), Vb(buf ^ 1), nxt, k0 + kBN, T, tid, ek, ev);
+    __syncthreads();
+  }
+
+  // dQ = s dQ_acc 2^-(edo + ev + ek), whole rows through LDS (both K/V
+  // buffers are free after the loop's last barrier).
+  constexpr int kEp = D + 4;
+  static_assert(sizeof(lds) >= kW128 * 32 * kEp * sizeof(float), "staging fits");
+  float* stage = reinterpret_cast<float*>(&lds[0][0]) + wave * 32 * kEp;
+  store_rows<D>(stage, acc, scale, -(edo + ev + ek), a.dq + head_base(a.ldq, tm.head, a.H),
+                (int)a.ldq.t, qw0, T, l32, hf, lane);
+}
+
 template <typename TIn, int D>
 hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
   const int n_chunks = (int)bwd_stat_chunks(a.T);
@@ -687,28 +1150,61 @@ hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
 
 template <typename TIn, int D>
 hipError_t launch_main(const BwdArgs& a, hipStream_t stream) {
-  const int n_ktiles = (a.T + kBK - 1) / kBK;
-  const float scale = 1.f / __builtin_sqrtf((float)D);
-  const dim3 grid(tiled_grid(a.n_heads, n_ktiles));
-  if (a.drop.thr != 0)
-    hipLaunchKernelGGL((attn_bwd_main_kernel<TIn, D, true>), grid, dim3(kThreads), 0, stream, a,
-                       n_ktiles, scale, scale * kLog2e);
-  else
-    hipLaunchKernelGGL((attn_bwd_main_kernel<TIn, D, false>), grid, dim3(kThreads), 0, stream, a,
-                       n_ktiles, scale, scale * kLog2e);
-  return hipGetLastError();
+  if constexpr (D == 128) {
+    const int n_tiles = (a.T + kStatRows - 1) / kStatRows;
+    const float scale = 1.f / __builtin_sqrtf((float)D);
+    const dim3 grid(tiled_grid(a.n_heads, n_tiles));
+    if (a.drop.thr != 0)
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<TIn, D, true>), grid, dim3(kT128), 0, stream, a,
+                         n_tiles, scale, scale * kLog2e);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<TIn, D, false>), grid, dim3(kT128), 0, stream, a,
+                         n_tiles, scale, scale * kLog2e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.drop.thr != 0)
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<TIn, D, true>), grid, dim3(kT128), 0, stream, a,
+                         n_tiles, scale, scale * kLog2e);
+    else
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<TIn, D, false>), grid, dim3(kT128), 0, stream, a,
+                         n_tiles, scale, scale * kLog2e);
+    return hipGetLastError();
+  } else {
+    const int n_ktiles = (a.T + kBK - 1) / kBK;
+    const float scale = 1.f / __builtin_sqrtf((float)D);
+    const dim3 grid(tiled_grid(a.n_heads, n_ktiles));
+    if (a.drop.thr != 0)
+      hipLaunchKernelGGL((attn_bwd_main_kernel<TIn, D, true>), grid, dim3(kThreads), 0, stream,
+                         a, n_ktiles, scale, scale * kLog2e);
+    else
+      hipLaunchKernelGGL((attn_bwd_main_kernel<TIn, D, false>), grid, dim3(kThreads), 0, stream,
+                         a, n_ktiles, scale, scale * kLog2e);
+    return hipGetLastError();
+  }
 }
 
 }  // namespace
 
+template <typename TIn>
+hipError_t launch_prep_d(const BwdArgs& a, int D, hipStream_t stream) {
+  return D == 32   ? launch_prep<TIn, 32>(a, stream)
+         : D == 64 ? launch_prep<TIn, 64>(a, stream)
+                   : launch_prep<TIn, 128>(a, stream);
+}
+
+template <typename TIn>
+hipError_t launch_main_d(const BwdArgs& a, int D, hipStream_t stream) {
+  return D == 32   ? launch_main<TIn, 32>(a, stream)
+         : D == 64 ? launch_main<TIn, 64>(a, stream)
+                   : launch_main<TIn, 128>(a, stream);
+}
+
 hipError_t launch_bwd_prep_16(const BwdArgs& a, bool fp16, int D, hipStream_t stream) {
-  if (fp16) return D == 32 ? launch_prep<f16, 32>(a, stream) : launch_prep<f16, 64>(a, stream);
-  return D == 32 ? launch_prep<bf16, 32>(a, stream) : launch_prep<bf16, 64>(a, stream);
+  return fp16 ? launch_prep_d<f16>(a, D, stream) : launch_prep_d<bf16>(a, D, stream);
 }
 
 hipError_t launch_bwd_main_16(const BwdArgs& a, bool fp16, int D, hipStream_t stream) {
-  if (fp16) return D == 32 ? launch_main<f16, 32>(a, stream) : launch_main<f16, 64>(a, stream);
-  return D == 32 ? launch_main<bf16, 32>(a, stream) : launch_main<bf16, 64>(a, stream);
+  return fp16 ? launch_main_d<f16>(a, D, stream) : launch_main_d<bf16>(a, D, stream);
 }
 
 }  // namespace gpt_attn

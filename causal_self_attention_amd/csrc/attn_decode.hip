@@ -1,5 +1,5 @@
 // One query per (sequence, head) against a key/value cache, for gfx950:
-// bf16, fp16 or fp32 inputs, head dim D in {32, 64}.
+// bf16, fp16 or fp32 inputs, head dim D in {32, 64, 128}.
 //
 // Sampling feeds the sequence back one position at a time (generate(), page
 // "nanoGPT: a real GPT in two 300-line files", section 2 "How the code
@@ -250,7 +250,9 @@ hipError_t launch_decode(const DecArgs& a, hipStream_t stream) {
 
 template <typename T>
 hipError_t launch_decode_d(const DecArgs& a, int D, hipStream_t stream) {
-  return D == 32 ? launch_decode<T, 32>(a, stream) : launch_decode<T, 64>(a, stream);
+  return D == 32   ? launch_decode<T, 32>(a, stream)
+         : D == 64 ? launch_decode<T, 64>(a, stream)
+                   : launch_decode<T, 128>(a, stream);
 }
 
 }  // namespace

@@ -1,5 +1,5 @@
 // Causal attention forward, bf16 or fp16 inputs, fp32 accumulation, head dim
-// D in {32, 64}, for gfx950 (CDNA4).
+// D in {32, 64, 128}, for gfx950 (CDNA4).
 //
 // Computes O = softmax(Q K^T / sqrt(D) with the future masked) V and the
 // natural-log LSE of every row without storing the T x T matrix (the fused
@@ -70,21 +70,16 @@ struct KVRegs {
 template <int D>
 struct KVOffsets {
   static constexpr int kN = kBN * D / 8 / kThreads;
-  uint32_t k[kN], v[kN];
+  static constexpr int kRowsPerPass = kThreads / (D / 8);  // rows between chunks p and p + 1
+  uint32_t k, v;  // chunk 0; chunk p lies p * kRowsPerPass rows further
 };
 
 template <typename TIn, int D>
 __device__ __forceinline__ KVOffsets<D> fwd_tile_offsets(int ldk, int ldv, int tid) {
   constexpr int kC = D / 8;
-  KVOffsets<D> o;
-#pragma unroll
-  for (int p = 0; p < KVOffsets<D>::kN; ++p) {
-    const int c = tid + kThreads * p;
-    const uint32_t col = (uint32_t)(c % kC) * 8u;
-    o.k[p] = ((uint32_t)(c / kC) * (uint32_t)ldk + col) * (uint32_t)sizeof(TIn);
-    o.v[p] = ((uint32_t)(c / kC) * (uint32_t)ldv + col) * (uint32_t)sizeof(TIn);
-  }
-  return o;
+  const uint32_t row = (uint32_t)(tid / kC), col = (uint32_t)(tid % kC) * 8u;
+  return {(row * (uint32_t)ldk + col) * (uint32_t)sizeof(TIn),
+          (row * (uint32_t)ldv + col) * (uint32_t)sizeof(TIn)};
 }
 
 template <typename TIn, int D>
@@ -98,8 +93,9 @@ __device__ __forceinline__ void fwd_load_tile(const TIn* kh, int ldk, const TIn*
   uint32_t ok[KVOffsets<D>::kN], ov[KVOffsets<D>::kN];
 #pragma unroll
   for (int p = 0; p < KVOffsets<D>::kN; ++p) {
-    ok[p] = off.k[p];
-    ov[p] = off.v[p];
+    constexpr uint32_t kStep = KVOffsets<D>::kRowsPerPass * (uint32_t)sizeof(TIn);
+    ok[p] = off.k + (uint32_t)p * kStep * (uint32_t)ldk;
+    ov[p] = off.v + (uint32_t)p * kStep * (uint32_t)ldv;
   }
   if (k0 + kBN > T) {
     // The sequence's last tile: rows past T - 1 read row T - 1 instead.
@@ -477,8 +473,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
     const int k0 = kt * kBN;
     const bool has_next = kt + 1 < n_kt;
     if (has_next) fwd_load_tile<TIn, D>(kh, ldk, vh, ldv, k0 + kBN, T, tid, kvoff, nxt);
-    fwd_tile<TIn, D, DROP>(Kbuf(buf), Vbuf(buf), qf, k0, my_q, T, l32, hf, lane, scale_log2,
-                           a.drop, tm.head, st);
+    if constexpr (D >= 128) {
+      // Half by half: one half's scores at a time keep the register count
+      // within two waves per SIMD at this head size.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        fwd_half<TIn, D, kFull, DROP>(Kbuf(buf), Vbuf(buf), qf, kb, k0, my_q, T, l32, hf, lane,
+                                      scale_log2, a.drop, tm.head, st);
+    } else {
+      fwd_tile<TIn, D, DROP>(Kbuf(buf), Vbuf(buf), qf, k0, my_q, T, l32, hf, lane, scale_log2,
+                             a.drop, tm.head, st);
+    }
     extra_barrier();
     if (has_next) {
       fwd_stage<TIn, D>(Kbuf(buf ^ 1), Vbuf(buf ^ 1), nxt, k0 + kBN, T, tid, vs.vexp);
@@ -600,8 +605,13 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_16(const FwdArgs& a, bool fp16, int D, hipStream_t stream) {
-  if (fp16) return D == 32 ? launch_fwd<f16, 32>(a, stream) : launch_fwd<f16, 64>(a, stream);
-  return D == 32 ? launch_fwd<bf16, 32>(a, stream) : launch_fwd<bf16, 64>(a, stream);
+  if (fp16)
+    return D == 32 ? launch_fwd<f16, 32>(a, stream)
+           : D == 64 ? launch_fwd<f16, 64>(a, stream)
+                     : launch_fwd<f16, 128>(a, stream);
+  return D == 32 ? launch_fwd<bf16, 32>(a, stream)
+         : D == 64 ? launch_fwd<bf16, 64>(a, stream)
+                   : launch_fwd<bf16, 128>(a, stream);
 }
 
 }  // namespace gpt_attn

@@ -78,7 +78,7 @@ struct BwdArgs {
   const void* dout;
   const float* lse;
   float* delta;
-  float* stats;  // per (head, kStatRows-row chunk): max|Q|, max|dO|, max|delta|, 0
+  float* stats;  // per (head, kStatRows-row chunk): see bwd_workspace_bytes
   float* dq;
   float* dk;
   float* dv;
@@ -88,17 +88,21 @@ struct BwdArgs {
 };
 
 // Backward workspace: delta [n_heads * T] fp32, then, from the next 16-byte
-// boundary, four floats per (head, chunk of kStatRows rows): the largest
-// |Q|, |dO| and |delta| of the chunk's rows and a zero. The 16-bit main
-// kernel sets its block exponents from them.
+// boundary, eight floats per (head, chunk of kStatRows rows): the largest
+// |Q|, |dO| and |delta| of the chunk's rows and a zero (written by the
+// preprocess), then the largest |K| and |V| of the chunk's rows and two
+// zeros (written by the D = 128 dK/dV kernel, whose workgroup covers one
+// chunk of keys, for the dQ kernel after it). The 16-bit backward kernels
+// set their block exponents from them.
 constexpr int kStatRows = 128;
+constexpr int kStatFloats = 8;
 
 inline long long bwd_stat_chunks(int T) { return ((long long)T + kStatRows - 1) / kStatRows; }
 
 inline long long bwd_stats_offset_bytes(long long rows) { return (rows * 4 + 15) / 16 * 16; }
 
 inline long long bwd_workspace_bytes(long long n_heads, int T) {
-  return bwd_stats_offset_bytes(n_heads * T) + 16 * n_heads * bwd_stat_chunks(T);
+  return bwd_stats_offset_bytes(n_heads * T) + 4 * kStatFloats * n_heads * bwd_stat_chunks(T);
 }
 
 // One query per head against a key/value cache. q and o are [B, H, D]
@@ -117,9 +121,9 @@ struct DecArgs {
   int n_heads, H, L;
 };
 
-// One chunk's partial: D (<= 64) unnormalized outputs, then max and sum.
-constexpr int kDecPart = 68;
-constexpr int kDecMax = 64, kDecSum = 65;
+// One chunk's partial: D (<= 128) unnormalized outputs, then max and sum.
+constexpr int kDecPart = 132;
+constexpr int kDecMax = 128, kDecSum = 129;
 
 // Cache rows per split workgroup: about 2048 workgroups in total, a multiple
 // of 128 keys (one step of the split kernel), between 128 and 1024.
@@ -129,7 +133,7 @@ __host__ __device__ inline int decode_chunk(int n_heads, int L) {
   return (int)(c < 128 ? 128 : (c > 1024 ? 1024 : c));
 }
 
-// dtype_code: 0 fp32, 1 bf16, 2 fp16 (the C ABI's codes); D is 32 or 64.
+// dtype_code: 0 fp32, 1 bf16, 2 fp16 (the C ABI's codes); D is 32, 64 or 128.
 hipError_t launch_decode(const DecArgs& a, int dtype_code, int D, hipStream_t stream);
 
 // Keep mask [n_heads, T, T] (uint8, 1 = kept; 0 above the diagonal).
@@ -137,7 +141,7 @@ hipError_t launch_dropout_mask(const Dropout& d, int n_heads, int T, uint8_t* ma
                                hipStream_t stream);
 
 // 16-bit inputs (bf16, or fp16 when fp16 is set) on the matrix cores, and
-// fp32 inputs on the vector ALUs; D is 32 or 64.
+// fp32 inputs on the vector ALUs; D is 32, 64 or 128.
 hipError_t launch_fwd_16(const FwdArgs& a, bool fp16, int D, hipStream_t stream);
 hipError_t launch_bwd_prep_16(const BwdArgs& a, bool fp16, int D, hipStream_t stream);
 hipError_t launch_bwd_main_16(const BwdArgs& a, bool fp16, int D, hipStream_t stream);

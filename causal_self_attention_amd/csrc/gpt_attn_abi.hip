@@ -32,7 +32,7 @@ int check_shape(int dtype, int B, int H, int T, int D, Shape* s) {
   if (dtype != GPT_ATTN_F32 && dtype != GPT_ATTN_BF16 && dtype != GPT_ATTN_F16)
     return GPT_ATTN_E_INVAL;
   if (B < 0 || H < 0 || T < 0 || D <= 0) return GPT_ATTN_E_INVAL;
-  if (D != 32 && D != 64) return GPT_ATTN_E_UNSUPPORTED;
+  if (D != 32 && D != 64 && D != 128) return GPT_ATTN_E_UNSUPPORTED;
   const long long heads = (long long)B * (long long)H;
   const long long r = heads * (long long)T;
   if (r >= (1LL << 31)) return GPT_ATTN_E_INVAL;
@@ -255,7 +255,7 @@ const char* gpt_attn_status_string(int status) {
       return "invalid argument (null pointer, negative or overflowing size, bad dtype, or bad "
              "dropout probability)";
     case GPT_ATTN_E_UNSUPPORTED:
-      return "unsupported head dimension (kernels exist for D = 32 and D = 64)";
+      return "unsupported head dimension (kernels exist for D = 32, 64 and 128)";
     case GPT_ATTN_E_ALIGN:
       return "pointer not 16-byte aligned";
     case GPT_ATTN_E_WORKSPACE:

@@ -71,6 +71,10 @@ WORKLOADS: dict[str, Workload] = {
         # block 64 (head size 128 / 4), in fp32 and bf16.
         Workload("shakespeare_char_small_f32_b12_h4_t64_d32", "f32", 12, 4, 64, 32),
         Workload("shakespeare_char_small_bf16_b12_h4_t64_d32", "bf16", 12, 4, 64, 32),
+        # Head size 128 (not a model of the pages; the head size of larger
+        # models): the GPT-2 774M layer's width, 1280 channels, as 10 heads of
+        # 128 instead of 20 of 64.
+        Workload("gpt2_774m_d128_bf16_b8_h10_t1024", "bf16", 8, 10, 1024, 128),
     )
 }
 

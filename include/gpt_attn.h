@@ -32,11 +32,12 @@
  *   - stream is a hipStream_t (NULL = the default stream). Calls only enqueue
  *     work and return; results are visible after the caller synchronizes.
  *   - Sizes: B, H, T >= 0; a call with B*H*T == 0 does nothing and returns
- *     GPT_ATTN_OK (pointers are not inspected). D must be 32 or 64 (the head
- *     sizes of the pages' models: 768/12 = 64 for GPT-2, 128/4 = 32 for the
- *     small Shakespeare-char run on a laptop, page "nanoGPT: a real GPT in
- *     two 300-line files", section 3 "Run it, tested"). B*H*T must be below
- *     2^31 and B*H*T*D below 2^40.
+ *     GPT_ATTN_OK (pointers are not inspected). D must be 32, 64 or 128
+ *     (64 and 32 are the head sizes of the pages' models: 768/12 = 64 for
+ *     GPT-2, 128/4 = 32 for the small Shakespeare-char run on a laptop, page
+ *     "nanoGPT: a real GPT in two 300-line files", section 3 "Run it,
+ *     tested"; 128 is the common head size of larger models). B*H*T must be
+ *     below 2^31 and B*H*T*D below 2^40.
  *   - Errors: argument errors are returned before any device work is
  *     enqueued and leave every buffer untouched. GPT_ATTN_E_HIP means the
  *     HIP runtime rejected a launch (hipGetLastError); a fault inside a
@@ -54,14 +55,14 @@
 extern "C" {
 #endif
 
-#define GPT_ATTN_ABI_VERSION 6
+#define GPT_ATTN_ABI_VERSION 7
 
 /* Status codes returned by every int-returning entry point. */
 enum gpt_attn_status {
   GPT_ATTN_OK = 0,
   GPT_ATTN_E_INVAL = 1,       /* null pointer, negative or overflowing size, bad dtype code,
                                  o_lo given with GPT_ATTN_F32, bad dropout probability */
-  GPT_ATTN_E_UNSUPPORTED = 2, /* a head dimension D with no kernel (D not 32 or 64) */
+  GPT_ATTN_E_UNSUPPORTED = 2, /* a head dimension D with no kernel (D not 32, 64 or 128) */
   GPT_ATTN_E_ALIGN = 3,       /* a pointer that is not 16-byte aligned */
   GPT_ATTN_E_WORKSPACE = 4,   /* workspace NULL or smaller than the *_workspace_bytes size */
   GPT_ATTN_E_HIP = 5,         /* the HIP runtime reported an error when launching */
@@ -172,9 +173,10 @@ int gpt_attn_fwd(int dtype, int B, int H, int T, int D, const void* q, const voi
 
 /*
  * Bytes of device workspace the backward needs for this shape, for every
- * dtype: the fp32 vector delta_i = sum_d dO_id O_id, [B,H,T], followed by 16
- * bytes per (head, 128-row chunk) of per-chunk maxima the main phase reads.
- * Returns 0 for an invalid or empty shape.
+ * dtype: the fp32 vector delta_i = sum_d dO_id O_id, [B,H,T], followed (from
+ * the next 16-byte boundary) by 32 bytes per (head, 128-row chunk) of
+ * per-chunk maxima the main phase reads. Returns 0 for an invalid or empty
+ * shape.
  */
 size_t gpt_attn_bwd_workspace_bytes(int B, int H, int T, int D);
 
@@ -200,7 +202,9 @@ size_t gpt_attn_bwd_workspace_bytes(int B, int H, int T, int D);
  * the rounding dropped, and remove that error.
  *
  * dk, dv are bitwise reproducible run to run. dq is accumulated with fp32
- * atomic adds for the 16-bit dtypes, so its low bits may vary between runs.
+ * atomic adds for the 16-bit dtypes at D = 32 and 64, so its low bits may
+ * vary between runs; at D = 128 (two kernels: dk and dv, then dq, each
+ * written once) and for fp32 it is reproducible too.
  */
 int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const void* k,
                  const void* v, const void* o, const void* dout, const float* lse, float* dq,
@@ -219,8 +223,9 @@ int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const voi
  *   not touched).
  * gpt_attn_bwd_main: everything else. Reads the workspace, which must hold
  *   the prep phase's result for the same q, o and dout (and, for the 16-bit
- *   dtypes, dq must still hold the prep phase's zeros). Writes dq, dk, dv.
- *   Arguments mean what they mean for gpt_attn_bwd.
+ *   dtypes at D = 32 and 64, dq must still hold the prep phase's zeros).
+ *   Writes dq, dk, dv (and, at D = 128, per-chunk maxima of |k| and |v| into
+ *   the workspace). Arguments mean what they mean for gpt_attn_bwd.
  */
 int gpt_attn_bwd_prep(int dtype, int B, int H, int T, int D, const void* q, const void* o,
                       const void* dout, float* dq, void* workspace, size_t workspace_bytes,

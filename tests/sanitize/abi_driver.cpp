@@ -49,7 +49,7 @@ int main() {
   CHECK(calls() == std::vector<std::string>{"fwd_f32"});
   // Bad arguments stop before any launch.
   CHECK(gpt_attn_fwd(3, 1, 1, 5, 64, P(), P(), P(), P(), F(), nullptr) == GPT_ATTN_E_INVAL);
-  CHECK(gpt_attn_fwd(GPT_ATTN_BF16, 1, 1, 5, 128, P(), P(), P(), P(), F(), nullptr) ==
+  CHECK(gpt_attn_fwd(GPT_ATTN_BF16, 1, 1, 5, 256, P(), P(), P(), P(), F(), nullptr) ==
         GPT_ATTN_E_UNSUPPORTED);
   CHECK(gpt_attn_fwd(GPT_ATTN_BF16, 1, 1, 5, 64, P(8), P(), P(), P(), F(), nullptr) ==
         GPT_ATTN_E_ALIGN);
@@ -64,7 +64,7 @@ int main() {
   const size_t ws_bytes = gpt_attn_bwd_workspace_bytes(B, H, T, 64);
   const size_t rows = (size_t)B * H * T;
   const size_t stats_off = (rows * 4 + 15) / 16 * 16;
-  CHECK(ws_bytes == stats_off + 16 * (size_t)B * H * ((T + 127) / 128));
+  CHECK(ws_bytes == stats_off + 32 * (size_t)B * H * ((T + 127) / 128));
   CHECK(gpt_attn_bwd(GPT_ATTN_BF16, B, H, T, 64, P(), P(), P(), P(), P(), F(), F(), F(), F(),
                      P(0x10000), ws_bytes, nullptr) == 0);
   CHECK((calls() == std::vector<std::string>{"prep_16", "main_16"}));

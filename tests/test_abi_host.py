@@ -91,7 +91,7 @@ def test_forward_validation(lib):
     assert fwd(lib, H=-1) == E_INVAL
     assert fwd(lib, T=-1) == E_INVAL
     assert fwd(lib, D=0) == E_INVAL
-    for D in (1, 16, 48, 63, 65, 96, 128):
+    for D in (1, 16, 48, 63, 65, 96, 127, 129, 256):
         assert fwd(lib, D=D) == E_UNSUP
     for name in ("q", "k", "v", "o", "lse"):
         assert fwd(lib, **{name: None}) == E_INVAL, name
@@ -117,14 +117,14 @@ def test_empty_calls_are_noops(lib):
 
 def test_backward_validation(lib):
     assert bwd(lib, dtype=-1) == E_INVAL
-    assert bwd(lib, D=128) == E_UNSUP
+    assert bwd(lib, D=256) == E_UNSUP
     for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
         assert bwd(lib, ptrs={name: None}) == E_INVAL, name
         assert bwd(lib, ptrs={name: P + 4}) == E_ALIGN, name
     assert bwd_lo(lib, dtype=F32) == E_INVAL
     assert bwd_lo(lib, o_lo=P + 2) == E_ALIGN
     need = lib.gpt_attn_bwd_workspace_bytes(1, 1, 8, 64)
-    assert need == 8 * 4 + 16  # delta, then one chunk's maxima at the next 16-byte boundary
+    assert need == 8 * 4 + 32  # delta, then one chunk's maxima at the next 16-byte boundary
     assert bwd_lo(lib, ws_bytes=need - 1) == E_WS
     assert bwd(lib, ws=None) == E_WS
     assert bwd(lib, ws_bytes=need - 1) == E_WS
@@ -132,12 +132,13 @@ def test_backward_validation(lib):
 
 
 def test_workspace_bytes(lib):
-    # delta (4 bytes per row), padded to 16 bytes, then 16 bytes per
-    # (head, 128-row chunk).
-    assert lib.gpt_attn_bwd_workspace_bytes(12, 12, 1024, 64) == 144 * 1024 * 4 + 144 * 8 * 16
-    assert lib.gpt_attn_bwd_workspace_bytes(1, 6, 256, 64) == 6 * 256 * 4 + 6 * 2 * 16
-    assert lib.gpt_attn_bwd_workspace_bytes(1, 1, 8, 128) == 0
-    assert lib.gpt_attn_bwd_workspace_bytes(1, 3, 129, 32) == 1552 + 3 * 2 * 16
+    # delta (4 bytes per row), padded to 16 bytes, then 32 bytes per
+    # (head, 128-row chunk); the same for every head dimension.
+    assert lib.gpt_attn_bwd_workspace_bytes(12, 12, 1024, 64) == 144 * 1024 * 4 + 144 * 8 * 32
+    assert lib.gpt_attn_bwd_workspace_bytes(1, 6, 256, 64) == 6 * 256 * 4 + 6 * 2 * 32
+    assert lib.gpt_attn_bwd_workspace_bytes(1, 6, 256, 128) == 6 * 256 * 4 + 6 * 2 * 32
+    assert lib.gpt_attn_bwd_workspace_bytes(1, 1, 8, 256) == 0
+    assert lib.gpt_attn_bwd_workspace_bytes(1, 3, 129, 32) == 1552 + 3 * 2 * 32
     assert lib.gpt_attn_bwd_workspace_bytes(-1, 1, 8, 64) == 0
     assert lib.gpt_attn_bwd_workspace_bytes(1, 1, 0, 64) == 0
 
@@ -223,7 +224,7 @@ def test_strided_backward_accepts_the_fused_layout(lib):
 
 def test_plain_calls_equal_strided_calls_with_null_layouts(lib):
     # Same validation outcome either way.
-    assert fwd_s(lib, D=128) == fwd(lib, D=128) == E_UNSUP
+    assert fwd_s(lib, D=256) == fwd(lib, D=256) == E_UNSUP
     assert bwd_s(lib) == E_WS
     assert lib.gpt_attn_bwd_prep_strided(BF16, 1, 1, 8, 64, P, None, P, None, None, None, P, None,
                                          P, ctypes.byref(L(0, 0, 32)), P, 1 << 20,
@@ -267,7 +268,7 @@ def test_dropout_descriptor_validation(lib):
     for p in (0.0, 0.1, 0.2, 0.99999):
         assert bwd_s(lib, drop=DROP(p, 2**64 - 1, 2**32 - 1)) == E_WS, p
     # Shape errors still come first.
-    assert fwd_s(lib, D=128, drop=DROP(2.0, 0, 0)) == E_UNSUP
+    assert fwd_s(lib, D=256, drop=DROP(2.0, 0, 0)) == E_UNSUP
 
 
 def test_dropout_mask_entry_validation(lib):
@@ -292,12 +293,13 @@ def dec(lib, dtype=BF16, B=2, H=3, L=100, D=64, q=P, k=P, v=P, lengths=None, o=P
 
 def test_decode_validation(lib):
     need = lib.gpt_attn_decode_workspace_bytes(BF16, 2, 3, 100, 64)
-    assert need == 2 * 3 * 1 * 68 * 4       # one 128-key chunk per head at most
-    assert lib.gpt_attn_decode_workspace_bytes(BF16, 64, 12, 1024, 64) == 768 * 8 * 68 * 4
+    assert need == 2 * 3 * 1 * 132 * 4      # one 128-key chunk per head at most
+    assert lib.gpt_attn_decode_workspace_bytes(BF16, 64, 12, 1024, 64) == 768 * 8 * 132 * 4
     assert lib.gpt_attn_decode_workspace_bytes(BF16, 2, 3, 0, 64) == 0
-    assert lib.gpt_attn_decode_workspace_bytes(BF16, 2, 3, 100, 128) == 0
+    assert lib.gpt_attn_decode_workspace_bytes(BF16, 2, 3, 100, 128) == need
+    assert lib.gpt_attn_decode_workspace_bytes(BF16, 2, 3, 100, 256) == 0
     assert lib.gpt_attn_decode_workspace_bytes(F16, 2, 3, 100, 32) == need
-    assert dec(lib, D=128) == E_UNSUP
+    assert dec(lib, D=256) == E_UNSUP
     assert dec(lib, dtype=5) == E_INVAL
     assert dec(lib, L=-1) == E_INVAL
     for name in ("q", "k", "v", "o", "lse"):
@@ -334,7 +336,7 @@ def test_sixteen_bit_dtypes_and_head_sizes_share_the_rules(lib):
 def test_noalloc_validation_before_any_device_work(lib):
     def call(dtype=BF16, B=1, H=1, T=8, D=64, q=P, dq=P):
         return lib.gpt_attn_bwd_noalloc(dtype, B, H, T, D, q, P, P, P, P, P, dq, P, P, None)
-    assert call(D=128) == E_UNSUP
+    assert call(D=256) == E_UNSUP
     assert call(q=None) == E_INVAL
     assert call(dq=P + 4) == E_ALIGN
     # 64 * 64 * 1024 rows need 16.8 MB of workspace, beyond the 8 MiB scratch.

@@ -50,7 +50,8 @@ def _run(inp, ragged_on_gpu=True):
 
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f32", 64), ("f16", 64), ("bf16", 32),
-                                     ("f32", 32), ("f16", 32)])
+                                     ("f32", 32), ("f16", 32), ("bf16", 128), ("f32", 128),
+                                     ("f16", 128)])
 @pytest.mark.parametrize("ragged", [False, True])
 @pytest.mark.parametrize("B,H,L", [(1, 1, 1), (1, 2, 7), (2, 3, 129), (1, 1, 1000), (3, 2, 257),
                                    (5, 1, 128)])

@@ -62,7 +62,8 @@ def _run(lib, inp, dropout, o_lo):
 CASES = [("bf16", 64, 1000, None, False), ("bf16", 64, 333, (0.2, 11, 3), True),
          ("f16", 64, 515, None, True), ("bf16", 32, 300, None, False),
          ("f16", 32, 129, (0.1, 5, 0), False), ("f32", 64, 300, None, False),
-         ("f32", 32, 77, (0.3, 9, 1), False), ("bf16", 64, 1000, "growing_v", False)]
+         ("f32", 32, 77, (0.3, 9, 1), False), ("bf16", 64, 1000, "growing_v", False),
+         ("bf16", 128, 700, None, True), ("f16", 128, 257, (0.2, 3, 4), False)]
 
 
 @pytest.mark.parametrize("dtype,D,T,dropout,o_lo", CASES)

@@ -193,7 +193,7 @@ def test_outputs_stay_in_bounds(dtype):
 
 def test_error_statuses_through_binding():
     dev = torch.device("cuda:0")
-    q = torch.zeros(1, 1, 8, 128, dtype=torch.bfloat16, device=dev)
+    q = torch.zeros(1, 1, 8, 256, dtype=torch.bfloat16, device=dev)
     with pytest.raises(gattn.GptAttnError) as ei:
         gattn.attention_forward(q, q, q)
     assert ei.value.status == 2  # unsupported head dim
