@@ -98,6 +98,7 @@ def col(row, *names):
 
 
 KERNELS = ("attn_fwd_kernel", "attn_bwd_prep_kernel", "attn_bwd_main_kernel",
+           "attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel",
            "attn_decode_split_kernel", "attn_decode_merge_kernel", "dropout_mask_kernel",
            "attn_fwd_f32_kernel", "attn_bwd_prep_f32_kernel", "attn_bwd_dkdv_f32_kernel",
            "attn_bwd_dq_f32_kernel")
@@ -227,12 +228,15 @@ def main():
     fwd_flop, bwd_flop = bench.flops(w)
     E = w.B * w.H * w.T * w.D
     R = w.B * w.H * w.T
-    stats = 16 * w.B * w.H * ((w.T + 127) // 128)  # per-chunk maxima in the workspace
+    stats = 32 * w.B * w.H * ((w.T + 127) // 128)  # per-chunk maxima in the workspace
+    zero_dq = 4 * E if w.D <= 64 else 0  # the main phase accumulates dQ at D <= 64 only
     algo = {  # compulsory bytes per launch of the plain calls, 16-bit inputs, fp32 gradients
-        "attn_fwd_kernel": 3 * 2 * E + 2 * E + 4 * R,                # q,k,v in; o, lse out
-        "attn_bwd_prep_kernel": 3 * 2 * E + 4 * R + 4 * E + stats,   # q,o,dout in; delta, dq=0
-        "attn_bwd_main_kernel": 4 * 2 * E + 8 * R + 3 * 4 * E + stats,  # q,k,v,dout,lse,delta,
-    }                                                                # maxima in; dq,dk,dv out
+        "attn_fwd_kernel": 3 * 2 * E + 2 * E + 4 * R,                    # q,k,v in; o, lse out
+        "attn_bwd_prep_kernel": 3 * 2 * E + 4 * R + zero_dq + stats,     # q,o,dout in; delta,
+        "attn_bwd_main_kernel": 4 * 2 * E + 8 * R + 3 * 4 * E + stats,   # (dq=0), maxima out;
+        "attn_bwd_dkdv_kernel": 4 * 2 * E + 8 * R + 2 * 4 * E + stats,   # q,k,v,dout,lse,delta,
+        "attn_bwd_dq_kernel": 4 * 2 * E + 8 * R + 4 * E + stats,         # maxima in; dq,dk,dv
+    }                                                                    # (their share) out
     lines = [f"# HBM traffic per dispatch: {args.workload}", "",
              f"Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one rocprofv3 --pmc run "
              f"each), scaled by what the same counters read for a plain {CALIB_MIB} MiB "

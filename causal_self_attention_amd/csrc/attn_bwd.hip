@@ -13,7 +13,8 @@
 //   dK_j    = s sum_i dS_ij Q_i,   dQ_i = s sum_j dS_ij K_j
 //
 // Kernel 1 (prep) forms delta from the stored O (plus its low part o_lo
-// when the forward kept it, which restores fp32 accuracy) and zeroes dQ.
+// when the forward kept it, which restores fp32 accuracy) and, at D = 32 and
+// 64, zeroes dQ.
 // Kernel 2 (main): a workgroup of 8 waves owns 256 consecutive keys of one
 // head (32 per wave), stages their K in LDS, and keeps their V fragments and
 // dK, dV accumulators in registers. It walks the 64-query tiles from its
@@ -124,11 +125,13 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const BwdArgs a, int
     fold_absmax(y[i], mdo);
     mdel = fmaxf(mdel, fabsf(acc));
     if (t < T) {
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      f32x4* dst = reinterpret_cast<f32x4*>(a.dq + head_base(a.ldq, head, a.H) + t * a.ldq.t +
-                                            part * 8);
-      dst[0] = z;
-      dst[1] = z;
+      if (a.dq) {  // null when the main phase writes dQ without atomics
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4* dst = reinterpret_cast<f32x4*>(a.dq + head_base(a.ldq, head, a.H) + t * a.ldq.t +
+                                              part * 8);
+        dst[0] = z;
+        dst[1] = z;
+      }
       if (part == 0) a.delta[(size_t)head * T + t] = acc;
     }
   }
@@ -680,29 +683,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_main_kernel(const BwdArg
 }
 
 // ---------------------------------------------------------------------------
-// Head dimension 128. A wave that owns 32 keys would hold 128 registers of dK
-// and dV accumulators and 64 of K and V operands, more than two waves per
-// SIMD can hold next to the main kernel's dQ work. So the backward runs as
-// two kernels after the preprocess: attn_bwd_dkdv_kernel (the main kernel's
-// step without dQ, one wave per SIMD) and attn_bwd_dq_kernel (dQ = dS K with
-// S and dP recomputed, one workgroup per 128 queries, like the forward), and
-// dQ is written once instead of accumulated with atomics. The products and
-// their block exponents are those of the main kernel.
+// The split backward: attn_bwd_dkdv_kernel (the main kernel's step without
+// dQ, 128 keys per workgroup) and attn_bwd_dq_kernel (dQ = dS K with S and dP
+// recomputed, one workgroup per 128 queries, like the forward); dQ is written
+// once instead of accumulated with atomics. The products and their block
+// exponents are those of the main kernel. It serves head dimension 128,
+// where a wave that owns 32 keys would hold 128 registers of dK and dV
+// accumulators and 64 of K and V operands, more than two waves per SIMD can
+// hold next to the main kernel's dQ work. (At D = 32 and 64 the main kernel
+// is faster at every sequence length measured, 64 to 2048: the split pair
+// computes S and dP twice.)
 
-constexpr int kW128 = 4;               // waves per workgroup in both kernels
-constexpr int kT128 = 64 * kW128;      // threads
-constexpr int kBK128 = 32 * kW128;     // keys per dK/dV workgroup (one statistics chunk)
-constexpr int kBM128 = 32 * kW128;     // queries per dQ workgroup (one statistics chunk)
-static_assert(kBK128 == kStatRows && kBM128 == kStatRows, "one chunk per workgroup");
-static_assert(kT128 == kLoaders, "every thread of the dK/dV kernel loads query tiles");
+constexpr int kSplitWaves = 4;                   // waves per workgroup in both kernels
+constexpr int kSplitThreads = 64 * kSplitWaves;  // threads
+constexpr int kSplitKeys = 32 * kSplitWaves;     // keys per dK/dV workgroup (one statistics chunk)
+constexpr int kSplitQueries = 32 * kSplitWaves;  // queries per dQ workgroup (one statistics chunk)
+static_assert(kSplitKeys == kStatRows && kSplitQueries == kStatRows, "one chunk per workgroup");
+static_assert(kSplitThreads == kLoaders, "every thread of the dK/dV kernel loads query tiles");
 
 // dK and dV for one workgroup of 128 keys: waves 0..3 own 32 keys each, as
 // the main kernel's waves do; all 256 threads load the next query tile a step
 // ahead. Also records the largest |K| and |V| of its keys (one statistics
 // chunk) for the dQ kernel.
 template <typename TIn, int D, bool DROP>
-__global__ __launch_bounds__(kT128, 1) void attn_bwd_dkdv_kernel(const BwdArgs a, int n_ktiles,
-                                                                 float scale, float scale_log2) {
+__global__ __launch_bounds__(kSplitThreads, 1) void attn_bwd_dkdv_kernel(const BwdArgs a,
+                                                                        int n_ktiles, float scale,
+                                                                        float scale_log2) {
   typedef typename In16<TIn>::vec vec;
   constexpr int kRowQ = row_of<D>();
   constexpr int kDB = D / 32;
@@ -711,8 +717,8 @@ __global__ __launch_bounds__(kT128, 1) void attn_bwd_dkdv_kernel(const BwdArgs a
   __shared__ __attribute__((aligned(16))) float sL[2][kBQ];         // LSE * log2(e)
   __shared__ __attribute__((aligned(16))) float sD[2][kBQ];         // -delta
   // Dropout: each wave's 32 x 32 keep-mask tile [query][key].
-  __shared__ __attribute__((aligned(16))) f16 sM[DROP ? kW128 : 1][32 * kRowS];
-  __shared__ float sRed[kW128][2];
+  __shared__ __attribute__((aligned(16))) f16 sM[DROP ? kSplitWaves : 1][32 * kRowS];
+  __shared__ float sRed[kSplitWaves][2];
 
   const int T = a.T;
   const TileMap tm = map_tile_xcd(blockIdx.x, a.n_heads, n_ktiles, false);
@@ -731,7 +737,7 @@ __global__ __launch_bounds__(kT128, 1) void attn_bwd_dkdv_kernel(const BwdArgs a
   const float* lseh = a.lse + roff;
   const float* delh = a.delta + roff;
 
-  const int k0 = tm.tile * kBK128;
+  const int k0 = tm.tile * kSplitKeys;
   const int kw0 = k0 + wave * 32;
   const int my_key = kw0 + l32;
 
@@ -775,7 +781,7 @@ __global__ __launch_bounds__(kT128, 1) void attn_bwd_dkdv_kernel(const BwdArgs a
   }
   __syncthreads();
 #pragma unroll
-  for (int w = 0; w < kW128; ++w) {
+  for (int w = 0; w < kSplitWaves; ++w) {
     mk = fmaxf(mk, sRed[w][0]);
     mv = fmaxf(mv, sRed[w][1]);
   }
@@ -847,7 +853,8 @@ __global__ __launch_bounds__(kT128, 1) void attn_bwd_dkdv_kernel(const BwdArgs a
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const f32x4 nd = *reinterpret_cast<const f32x4*>(&cD[mb * 32 + 16 * c + 8 * hf + 4 * h]);
+            const f32x4 nd =
+                *reinterpret_cast<const f32x4*>(&cD[mb * 32 + 16 * c + 8 * hf + 4 * h]);
 #pragma unroll
             for (int t = 0; t < 4; ++t) dp[8 * c + 4 * h + t] = nd[t];
           }
@@ -901,7 +908,8 @@ __global__ __launch_bounds__(kT128, 1) void attn_bwd_dkdv_kernel(const BwdArgs a
   constexpr int kEp = D + 4;
   static_assert(sizeof(sQ) >= 2 * 32 * kEp * sizeof(float), "staging fits");
   static_assert(sizeof(sdO) >= 2 * 32 * kEp * sizeof(float), "staging fits");
-  float* stage = reinterpret_cast<float*>(wave < 2 ? &sQ[0][0] : &sdO[0][0]) + (wave & 1) * 32 * kEp;
+  float* stage =
+      reinterpret_cast<float*>(wave < 2 ? &sQ[0][0] : &sdO[0][0]) + (wave & 1) * 32 * kEp;
   store_rows<D>(stage, dvacc, zs, -edo, a.dv + head_base(a.ldv, tm.head, a.H), (int)a.ldv.t, kw0,
                 T, l32, hf, lane);
   store_rows<D>(stage, dkacc, scale, -(edo + ev + eq), a.dk + head_base(a.ldk, tm.head, a.H),
@@ -913,7 +921,7 @@ __global__ __launch_bounds__(kT128, 1) void attn_bwd_dkdv_kernel(const BwdArgs a
 // T - 1; rows past T are zeroed when staged).
 template <typename TIn, int D>
 struct KVTile {
-  static constexpr int kN = 64 * D / 8 / kT128;
+  static constexpr int kN = 64 * D / 8 / kSplitThreads;
   typename In16<TIn>::vec k[kN], v[kN];
 };
 
@@ -924,7 +932,7 @@ __device__ __forceinline__ void dq_load_kv(const TIn* kh, int ldk, const TIn* vh
   constexpr int kC = D / 8;
 #pragma unroll
   for (int p = 0; p < KVTile<TIn, D>::kN; ++p) {
-    const int c = tid + kT128 * p;
+    const int c = tid + kSplitThreads * p;
     const int row = min(k0 + c / kC, T - 1), col = (c % kC) * 8;
     r.k[p] = *reinterpret_cast<const vec*>(kh + row * ldk + col);
     r.v[p] = *reinterpret_cast<const vec*>(vh + row * ldv + col);
@@ -937,11 +945,13 @@ __device__ __forceinline__ void dq_store_kv(f16* Ks, f16* Vs, const KVTile<TIn, 
   constexpr int kC = D / 8, kRow = row_of<D>();
 #pragma unroll
   for (int p = 0; p < KVTile<TIn, D>::kN; ++p) {
-    const int c = tid + kT128 * p;
+    const int c = tid + kSplitThreads * p;
     const int row = c / kC, col = (c % kC) * 8;
     const bool ok = k0 + row < T;
-    *reinterpret_cast<f16x8*>(&Ks[row * kRow + col]) = ok ? cvt_f16_scaled(r.k[p], ek) : zero_f16x8();
-    *reinterpret_cast<f16x8*>(&Vs[row * kRow + col]) = ok ? cvt_f16_scaled(r.v[p], ev) : zero_f16x8();
+    *reinterpret_cast<f16x8*>(&Ks[row * kRow + col]) =
+        ok ? cvt_f16_scaled(r.k[p], ek) : zero_f16x8();
+    *reinterpret_cast<f16x8*>(&Vs[row * kRow + col]) =
+        ok ? cvt_f16_scaled(r.v[p], ev) : zero_f16x8();
   }
 }
 
@@ -976,8 +986,8 @@ __device__ __forceinline__ void dq_half(const f16* Ks, const f16* Vs, const f16x
   for (int c = 0; c < 2; ++c) {
     uint32_t m[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
     if (DROP)
-      keep_mask8(drop, (uint32_t)head, (uint32_t)my_q, (uint32_t)((k0 + 32 * kb + 16 * c) >> 3) + hf,
-                 m);
+      keep_mask8(drop, (uint32_t)head, (uint32_t)my_q,
+                 (uint32_t)((k0 + 32 * kb + 16 * c) >> 3) + hf, m);
     float ds[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -1008,15 +1018,16 @@ __device__ __forceinline__ void dq_half(const f16* Ks, const f16* Vs, const f16x
 // statistics, K and V from the chunks of every key visited (written by the
 // dK/dV kernel), dO's from the dS bound.
 template <typename TIn, int D, bool DROP>
-__global__ __launch_bounds__(kT128, 1) void attn_bwd_dq_kernel(const BwdArgs a, int n_qtiles,
-                                                               float scale, float scale_log2) {
+__global__ __launch_bounds__(kSplitThreads, 1) void attn_bwd_dq_kernel(const BwdArgs a,
+                                                                      int n_qtiles, float scale,
+                                                                      float scale_log2) {
   typedef typename In16<TIn>::vec vec;
   constexpr int kRow = row_of<D>();
   constexpr int kBN = 64;
   // Two K/V buffers, fp16 [key][d]. In the prologue the Q rows (buffer 0)
   // and dO rows (buffer 1), 128 x D each, pass through them.
   __shared__ __attribute__((aligned(16))) f16 lds[2][2 * kBN * kRow];
-  static_assert(kBM128 * kRow <= 2 * kBN * kRow, "Q / dO rows fit one buffer");
+  static_assert(kSplitQueries * kRow <= 2 * kBN * kRow, "Q / dO rows fit one buffer");
 
   const int T = a.T;
   const TileMap tm = map_tile_xcd(blockIdx.x, a.n_heads, n_qtiles, true);
@@ -1033,18 +1044,18 @@ __global__ __launch_bounds__(kT128, 1) void attn_bwd_dq_kernel(const BwdArgs a, 
   const TIn* __restrict__ doh = static_cast<const TIn*>(a.dout) + head_base(a.ldo, tm.head, a.H);
   const int ldq = (int)a.lq.t, ldk = (int)a.lk.t, ldv = (int)a.lv.t, lddo = (int)a.ldo.t;
 
-  const int q0 = tm.tile * kBM128;
+  const int q0 = tm.tile * kSplitQueries;
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + l32;
 
   // Issue the first K/V tile and this workgroup's Q and dO rows.
   KVTile<TIn, D> nxt;
   dq_load_kv<TIn, D>(kh, ldk, vh, ldv, 0, T, tid, nxt);
-  constexpr int kC = D / 8, kNQ = kBM128 * D / 8 / kT128;
+  constexpr int kC = D / 8, kNQ = kSplitQueries * D / 8 / kSplitThreads;
   vec xq[kNQ], xd[kNQ];
 #pragma unroll
   for (int p = 0; p < kNQ; ++p) {
-    const int c = tid + kT128 * p;
+    const int c = tid + kSplitThreads * p;
     const int row = min(q0 + c / kC, T - 1);
     xq[p] = *reinterpret_cast<const vec*>(qh + row * ldq + (c % kC) * 8);
     xd[p] = *reinterpret_cast<const vec*>(doh + row * lddo + (c % kC) * 8);
@@ -1079,11 +1090,13 @@ __global__ __launch_bounds__(kT128, 1) void attn_bwd_dq_kernel(const BwdArgs a, 
   f16* dOs = lds[1];
 #pragma unroll
   for (int p = 0; p < kNQ; ++p) {
-    const int c = tid + kT128 * p;
+    const int c = tid + kSplitThreads * p;
     const int row = c / kC, col = (c % kC) * 8;
     const bool ok = q0 + row < T;
-    *reinterpret_cast<f16x8*>(&Qs[row * kRow + col]) = ok ? cvt_f16_scaled(xq[p], eq) : zero_f16x8();
-    *reinterpret_cast<f16x8*>(&dOs[row * kRow + col]) = ok ? cvt_f16_scaled(xd[p], edo) : zero_f16x8();
+    *reinterpret_cast<f16x8*>(&Qs[row * kRow + col]) =
+        ok ? cvt_f16_scaled(xq[p], eq) : zero_f16x8();
+    *reinterpret_cast<f16x8*>(&dOs[row * kRow + col]) =
+        ok ? cvt_f16_scaled(xd[p], edo) : zero_f16x8();
   }
   __syncthreads();
   f16x8 qf[D / 16], dof[D / 16];
@@ -1105,7 +1118,7 @@ __global__ __launch_bounds__(kT128, 1) void attn_bwd_dq_kernel(const BwdArgs a, 
   dq_store_kv<TIn, D>(Kb(0), Vb(0), nxt, 0, T, tid, ek, ev);
   __syncthreads();
 
-  const int kv_end = min(T, q0 + kBM128);
+  const int kv_end = min(T, q0 + kSplitQueries);
   const int n_kt = (kv_end + kBN - 1) / kBN;
   int buf = 0;
   for (int kt = 0; kt < n_kt; ++kt, buf ^= 1) {
@@ -1133,14 +1146,16 @@ __global__ __launch_bounds__(kT128, 1) void attn_bwd_dq_kernel(const BwdArgs a, 
   // dQ = s dQ_acc 2^-(edo + ev + ek), whole rows through LDS (both K/V
   // buffers are free after the loop's last barrier).
   constexpr int kEp = D + 4;
-  static_assert(sizeof(lds) >= kW128 * 32 * kEp * sizeof(float), "staging fits");
+  static_assert(sizeof(lds) >= kSplitWaves * 32 * kEp * sizeof(float), "staging fits");
   float* stage = reinterpret_cast<float*>(&lds[0][0]) + wave * 32 * kEp;
   store_rows<D>(stage, acc, scale, -(edo + ev + ek), a.dq + head_base(a.ldq, tm.head, a.H),
                 (int)a.ldq.t, qw0, T, l32, hf, lane);
 }
 
 template <typename TIn, int D>
-hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_prep(const BwdArgs& a_in, hipStream_t stream) {
+  BwdArgs a = a_in;
+  if (!bwd_dq_atomic(D)) a.dq = nullptr;  // dQ is written, not accumulated
   const int n_chunks = (int)bwd_stat_chunks(a.T);
   const unsigned blocks = (unsigned)a.n_heads * (unsigned)n_chunks;
   hipLaunchKernelGGL((attn_bwd_prep_kernel<TIn, D>), dim3(blocks), dim3(256), 0, stream, a,
@@ -1149,26 +1164,31 @@ hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
 }
 
 template <typename TIn, int D>
+hipError_t launch_split(const BwdArgs& a, hipStream_t stream) {
+  const int n_tiles = (a.T + kStatRows - 1) / kStatRows;
+  const float scale = 1.f / __builtin_sqrtf((float)D);
+  const dim3 grid(tiled_grid(a.n_heads, n_tiles));
+  if (a.drop.thr != 0)
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<TIn, D, true>), grid, dim3(kSplitThreads), 0, stream,
+                       a, n_tiles, scale, scale * kLog2e);
+  else
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<TIn, D, false>), grid, dim3(kSplitThreads), 0,
+                       stream, a, n_tiles, scale, scale * kLog2e);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.drop.thr != 0)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<TIn, D, true>), grid, dim3(kSplitThreads), 0, stream,
+                       a, n_tiles, scale, scale * kLog2e);
+  else
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<TIn, D, false>), grid, dim3(kSplitThreads), 0, stream,
+                       a, n_tiles, scale, scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <typename TIn, int D>
 hipError_t launch_main(const BwdArgs& a, hipStream_t stream) {
-  if constexpr (D == 128) {
-    const int n_tiles = (a.T + kStatRows - 1) / kStatRows;
-    const float scale = 1.f / __builtin_sqrtf((float)D);
-    const dim3 grid(tiled_grid(a.n_heads, n_tiles));
-    if (a.drop.thr != 0)
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<TIn, D, true>), grid, dim3(kT128), 0, stream, a,
-                         n_tiles, scale, scale * kLog2e);
-    else
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<TIn, D, false>), grid, dim3(kT128), 0, stream, a,
-                         n_tiles, scale, scale * kLog2e);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (a.drop.thr != 0)
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<TIn, D, true>), grid, dim3(kT128), 0, stream, a,
-                         n_tiles, scale, scale * kLog2e);
-    else
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<TIn, D, false>), grid, dim3(kT128), 0, stream, a,
-                         n_tiles, scale, scale * kLog2e);
-    return hipGetLastError();
+  if constexpr (D >= 128) {
+    return launch_split<TIn, D>(a, stream);
   } else {
     const int n_ktiles = (a.T + kBK - 1) / kBK;
     const float scale = 1.f / __builtin_sqrtf((float)D);

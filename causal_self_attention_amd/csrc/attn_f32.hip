@@ -342,15 +342,21 @@ hipError_t main_f32(const BwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_f32(const FwdArgs& a, int D, hipStream_t stream) {
-  return D == 32 ? fwd_f32<32>(a, stream) : D == 64 ? fwd_f32<64>(a, stream) : fwd_f32<128>(a, stream);
+  return D == 32   ? fwd_f32<32>(a, stream)
+         : D == 64 ? fwd_f32<64>(a, stream)
+                   : fwd_f32<128>(a, stream);
 }
 
 hipError_t launch_bwd_prep_f32(const BwdArgs& a, int D, hipStream_t stream) {
-  return D == 32 ? prep_f32<32>(a, stream) : D == 64 ? prep_f32<64>(a, stream) : prep_f32<128>(a, stream);
+  return D == 32   ? prep_f32<32>(a, stream)
+         : D == 64 ? prep_f32<64>(a, stream)
+                   : prep_f32<128>(a, stream);
 }
 
 hipError_t launch_bwd_main_f32(const BwdArgs& a, int D, hipStream_t stream) {
-  return D == 32 ? main_f32<32>(a, stream) : D == 64 ? main_f32<64>(a, stream) : main_f32<128>(a, stream);
+  return D == 32   ? main_f32<32>(a, stream)
+         : D == 64 ? main_f32<64>(a, stream)
+                   : main_f32<128>(a, stream);
 }
 
 }  // namespace gpt_attn

@@ -435,7 +435,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdArgs a, 
   }
 
   __shared__ float s_vred[4];   // per wave: largest |V| of a tile
-  __shared__ __attribute__((aligned(16))) int s_vflag[2][4];  // per tile parity, wave: |V| too large
+  // Per tile parity and wave: the tile holds a |V| too large for V's exponent.
+  __shared__ __attribute__((aligned(16))) int s_vflag[2][4];
   if (kScaleV<TIn>) {
     const float m = wave_max(bf16_bits_to_float(tile_vmax_bits<TIn, D>(nxt)));
     if (lane == 0) s_vred[wave] = m;

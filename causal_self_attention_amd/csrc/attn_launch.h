@@ -97,6 +97,12 @@ struct BwdArgs {
 constexpr int kStatRows = 128;
 constexpr int kStatFloats = 8;
 
+// The 16-bit backward at D = 32 and 64 accumulates dQ with atomic adds into
+// the dQ the preprocess zero-filled (one main kernel, 256 keys per
+// workgroup); at D = 128 it runs the split dK/dV and dQ kernels, which write
+// dQ once, and the preprocess leaves dQ alone.
+__host__ __device__ inline bool bwd_dq_atomic(int D) { return D <= 64; }
+
 inline long long bwd_stat_chunks(int T) { return ((long long)T + kStatRows - 1) / kStatRows; }
 
 inline long long bwd_stats_offset_bytes(long long rows) { return (rows * 4 + 15) / 16 * 16; }

@@ -216,11 +216,11 @@ int gpt_attn_bwd(int dtype, int B, int H, int T, int D, const void* q, const voi
  * gpt_attn_bwd_prep(...) followed by gpt_attn_bwd_main(...) on one stream.
  *
  * gpt_attn_bwd_prep: the preprocess pass. Writes delta_i = sum_d dout_id O_id
- *   into the workspace; for the 16-bit dtypes it also zero-fills dq, which
- *   the main phase accumulates into, and records the largest |q|, |dout| and
- *   |delta| of every 128-row chunk of each head, from which the main phase
- *   sets its operand scales (q and dq may be NULL for GPT_ATTN_F32 and are
- *   not touched).
+ *   into the workspace; for the 16-bit dtypes it also records the largest
+ *   |q|, |dout| and |delta| of every 128-row chunk of each head, from which
+ *   the main phase sets its operand scales, and at D = 32 and 64 zero-fills
+ *   dq, which the main phase accumulates into (q and dq may be NULL for
+ *   GPT_ATTN_F32 and are not touched; dq is not touched at D = 128).
  * gpt_attn_bwd_main: everything else. Reads the workspace, which must hold
  *   the prep phase's result for the same q, o and dout (and, for the 16-bit
  *   dtypes at D = 32 and 64, dq must still hold the prep phase's zeros).
