@@ -9,14 +9,19 @@
 // works": q @ k^T / sqrt(head size), future at -inf, softmax, @ v; the
 // gradient autograd forms for it, section 1 "Summary").
 //
-// Forward: one thread per query row; K/V tiles of 64 rows are staged in LDS
-// and read by broadcast; the softmax is the online (running max / sum) form
-// over tiles, so no T x T matrix exists. Backward: delta = rowsum(dO * O)
-// first; then dK, dV with two threads per key (32 dims each) looping over
-// the query tiles at and after the key, and dQ with two threads per query
-// looping over the key tiles up to the query. Nothing is accumulated with
-// atomics, so every output is bitwise reproducible. Operands are addressed
-// through per-tensor element strides (D contiguous), like the bf16 path.
+// Layout of the work: 16 lanes per row (a query, or a key for dK/dV), each
+// holding D/16 consecutive dims of that row's vectors, so a wave carries four
+// rows; a dot product is the lanes' partial sums added across the 16 lanes
+// with four DPP steps, which leave the same sum in every lane. Keys (or
+// queries) are read straight from global memory: the four rows of a wave
+// read the same key at the same time, so each load is one coalesced 256-byte
+// row shared by the wave. Forward: a wave per four queries, online softmax
+// (running max and sum) over blocks of 8 keys. Backward: delta =
+// rowsum(dO * O) first; then dK, dV with a wave per four keys looping over
+// the queries at and after them, and dQ with a wave per four queries looping
+// over the keys up to them. Nothing is accumulated with atomics, so every
+// output is bitwise reproducible. Operands are addressed through per-tensor
+// element strides (D contiguous), like the bf16 path.
 // Attention dropout regenerates the same Philox keep mask as the bf16 path
 // (one block per query and 8 keys) wherever a (query, key) weight is used.
 #include "attn_common.h"
@@ -37,74 +42,157 @@ __device__ __forceinline__ float* fptr_w(void* base, const Layout& L, int hd, in
   return static_cast<float*>(base) + head_base(L, hd, H);
 }
 
+// Sum over the 16 lanes of a row of x (DPP: swap neighbours, swap pairs,
+// mirror within 8 lanes, mirror within 16). Every step adds two values that
+// partner lanes hold in opposite order, so all 16 lanes end with the same sum.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_get(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum16(float x) {
+  x += dpp_get<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_get<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_get<0x141>(x);  // row_half_mirror
+  x += dpp_get<0x140>(x);  // row_mirror
+  return x;
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// kE consecutive floats at p (8-byte aligned for kE = 2, 16-byte otherwise).
+template <int kE>
+__device__ __forceinline__ void load_part(const float* p, float (&x)[kE]) {
+  if constexpr (kE == 2) {
+    const f32x2 v = *reinterpret_cast<const f32x2*>(p);
+    x[0] = v[0];
+    x[1] = v[1];
+  } else {
+#pragma unroll
+    for (int c = 0; c < kE / 4; ++c) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p + 4 * c);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) x[4 * c + t] = v[t];
+    }
+  }
+}
+
+template <int kE>
+__device__ __forceinline__ float dot_part(const float (&x)[kE], const float (&y)[kE]) {
+  float d = 0.f;
+#pragma unroll
+  for (int e = 0; e < kE; ++e) d = fmaf(x[e], y[e], d);
+  return d;
+}
+
+// A workgroup of kW waves per four rows: every wave holds the same four rows
+// and takes every kW-th batch of the loop, and the waves' partial results
+// meet in LDS at the end (in a fixed order, so the outputs stay
+// reproducible). kU rows of the loop per batch; the next batch's loads are
+// issued before the current batch is used.
+constexpr int kW = 4, kU = 8;
+
+// One workgroup per four queries (16 lanes each, kE = D/16 dims per lane).
+// Each wave runs the online softmax over its share of the key batches; the
+// partial (max, sum, output) triples are merged with the log-sum-exp rule.
 template <int kD>
-__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const FwdArgs a, int n_tiles,
-                                                          float scale) {
-  __shared__ float Ks[64 * kD];
-  __shared__ float Vs[64 * kD];
+__global__ __launch_bounds__(64 * kW) void attn_fwd_f32_kernel(const FwdArgs a, int n_tiles,
+                                                               float scale) {
+  constexpr int kE = kD / 16;
+  __shared__ float s_part[kW][64][kE + 2];
   const int T = a.T;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane & 15;
   const int head = blockIdx.x / n_tiles;
-  const int q0 = (blockIdx.x % n_tiles) * 64;
-  const int i = q0 + tid;
+  const int q0 = (blockIdx.x % n_tiles) * 4;
+  const int i = q0 + (lane >> 4);
+  const int ie = min(i, T - 1);  // rows past T run as row T - 1 and store nothing
   const float* qh = fptr(a.q, a.lq, head, a.H);
-  const float* kh = fptr(a.k, a.lk, head, a.H);
-  const float* vh = fptr(a.v, a.lv, head, a.H);
-  const long long ldq = a.lq.t, ldk = a.lk.t, ldv = a.lv.t;
+  const float* kh = fptr(a.k, a.lk, head, a.H) + g * kE;
+  const float* vh = fptr(a.v, a.lv, head, a.H) + g * kE;
+  const int ldk = (int)a.lk.t, ldv = (int)a.lv.t;
   const bool drop = a.drop.thr != 0;
 
-  float qr[kD], acc[kD];
+  float qr[kE], acc[kE];
+  load_part<kE>(qh + ie * a.lq.t + g * kE, qr);
 #pragma unroll
-  for (int d = 0; d < kD; ++d) {
-    qr[d] = i < T ? qh[i * ldq + d] : 0.f;
-    acc[d] = 0.f;
-  }
+  for (int e = 0; e < kE; ++e) acc[e] = 0.f;
   float m = -INFINITY, l = 0.f;
-  const int kv_end = min(T, q0 + 64);
-  for (int k0 = 0; k0 < kv_end; k0 += 64) {
-    __syncthreads();
-    for (int e = tid; e < 64 * kD; e += 64) {
-      const int r = e / kD, d = e % kD;
-      const bool ok = k0 + r < T;
-      Ks[e] = ok ? kh[(k0 + r) * ldk + d] : 0.f;
-      Vs[e] = ok ? vh[(k0 + r) * ldv + d] : 0.f;
-    }
-    __syncthreads();
-    float sc[64];
-    float mx = -INFINITY;
+  const int kend = min(q0 + 3, T - 1) + 1;  // keys 0 .. the block's last query
+  float kb[2][kU][kE], vb[2][kU][kE];
+  auto load_block = [&](int j0, int b) {
 #pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      float dot = 0.f;
-#pragma unroll
-      for (int d = 0; d < kD; ++d) dot = fmaf(qr[d], Ks[j * kD + d], dot);
-      const int key = k0 + j;
-      sc[j] = (key <= i && key < T) ? dot * scale : -INFINITY;
-      mx = fmaxf(mx, sc[j]);
+    for (int t = 0; t < kU; ++t) {
+      const int j = min(j0 + t, T - 1);
+      load_part<kE>(kh + j * ldk, kb[b][t]);
+      load_part<kE>(vh + j * ldv, vb[b][t]);
     }
-    const float m_new = fmaxf(m, mx);
-    const float alpha = expf(m - m_new);
+  };
+  auto use_block = [&](int j0, int b) {
+    float sc[kU];
+    float mx = m;
+#pragma unroll
+    for (int t = 0; t < kU; ++t) {
+      const float d = sum16(dot_part<kE>(qr, kb[b][t]));
+      sc[t] = j0 + t <= ie ? d * scale : -INFINITY;
+      mx = fmaxf(mx, sc[t]);
+    }
+    if (mx == -INFINITY) return;  // nothing visible yet in this wave's share
+    const float alpha = expf(m - mx);
     l *= alpha;
 #pragma unroll
-    for (int d = 0; d < kD; ++d) acc[d] *= alpha;
+    for (int e = 0; e < kE; ++e) acc[e] *= alpha;
     uint32_t km[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+    if (drop) keep_mask8(a.drop, head, ie, (uint32_t)j0 >> 3, km);
 #pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      if (drop && (j & 7) == 0) keep_mask8(a.drop, head, i, (uint32_t)(k0 + j) >> 3, km);
-      const float p = expf(sc[j] - m_new);
+    for (int t = 0; t < kU; ++t) {
+      const float p = expf(sc[t] - mx);
       l += p;
-      const float pd = kept_bit(km, j & 7) ? p : 0.f;
+      const float pd = kept_bit(km, t) ? p : 0.f;
 #pragma unroll
-      for (int d = 0; d < kD; ++d) acc[d] = fmaf(pd, Vs[j * kD + d], acc[d]);
+      for (int e = 0; e < kE; ++e) acc[e] = fmaf(pd, vb[b][t][e], acc[e]);
     }
-    m = m_new;
+    m = mx;
+  };
+  // Wave w takes key batches w, w + kW, ...
+  // (Two register buffers with fixed indices: a loop-carried buffer index
+  // would put the arrays in scratch memory.)
+  const int step = kW * kU;
+  int j0 = w * kU;
+  if (j0 < kend) load_block(j0, 0);
+  for (; j0 < kend; j0 += 2 * step) {
+    if (j0 + step < kend) load_block(j0 + step, 1);
+    use_block(j0, 0);
+    if (j0 + step >= kend) break;
+    if (j0 + 2 * step < kend) load_block(j0 + 2 * step, 0);
+    use_block(j0 + step, 1);
   }
-  if (i < T) {
-    const float inv = (drop ? a.drop.scale : 1.f) / l;
-    float* orow = fptr_w(a.o, a.lo, head, a.H) + i * a.lo.t;
+  s_part[w][lane][0] = m;
+  s_part[w][lane][1] = l;
 #pragma unroll
-    for (int d = 0; d < kD; ++d) orow[d] = acc[d] * inv;
-    a.lse[(size_t)head * T + i] = m + logf(l);
+  for (int e = 0; e < kE; ++e) s_part[w][lane][2 + e] = acc[e];
+  __syncthreads();
+  if (w != 0 || i >= T) return;
+  // Wave 0 merges the partials in wave order. Wave 0's share holds key 0,
+  // which every row sees, so the merged max is finite.
+  float M = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < kW; ++v) M = fmaxf(M, s_part[v][lane][0]);
+  float L = 0.f, o[kE];
+#pragma unroll
+  for (int e = 0; e < kE; ++e) o[e] = 0.f;
+#pragma unroll
+  for (int v = 0; v < kW; ++v) {
+    const float mv = s_part[v][lane][0];
+    const float f = mv == -INFINITY ? 0.f : expf(mv - M);
+    L = fmaf(s_part[v][lane][1], f, L);
+#pragma unroll
+    for (int e = 0; e < kE; ++e) o[e] = fmaf(s_part[v][lane][2 + e], f, o[e]);
   }
+  const float inv = (drop ? a.drop.scale : 1.f) / L;
+  float* orow = fptr_w(a.o, a.lo, head, a.H) + i * a.lo.t + g * kE;
+#pragma unroll
+  for (int e = 0; e < kE; ++e) orow[e] = o[e] * inv;
+  if (g == 0) a.lse[(size_t)head * T + i] = M + logf(L);
 }
 
 // Eight threads per (head, row); row r of [B*H, T] is head r / T, position r % T.
@@ -127,154 +215,183 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_f32_kernel(const BwdArgs a,
   if (row < rows && part == 0) a.delta[row] = acc;
 }
 
-// dK, dV: thread pair (key j, half) holds D/2 dims of K_j, V_j, dK_j, dV_j.
+// dK, dV: one workgroup per four keys (16 lanes each, kE = D/16 dims of
+// K_j, V_j, dK_j, dV_j per lane); its waves share the queries at and after
+// the first key.
 template <int kD>
-__global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(const BwdArgs a, int n_tiles,
-                                                               float scale) {
-  constexpr int kH = kD / 2;
-  __shared__ float Qs[32 * kD];
-  __shared__ float dOs[32 * kD];
-  __shared__ float lses[32];
-  __shared__ float dels[32];
+__global__ __launch_bounds__(64 * kW) void attn_bwd_dkdv_f32_kernel(const BwdArgs a,
+                                                                    int n_tiles, float scale) {
+  constexpr int kE = kD / 16;
+  __shared__ float s_part[kW][64][2 * kE];
   const int T = a.T;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane & 15;
   const int head = blockIdx.x / n_tiles;
-  const int k0 = (blockIdx.x % n_tiles) * 32;
-  const int j = k0 + (tid >> 1);
-  const int half = tid & 1;
-  const float* qh = fptr(a.q, a.lq, head, a.H);
-  const float* kh = fptr(a.k, a.lk, head, a.H);
-  const float* vh = fptr(a.v, a.lv, head, a.H);
-  const float* doh = fptr(a.dout, a.ldo, head, a.H);
+  const int k0 = (blockIdx.x % n_tiles) * 4;
+  const int j = k0 + (lane >> 4);
+  const float* qh = fptr(a.q, a.lq, head, a.H) + g * kE;
+  const float* doh = fptr(a.dout, a.ldo, head, a.H) + g * kE;
+  const int ldq = (int)a.lq.t, lddo = (int)a.ldo.t;
   const size_t roff = (size_t)head * T;
   const bool drop = a.drop.thr != 0;
   const float zs = drop ? a.drop.scale : 1.f;
 
-  float kr[kH], vr[kH], dka[kH], dva[kH];
+  float kr[kE], vr[kE], dka[kE], dva[kE];
+  const int jr = min(j, T - 1);
+  load_part<kE>(fptr(a.k, a.lk, head, a.H) + jr * a.lk.t + g * kE, kr);
+  load_part<kE>(fptr(a.v, a.lv, head, a.H) + jr * a.lv.t + g * kE, vr);
 #pragma unroll
-  for (int d = 0; d < kH; ++d) {
-    kr[d] = j < T ? kh[j * a.lk.t + half * kH + d] : 0.f;
-    vr[d] = j < T ? vh[j * a.lv.t + half * kH + d] : 0.f;
-    dka[d] = 0.f;
-    dva[d] = 0.f;
+  for (int e = 0; e < kE; ++e) {
+    dka[e] = 0.f;
+    dva[e] = 0.f;
   }
-  for (int qs = k0; qs < T; qs += 32) {
-    __syncthreads();
-    for (int e = tid; e < 32 * kD; e += 64) {
-      const int r = e / kD, d = e % kD;
-      const bool ok = qs + r < T;
-      Qs[e] = ok ? qh[(qs + r) * a.lq.t + d] : 0.f;
-      dOs[e] = ok ? doh[(qs + r) * a.ldo.t + d] : 0.f;
-    }
-    if (tid < 32) {
-      const bool ok = qs + tid < T;
-      lses[tid] = ok ? a.lse[roff + qs + tid] : 0.f;
-      dels[tid] = ok ? a.delta[roff + qs + tid] : 0.f;
-    }
-    __syncthreads();
-    for (int ii = 0; ii < 32; ++ii) {
-      const int i = qs + ii;
-      float s = 0.f, dp = 0.f;
+  // The block's four keys lie in one 8-key group (k0 is a multiple of 4), so
+  // one keep-mask block per query serves every lane.
+  float qb[2][kU][kE], db[2][kU][kE], lb[2][kU], eb[2][kU];
+  auto load_batch = [&](int i0, int b) {
 #pragma unroll
-      for (int d = 0; d < kH; ++d) {
-        s = fmaf(Qs[ii * kD + half * kH + d], kr[d], s);
-        dp = fmaf(dOs[ii * kD + half * kH + d], vr[d], dp);
-      }
-      s += __shfl_xor(s, 1, 64);
-      dp += __shfl_xor(dp, 1, 64);
-      if (i < T && j < T && j <= i) {
+    for (int u = 0; u < kU; ++u) {
+      const int i = min(i0 + u, T - 1);
+      load_part<kE>(qh + i * ldq, qb[b][u]);
+      load_part<kE>(doh + i * lddo, db[b][u]);
+      lb[b][u] = a.lse[roff + i];
+      eb[b][u] = a.delta[roff + i];
+    }
+  };
+  auto use_batch = [&](int i0, int b) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = i0 + u;
+      const float s = sum16(dot_part<kE>(qb[b][u], kr));
+      const float dp = sum16(dot_part<kE>(db[b][u], vr));
+      float ds = 0.f, pd = 0.f;
+      if (j <= i && i < T && j < T) {
         bool kept = true;
         if (drop) {
           uint32_t km[4];
           keep_mask8(a.drop, head, i, (uint32_t)j >> 3, km);
           kept = kept_bit(km, j & 7);
         }
-        const float p = expf(s * scale - lses[ii]);
-        const float ds = p * ((kept ? dp * zs : 0.f) - dels[ii]);
-        const float pd = kept ? p : 0.f;
+        const float p = expf(s * scale - lb[b][u]);
+        ds = p * ((kept ? dp * zs : 0.f) - eb[b][u]);
+        pd = kept ? p : 0.f;
+      }
 #pragma unroll
-        for (int d = 0; d < kH; ++d) {
-          dva[d] = fmaf(pd, dOs[ii * kD + half * kH + d], dva[d]);
-          dka[d] = fmaf(ds, Qs[ii * kD + half * kH + d], dka[d]);
-        }
+      for (int e = 0; e < kE; ++e) {
+        dva[e] = fmaf(pd, db[b][u][e], dva[e]);
+        dka[e] = fmaf(ds, qb[b][u][e], dka[e]);
       }
     }
+  };
+  // Wave w takes query batches k0 + w kU, k0 + (w + kW) kU, ...
+  const int step = kW * kU;
+  int i0 = k0 + w * kU;
+  if (i0 < T) load_batch(i0, 0);
+  for (; i0 < T; i0 += 2 * step) {
+    if (i0 + step < T) load_batch(i0 + step, 1);
+    use_batch(i0, 0);
+    if (i0 + step >= T) break;
+    if (i0 + 2 * step < T) load_batch(i0 + 2 * step, 0);
+    use_batch(i0 + step, 1);
   }
-  if (j < T) {
-    float* dkr = fptr_w(a.dk, a.ldk, head, a.H) + j * a.ldk.t + half * kH;
-    float* dvr = fptr_w(a.dv, a.ldv, head, a.H) + j * a.ldv.t + half * kH;
 #pragma unroll
-    for (int d = 0; d < kH; ++d) {
-      dkr[d] = dka[d] * scale;
-      dvr[d] = dva[d] * zs;
+  for (int e = 0; e < kE; ++e) {
+    s_part[w][lane][e] = dka[e];
+    s_part[w][lane][kE + e] = dva[e];
+  }
+  __syncthreads();
+  if (w != 0 || j >= T) return;
+  float* dkr = fptr_w(a.dk, a.ldk, head, a.H) + j * a.ldk.t + g * kE;
+  float* dvr = fptr_w(a.dv, a.ldv, head, a.H) + j * a.ldv.t + g * kE;
+#pragma unroll
+  for (int e = 0; e < kE; ++e) {
+    float sk = 0.f, sv = 0.f;
+#pragma unroll
+    for (int v = 0; v < kW; ++v) {
+      sk += s_part[v][lane][e];
+      sv += s_part[v][lane][kE + e];
     }
+    dkr[e] = sk * scale;
+    dvr[e] = sv * zs;
   }
 }
 
-// dQ: thread pair (query i, half) holds D/2 dims of Q_i, dO_i, dQ_i.
+// dQ: one workgroup per four queries (16 lanes each, kE dims of Q_i, dO_i,
+// dQ_i per lane); its waves share the keys up to the last query.
 template <int kD>
-__global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(const BwdArgs a, int n_tiles,
-                                                             float scale) {
-  constexpr int kH = kD / 2;
-  __shared__ float Ks[32 * kD];
-  __shared__ float Vs[32 * kD];
+__global__ __launch_bounds__(64 * kW) void attn_bwd_dq_f32_kernel(const BwdArgs a, int n_tiles,
+                                                                  float scale) {
+  constexpr int kE = kD / 16;
+  __shared__ float s_part[kW][64][kE];
   const int T = a.T;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane & 15;
   const int head = blockIdx.x / n_tiles;
-  const int q0 = (blockIdx.x % n_tiles) * 32;
-  const int i = q0 + (tid >> 1);
-  const int half = tid & 1;
-  const float* qh = fptr(a.q, a.lq, head, a.H);
-  const float* kh = fptr(a.k, a.lk, head, a.H);
-  const float* vh = fptr(a.v, a.lv, head, a.H);
-  const float* doh = fptr(a.dout, a.ldo, head, a.H);
+  const int q0 = (blockIdx.x % n_tiles) * 4;
+  const int i = q0 + (lane >> 4);
+  const int ie = min(i, T - 1);
+  const float* kh = fptr(a.k, a.lk, head, a.H) + g * kE;
+  const float* vh = fptr(a.v, a.lv, head, a.H) + g * kE;
+  const int ldk = (int)a.lk.t, ldv = (int)a.lv.t;
   const size_t roff = (size_t)head * T;
-
-  float qr[kH], dor[kH], dqa[kH];
-#pragma unroll
-  for (int d = 0; d < kH; ++d) {
-    qr[d] = i < T ? qh[i * a.lq.t + half * kH + d] : 0.f;
-    dor[d] = i < T ? doh[i * a.ldo.t + half * kH + d] : 0.f;
-    dqa[d] = 0.f;
-  }
   const bool drop = a.drop.thr != 0;
   const float zs = drop ? a.drop.scale : 1.f;
-  const float lse_i = i < T ? a.lse[roff + i] : 0.f;
-  const float del_i = i < T ? a.delta[roff + i] : 0.f;
-  const int kv_end = min(T, q0 + 32);
-  for (int k0 = 0; k0 < kv_end; k0 += 32) {
-    __syncthreads();
-    for (int e = tid; e < 32 * kD; e += 64) {
-      const int r = e / kD, d = e % kD;
-      const bool ok = k0 + r < T;
-      Ks[e] = ok ? kh[(k0 + r) * a.lk.t + d] : 0.f;
-      Vs[e] = ok ? vh[(k0 + r) * a.lv.t + d] : 0.f;
+
+  float qr[kE], dor[kE], dqa[kE];
+  load_part<kE>(fptr(a.q, a.lq, head, a.H) + ie * a.lq.t + g * kE, qr);
+  load_part<kE>(fptr(a.dout, a.ldo, head, a.H) + ie * a.ldo.t + g * kE, dor);
+#pragma unroll
+  for (int e = 0; e < kE; ++e) dqa[e] = 0.f;
+  const float lse_i = a.lse[roff + ie];
+  const float del_i = a.delta[roff + ie];
+  const int kend = min(q0 + 3, T - 1) + 1;
+  // Key batches of kU = 8 (one keep-mask block).
+  float kb[2][kU][kE], vb[2][kU][kE];
+  auto load_batch = [&](int j0, int b) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int jj = min(j0 + u, T - 1);
+      load_part<kE>(kh + jj * ldk, kb[b][u]);
+      load_part<kE>(vh + jj * ldv, vb[b][u]);
     }
-    __syncthreads();
+  };
+  auto use_batch = [&](int j0, int b) {
     uint32_t km[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
-    for (int jj = 0; jj < 32; ++jj) {
-      const int j = k0 + jj;
-      if (drop && (jj & 7) == 0) keep_mask8(a.drop, head, i, (uint32_t)j >> 3, km);
-      float s = 0.f, dp = 0.f;
+    if (drop) keep_mask8(a.drop, head, ie, (uint32_t)j0 >> 3, km);
 #pragma unroll
-      for (int d = 0; d < kH; ++d) {
-        s = fmaf(qr[d], Ks[jj * kD + half * kH + d], s);
-        dp = fmaf(dor[d], Vs[jj * kD + half * kH + d], dp);
-      }
-      s += __shfl_xor(s, 1, 64);
-      dp += __shfl_xor(dp, 1, 64);
-      if (i < T && j < T && j <= i) {
+    for (int u = 0; u < kU; ++u) {
+      const int jj = j0 + u;
+      const float s = sum16(dot_part<kE>(qr, kb[b][u]));
+      const float dp = sum16(dot_part<kE>(dor, vb[b][u]));
+      float ds = 0.f;
+      if (jj <= ie) {
         const float p = expf(s * scale - lse_i);
-        const float ds = p * ((kept_bit(km, jj & 7) ? dp * zs : 0.f) - del_i);
-#pragma unroll
-        for (int d = 0; d < kH; ++d) dqa[d] = fmaf(ds, Ks[jj * kD + half * kH + d], dqa[d]);
+        ds = p * ((kept_bit(km, u) ? dp * zs : 0.f) - del_i);
       }
-    }
-  }
-  if (i < T) {
-    float* dqr = fptr_w(a.dq, a.ldq, head, a.H) + i * a.ldq.t + half * kH;
 #pragma unroll
-    for (int d = 0; d < kH; ++d) dqr[d] = dqa[d] * scale;
+      for (int e = 0; e < kE; ++e) dqa[e] = fmaf(ds, kb[b][u][e], dqa[e]);
+    }
+  };
+  // Wave w takes key batches w kU, (w + kW) kU, ...
+  const int step = kW * kU;
+  int j0 = w * kU;
+  if (j0 < kend) load_batch(j0, 0);
+  for (; j0 < kend; j0 += 2 * step) {
+    if (j0 + step < kend) load_batch(j0 + step, 1);
+    use_batch(j0, 0);
+    if (j0 + step >= kend) break;
+    if (j0 + 2 * step < kend) load_batch(j0 + 2 * step, 0);
+    use_batch(j0 + step, 1);
+  }
+#pragma unroll
+  for (int e = 0; e < kE; ++e) s_part[w][lane][e] = dqa[e];
+  __syncthreads();
+  if (w != 0 || i >= T) return;
+  float* dqr = fptr_w(a.dq, a.ldq, head, a.H) + i * a.ldq.t + g * kE;
+#pragma unroll
+  for (int e = 0; e < kE; ++e) {
+    float sq = 0.f;
+#pragma unroll
+    for (int v = 0; v < kW; ++v) sq += s_part[v][lane][e];
+    dqr[e] = sq * scale;
   }
 }
 
@@ -312,9 +429,9 @@ namespace {
 
 template <int D>
 hipError_t fwd_f32(const FwdArgs& a, hipStream_t stream) {
-  const int n_tiles = (a.T + 63) / 64;
-  hipLaunchKernelGGL(attn_fwd_f32_kernel<D>, dim3((unsigned)a.n_heads * n_tiles), dim3(64), 0,
-                     stream, a, n_tiles, 1.f / __builtin_sqrtf((float)D));
+  const int n_tiles = (a.T + 3) / 4;
+  hipLaunchKernelGGL(attn_fwd_f32_kernel<D>, dim3((unsigned)a.n_heads * n_tiles), dim3(64 * kW),
+                     0, stream, a, n_tiles, 1.f / __builtin_sqrtf((float)D));
   return hipGetLastError();
 }
 
@@ -329,13 +446,15 @@ hipError_t prep_f32(const BwdArgs& a, hipStream_t stream) {
 
 template <int D>
 hipError_t main_f32(const BwdArgs& a, hipStream_t stream) {
-  const int n_tiles = (a.T + 31) / 32;
+  const int n_tiles = (a.T + 3) / 4;
   const dim3 grid((unsigned)a.n_heads * n_tiles);
   const float scale = 1.f / __builtin_sqrtf((float)D);
-  hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<D>, grid, dim3(64), 0, stream, a, n_tiles, scale);
+  hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<D>, grid, dim3(64 * kW), 0, stream, a, n_tiles,
+                     scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<D>, grid, dim3(64), 0, stream, a, n_tiles, scale);
+  hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<D>, grid, dim3(64 * kW), 0, stream, a, n_tiles,
+                     scale);
   return hipGetLastError();
 }
 
