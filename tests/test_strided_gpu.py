@@ -85,7 +85,8 @@ def test_fused_layout_parity(dtype, B, H, T):
                              f"{dtype} B={B} H={H} T={T}")
 
 
-@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 32), ("f16", 32), ("f32", 32)])
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 32), ("f16", 32), ("f32", 32),
+                                     ("bf16", 128), ("f16", 128), ("f32", 128)])
 def test_fused_layout_other_dtypes_and_head_sizes(dtype, D):
     B, H, T = 2, 3, 200
     announce(f"fused layout dtype={dtype} D={D} B={B} H={H} T={T}")

@@ -31,13 +31,13 @@ def _grads(q):
                  for _ in range(3))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_noalloc_equals_workspace_form_two_calls(dtype):
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f32", 64), ("bf16", 128)])
+def test_noalloc_equals_workspace_form_two_calls(dtype, D):
     for (B, H, T) in [(3, 12, 1024), (2, 3, 333)]:
-        announce(f"noalloc dtype={dtype} B={B} H={H} T={T}")
-        inp = make_inputs(B, H, T, 64, dtype, seed=T)
+        announce(f"noalloc dtype={dtype} D={D} B={B} H={H} T={T}")
+        inp = make_inputs(B, H, T, D, dtype, seed=T)
         q, k, v, do, o, lse = _forward(inp)
-        ws = torch.empty(gattn.gpt_attn_bwd_workspace_bytes(B, H, T, 64) // 4,
+        ws = torch.empty(gattn.gpt_attn_bwd_workspace_bytes(B, H, T, D) // 4,
                          dtype=torch.float32, device=DEV)
         ref = _grads(q)
         gattn.gpt_attn_bwd(q, k, v, o, do, lse, *ref, ws)
