@@ -25,12 +25,12 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-def _cases(n: int = 24, seed: int = 20261203):
+def _cases(n: int = 32, seed: int = 20261203):
     rng = random.Random(seed)
     out = []
     for i in range(n):
         dtype = rng.choice(["bf16", "bf16", "f16", "f32"])
-        D = rng.choice([64, 64, 32])
+        D = rng.choice([64, 64, 32, 128])
         B, H = rng.randint(1, 3), rng.randint(1, 5)
         T = rng.choice([rng.randint(1, 70), rng.randint(60, 330), rng.randint(250, 520)])
         fused = rng.random() < 0.5
