@@ -31,7 +31,10 @@ the preprocess. Last comes the timed region: exactly ``--steps`` whole steps
 between two HIP events (nothing recorded between launches, since an event
 between two kernels adds a gap; ``--graph`` replays the step from a HIP
 graph instead), bracketed by device synchronizations. ``value`` is the
-algorithmic FLOPs of those steps over that region.
+algorithmic FLOPs of those steps over that region. ``sclk_mhz`` is the
+shader clock the steps ran at: the same steps once more, beside a one-wave
+probe kernel that counts shader cycles against the 100 MHz real-time
+counter (``causal_self_attention_amd/probe``).
 
 FLOPs are the causal algorithmic count: only the T(T+1)/2 unmasked (query,
 key) pairs per head, 4*D per pair forward (QK^T and PV) and 10*D per pair
@@ -84,6 +87,35 @@ DOMINANT_KERNEL = "attn_bwd_main_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bwd_main_gpt2_124m_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "causal_self_attention_amd", "csrc", f)
                   for f in ("attn_bwd.hip", "attn_common.h", "attn_launch.h", "attn_dropout.h")]
+
+
+PROBE_LIB = os.path.join(ROOT, "causal_self_attention_amd", "libsclkprobe.so")
+
+
+def sclk_during(run_steps, span_ms: float, dev):
+    """Shader clock (MHz) while run_steps() runs: a one-wave probe on a stream
+    of its own counts shader cycles (s_memtime) against the 100 MHz real-time
+    counter over about 80% of span_ms, started just before the steps are
+    launched. The probe holds one wave slot of one CU; the clock it reads is
+    that CU's. None when the probe library is not built."""
+    import ctypes
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.sclk_probe_launch.argtypes = [ctypes.c_void_p, ctypes.c_ulonglong, ctypes.c_void_p]
+    lib.sclk_probe_launch.restype = ctypes.c_int
+    out = torch.zeros(2, dtype=torch.int64, device=dev)
+    side = torch.cuda.Stream(dev)  # default priority
+    ticks = max(1, int(0.8 * span_ms * 1e5))
+    torch.cuda.synchronize()
+    if lib.sclk_probe_launch(ctypes.c_void_p(out.data_ptr()), ticks,
+                             ctypes.c_void_p(side.cuda_stream)) != 0:
+        return None
+    run_steps()
+    torch.cuda.synchronize()
+    cycles, real = (int(x) for x in out.tolist())
+    return round(cycles / real * 100.0, 1) if real > 0 else None
 
 
 def flops(w):
@@ -477,6 +509,15 @@ def run_train(w, args, with_errors: bool = False, cpu_base: bool = True):
     if not (torch.isfinite(last["dq"]).all() and torch.isfinite(last["o"].float()).all()):
         raise RuntimeError("non-finite outputs")
 
+    # After the timed region, the same steps again beside the clock probe.
+    def again():
+        for i in range(args.steps):
+            if graphs is not None:
+                graphs[i % ns].replay()
+            else:
+                step(i)
+    sclk = sclk_during(again, ms_per_step * args.steps, dev)
+
     peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_MFMA_TFLOPS
 
     def tf(fl, ms):
@@ -530,6 +571,7 @@ def run_train(w, args, with_errors: bool = False, cpu_base: bool = True):
                      "avg_launch_ms": t_main, "flop_per_launch": bwd_flop,
                      "traffic": traffic},
         "wall_s_timed": round(wall, 4),
+        "sclk_mhz": sclk,
     }
     if with_errors:
         out["errors_vs_oracle"] = errs

@@ -3,7 +3,9 @@
 Produces causal_self_attention_amd/libgptattn.so from every csrc/*.hip file,
 and libgptattn_dbg.so, the same sources with GPT_ATTN_EXTRA_BARRIERS (a
 full workgroup barrier at every marked LDS stage boundary; the race check
-of the test suite compares its results with the release library's). Run as
+of the test suite compares its results with the release library's), and
+libsclkprobe.so from probe/sclk_probe.hip (the benchmark's shader-clock
+probe; not part of the attention library). Run as
 ``python -m causal_self_attention_amd.build``; it compiles every time it is
 called.
 """
@@ -18,6 +20,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libgptattn.so")
 DBG_LIB_PATH = os.path.join(HERE, "libgptattn_dbg.so")
+PROBE_LIB_PATH = os.path.join(HERE, "libsclkprobe.so")
+PROBE_SOURCE = os.path.join(HERE, "probe", "sclk_probe.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU instructions stay off: the compiler is told the target
@@ -33,9 +37,9 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def _command(out: str, extra_flags: list[str] | None) -> list[str]:
+def _command(out: str, extra_flags: list[str] | None, srcs: list[str] | None = None) -> list[str]:
     return [HIPCC, *HIP_FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"),
-            "-I", os.path.join(HERE, "csrc"), *sources(), "-o", out + ".tmp"]
+            "-I", os.path.join(HERE, "csrc"), *(srcs or sources()), "-o", out + ".tmp"]
 
 
 def build(verbose: bool = False, extra_flags: list[str] | None = None,
@@ -43,12 +47,13 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None,
     """Build libgptattn.so (and, unless debug_too is false, libgptattn_dbg.so
     alongside it, the two compilations running at once)."""
     out = out or LIB_PATH
-    jobs = [(out, extra_flags)]
+    jobs = [(out, extra_flags, None)]
     if debug_too and out == LIB_PATH:
-        jobs.append((DBG_LIB_PATH, [*(extra_flags or []), "-DGPT_ATTN_EXTRA_BARRIERS"]))
+        jobs.append((DBG_LIB_PATH, [*(extra_flags or []), "-DGPT_ATTN_EXTRA_BARRIERS"], None))
+        jobs.append((PROBE_LIB_PATH, None, [PROBE_SOURCE]))
     procs = []
-    for path, flags in jobs:
-        cmd = _command(path, flags)
+    for path, flags, srcs in jobs:
+        cmd = _command(path, flags, srcs)
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((path, subprocess.Popen(cmd)))

@@ -51,6 +51,8 @@ def test_training_step_report():
     total = (19_346_227_200 + 48_365_568_000) / (d["ms_per_step"] * 1e-3) / 1e12
     assert abs(total - d["value"]) <= 0.01 * total
     assert "cpu_baseline" not in d
+    # The shader clock the steps ran at, from the probe beside them.
+    assert d["sclk_mhz"] is not None and 300.0 < d["sclk_mhz"] < 3000.0, d["sclk_mhz"]
     assert d["config"]["entry_points"] == "plain" and d["config"]["o_lo"] is False
     for part in ("fwd", "bwd"):
         assert d[part]["ms"] > 0 and d[part]["pct_peak"] > 0

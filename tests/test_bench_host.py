@@ -81,3 +81,12 @@ def test_every_benchmark_configuration_is_a_workload():
     for name in bench.ALL_CONFIGS:
         assert name in WORKLOADS
     assert bench.DEFAULT_WORKLOAD in bench.ALL_CONFIGS
+
+
+def test_clock_probe_library_exports_its_launch():
+    # Built beside the attention library by causal_self_attention_amd.build;
+    # loading it needs no GPU.
+    import ctypes
+    assert os.path.exists(bench.PROBE_LIB), "build the libraries first"
+    lib = ctypes.CDLL(bench.PROBE_LIB)
+    assert hasattr(lib, "sclk_probe_launch")
