@@ -101,7 +101,7 @@ KERNELS = ("attn_fwd_kernel", "attn_bwd_prep_kernel", "attn_bwd_main_kernel",
            "attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel",
            "attn_decode_split_kernel", "attn_decode_merge_kernel", "dropout_mask_kernel",
            "attn_fwd_f32_kernel", "attn_bwd_prep_f32_kernel", "attn_bwd_dkdv_f32_kernel",
-           "attn_bwd_dq_f32_kernel")
+           "attn_bwd_dq_f32_kernel", "sclk_probe_kernel")
 
 
 def short_name(kernel_name):
