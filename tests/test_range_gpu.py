@@ -120,17 +120,18 @@ def _relative_to_max(gpu, ref, bound, label):
     assert not bad, f"{label}: " + "; ".join(bad)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("name", ["v", "do", "q"])
-def test_magnitude_growing_along_the_sequence(name):
+def test_magnitude_growing_along_the_sequence(name, D):
     """Row t of one input scaled by 2^(t // 64): every 64-row tile is twice
     the one before, 2^15 from first to last at T = 1000, so no single scale
     fits all of a head in fp16. The forward lowers V's exponent tile by tile
     as larger values arrive; the backward's exponents come from the maxima
     over each workgroup's rows. Bound: max|err| / max|ref| <= 2^-8 per
     output (bf16 keeps 2^-9)."""
-    announce(f"growing magnitude along T: {name}")
+    announce(f"growing magnitude along T: {name} D={D}")
     T = 1000
-    inp = make_inputs(2, 2, T, 64, "bf16", seed=42)
+    inp = make_inputs(2, 2, T, D, "bf16", seed=42)
     f = (2.0 ** (torch.arange(T) // 64).double()).view(1, 1, T, 1)
     inp[name] = (inp[name].double() * f).to(torch.bfloat16)
     if name == "q":
@@ -140,17 +141,18 @@ def test_magnitude_growing_along_the_sequence(name):
         inp["k"] = (inp["k"].double() * 2.0 ** -15).to(torch.bfloat16)
     for o_lo in (False, True):
         _relative_to_max(run_gpu(inp, o_lo=o_lo), run_oracle(inp), 2.0 ** -8,
-                         f"{name} growing, o_lo={o_lo}")
+                         f"{name} growing, D={D}, o_lo={o_lo}")
 
 
-def test_magnitude_shrinking_and_zero_first_tile():
+@pytest.mark.parametrize("D", [64, 128])
+def test_magnitude_shrinking_and_zero_first_tile(D):
     """V zero on the first 64 keys and tiny (~2^-30) after them: the
     forward's first tile fixes no exponent, the first nonzero tile does."""
-    announce("zero first tile, tiny V")
-    inp = make_inputs(1, 3, 300, 64, "bf16", seed=43)
+    announce(f"zero first tile, tiny V, D={D}")
+    inp = make_inputs(1, 3, 300, D, "bf16", seed=43)
     v = inp["v"].double() * 2.0 ** -30
     v[:, :, :64, :] = 0.0
     inp["v"] = v.to(torch.bfloat16)
     gpu, ref = run_gpu(inp), run_oracle(inp)
-    _relative_to_max(gpu, ref, 2.0 ** -8, "zero first tile")
+    _relative_to_max(gpu, ref, 2.0 ** -8, f"zero first tile, D={D}")
     assert torch.equal(gpu["o"][:, :, :64], torch.zeros_like(gpu["o"][:, :, :64]))
